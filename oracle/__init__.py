@@ -1,0 +1,236 @@
+"""CPU oracle for paged decode attention and the KV-append scatter.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of bench.py may import this package.  The GPU library
+(paged_kv_cache_54_amd) never imports, links or calls it, and it shares no
+code with the GPU library.
+
+All arithmetic lives in ``pa_oracle.c`` (double precision, OpenMP over query
+rows); this module only marshals numpy / CPU torch arrays into it.  What each
+function computes, and the passage of the pages it follows, is stated in the C
+file's header:
+
+  decode      -- PagedAttention pseudocode of the vLLM concept page ("Technical
+                 principles"): concatenate the blocks the page table names, cut
+                 to seq_len rows, softmax(scale * q.K^T).V in fp64; query head h
+                 reads KV head h // (H / Hkv).
+  kv_append   -- write each new row at block = slot // bs, offset = slot % bs
+                 (bit copy; e4m3 caches store nearest-e4m3(x *f32 (1/scale))).
+  e4m3_*      -- OCP E4M3FN codec from the format definition.
+
+Parity pinned: every function above is checked in tests/test_oracle_*.py
+against something other than itself (50-digit brute force, torch's fp64
+scaled-dot-product attention, closed forms, invariants, the pages' block-table
+figures, torch's float8_e4m3fn conversion and an independent bitwise encoder).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+from . import build as _build
+
+F32, BF16, E4M3 = 0, 1, 2
+_ERRORS = {1: "bad argument", 2: "block id outside the pool", 3: "slot outside the pool",
+           4: "out of memory", 5: "sequence length outside [0, capacity]"}
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _build.ensure_built()
+        lib = ctypes.CDLL(path)
+        c_i64, c_i32, c_dbl, c_vp = ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_void_p
+        lib.oracle_decode.restype = c_i32
+        lib.oracle_decode.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_dbl, c_dbl, c_vp, c_i64,
+                                      c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl,
+                                      c_vp, c_i64, c_vp, c_vp, c_i64]
+        lib.oracle_kv_append.restype = c_i32
+        lib.oracle_kv_append.argtypes = [c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
+                                         c_i32, c_i64, c_i64, ctypes.c_float, ctypes.c_float]
+        lib.oracle_e4m3_encode_array.argtypes = [c_vp, c_vp, c_i64]
+        lib.oracle_e4m3_decode_array.argtypes = [c_vp, c_vp, c_i64]
+        lib.oracle_bf16_decode_array.argtypes = [c_vp, c_vp, c_i64]
+        lib.oracle_e4m3_from_f32.restype = ctypes.c_uint8
+        lib.oracle_e4m3_from_f32.argtypes = [ctypes.c_float]
+        _lib = lib
+    return _lib
+
+
+def _as_host_array(x, dtype_hint=None):
+    """Return (numpy array, oracle dtype code) for a CPU tensor / numpy array.
+    bf16 tensors are passed as their raw uint16 bits; float8_e4m3fn and uint8
+    tensors as raw e4m3 codes."""
+    if torch.is_tensor(x):
+        x = x.detach()
+        if x.device.type != "cpu":
+            raise ValueError("the oracle takes host tensors")
+        x = x.contiguous()
+        if x.dtype == torch.bfloat16:
+            return x.view(torch.int16).numpy().view(np.uint16), BF16
+        if x.dtype == torch.float8_e4m3fn:
+            return x.view(torch.uint8).numpy(), E4M3
+        x = x.numpy()
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, F32
+    if x.dtype == np.uint16 and dtype_hint == BF16:
+        return x, BF16
+    if x.dtype == np.uint8:
+        return x, E4M3
+    if x.dtype in (np.int32, np.int64):
+        return x, None
+    raise TypeError(f"unsupported array dtype {x.dtype}")
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, k_scale=1.0, v_scale=1.0,
+           rows=None, with_weights=False):
+    """fp64 paged decode attention.
+
+    q [S, H, D] (f32 or bf16); caches [NB, bs, Hkv, D] (f32, bf16, or e4m3 codes as
+    uint8 / float8_e4m3fn); block_tables int32 [S, max_nb]; seq_lens int32 [S].
+    ``rows``: optional flat ids s*H + h to compute (default: all).  Returns a
+    float64 array [S, H, D] (or [len(rows), D]); with ``with_weights`` also the
+    softmax weights [n_rows, max_nb*bs] (NaN beyond each row's seq_len).
+    """
+    lib = _load()
+    qa, q_dt = _as_host_array(q)
+    ka, kv_dt = _as_host_array(key_cache)
+    va, kv_dt2 = _as_host_array(value_cache)
+    if kv_dt != kv_dt2:
+        raise TypeError("key and value caches differ in dtype")
+    bt = np.ascontiguousarray(np.asarray(block_tables.cpu() if torch.is_tensor(block_tables)
+                                         else block_tables, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens.cpu() if torch.is_tensor(seq_lens)
+                                         else seq_lens, dtype=np.int32))
+    S, H, D = qa.shape
+    NB, bs, Hkv, D2 = ka.shape
+    if D2 != D or va.shape != ka.shape or bt.shape[0] != S or sl.shape != (S,):
+        raise ValueError("shape mismatch")
+    max_nb = bt.shape[1]
+    if rows is None:
+        n_rows, rows_arr = S * H, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n_rows = rows_arr.size
+    out = np.zeros((n_rows, D), dtype=np.float64)
+    w = None
+    if with_weights:
+        w = np.full((n_rows, max(max_nb * bs, 1)), np.nan, dtype=np.float64)
+    rc = lib.oracle_decode(_ptr(qa), q_dt, _ptr(ka), _ptr(va), kv_dt, float(k_scale),
+                           float(v_scale), _ptr(bt), max_nb, _ptr(sl), S, H, Hkv, D, bs, NB,
+                           float(scale), None if rows_arr is None else _ptr(rows_arr), n_rows,
+                           _ptr(out), None if w is None else _ptr(w),
+                           0 if w is None else w.shape[1])
+    if rc:
+        raise ValueError(f"oracle_decode: {_ERRORS.get(rc, rc)}")
+    if rows is None:
+        out = out.reshape(S, H, D)
+    return (out, w) if with_weights else out
+
+
+def kv_append(k, v, slot_mapping, key_cache, value_cache, k_scale=1.0, v_scale=1.0):
+    """Scatter rows k, v [T, Hkv, D] into host caches [NB, bs, Hkv, D] in place.
+
+    Caches are CPU torch tensors (float32 / bfloat16 / uint8 e4m3 codes) or numpy
+    arrays; they are modified in place.
+    """
+    lib = _load()
+    ka, in_dt = _as_host_array(k)
+    va, in_dt2 = _as_host_array(v)
+    if in_dt != in_dt2:
+        raise TypeError("k and v differ in dtype")
+    kc, c_dt = _cache_view(key_cache)
+    vc, c_dt2 = _cache_view(value_cache)
+    if c_dt != c_dt2:
+        raise TypeError("key and value caches differ in dtype")
+    slots = np.ascontiguousarray(np.asarray(slot_mapping.cpu() if torch.is_tensor(slot_mapping)
+                                            else slot_mapping, dtype=np.int64))
+    T, Hkv, D = ka.shape
+    NB, bs, Hkv2, D2 = kc.shape
+    if (Hkv2, D2) != (Hkv, D) or slots.shape != (T,) or va.shape != ka.shape:
+        raise ValueError("shape mismatch")
+    rc = lib.oracle_kv_append(_ptr(ka), _ptr(va), in_dt, T, Hkv, D, _ptr(slots), _ptr(kc),
+                              _ptr(vc), c_dt, NB, bs, float(k_scale), float(v_scale))
+    if rc:
+        raise ValueError(f"oracle_kv_append: {_ERRORS.get(rc, rc)}")
+
+
+def _cache_view(c):
+    """Writable numpy view sharing memory with a contiguous CPU cache."""
+    if torch.is_tensor(c):
+        if c.device.type != "cpu" or not c.is_contiguous():
+            raise ValueError("caches must be contiguous host tensors")
+        if c.dtype == torch.bfloat16:
+            return c.view(torch.int16).numpy().view(np.uint16), BF16
+        if c.dtype in (torch.uint8, torch.float8_e4m3fn):
+            return c.view(torch.uint8).numpy(), E4M3
+        if c.dtype == torch.float32:
+            return c.numpy(), F32
+        raise TypeError(f"unsupported cache dtype {c.dtype}")
+    if not c.flags["C_CONTIGUOUS"]:
+        raise ValueError("caches must be contiguous")
+    return {np.float32: (c, F32), np.uint8: (c, E4M3)}[c.dtype.type]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest-e4m3 codes (ties to even, NaN kept, |x| > 448 saturated) of float32 values."""
+    lib = _load()
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(a.shape, dtype=np.uint8)
+    lib.oracle_e4m3_encode_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    a = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(a.shape, dtype=np.float64)
+    lib.oracle_e4m3_decode_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def bf16_decode(bits) -> np.ndarray:
+    lib = _load()
+    a = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    out = np.empty(a.shape, dtype=np.float64)
+    lib.oracle_bf16_decode_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def fill_cache(batch, rows_k, rows_v, slots=None):
+    """Host cache of ``batch``'s cache dtype holding ``rows_k``/``rows_v``
+    ([NB*bs, Hkv, D] pool values) appended at ``slots`` (default: every slot)
+    by this oracle's own append."""
+    NB, bs, Hkv, D = batch.num_blocks, batch.block_size, batch.num_kv_heads, batch.head_dim
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8_e4m3": torch.uint8}[batch.cache_dtype]
+    kc = torch.zeros((NB, bs, Hkv, D), dtype=dt)
+    vc = torch.zeros((NB, bs, Hkv, D), dtype=dt)
+    if slots is None:
+        slots = torch.arange(NB * bs, dtype=torch.int64)
+    kv_append(rows_k, rows_v, slots, kc, vc, batch.k_scale, batch.v_scale)
+    return kc, vc
+
+
+def reference_step(batch):
+    """Oracle result of one decode step of ``batch``: the pool (quantised by the
+    oracle's own append for an e4m3 cache), the new rows appended at their
+    slots, then decode.  Returns (out fp64 [S, H, D], key_cache, value_cache)."""
+    NB, bs, Hkv, D = batch.num_blocks, batch.block_size, batch.num_kv_heads, batch.head_dim
+    kp = batch.key_pool.cpu().reshape(NB * bs, Hkv, D)
+    vp = batch.value_pool.cpu().reshape(NB * bs, Hkv, D)
+    kc, vc = fill_cache(batch, kp, vp)
+    kv_append(batch.k_new.cpu(), batch.v_new.cpu(), batch.slot_mapping.cpu(), kc, vc,
+              batch.k_scale, batch.v_scale)
+    out = decode(batch.q.cpu(), kc, vc, batch.block_tables.cpu(), batch.seq_lens.cpu(),
+                 batch.scale, batch.k_scale, batch.v_scale)
+    return out, kc, vc
