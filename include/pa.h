@@ -1,0 +1,186 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged KV-cache append and paged decode attention
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operations (the pages' definitions):
+ *
+ *   pa_kv_append -- the write side of PagedAttention: the KV cache of a layer
+ *     is cut into fixed-size blocks held in one shared pool, and a new token's
+ *     key and value rows are written into a block slot on demand (vLLM concept
+ *     page, "15-minute deep dive", memory-manager item; the same page names
+ *     the high-bandwidth pack/unpack kernels that do this on the GPU).  Token t
+ *     goes to slot slot_mapping[t] = block * block_size + offset.
+ *
+ *   pa_decode -- the read side: for each sequence, gather the blocks its
+ *     block table names in logical order and run scaled-dot-product attention
+ *     of its one new query token over them (vLLM concept page, "Technical
+ *     principles": PagedAttention pseudocode, and the remark that the real
+ *     kernel gathers by page table inside one fused GPU kernel, without first
+ *     concatenating into HBM).  Query head h reads KV head h / (H / Hkv)
+ *     (grouped-query attention, same page).  Only the first seq_len tokens are
+ *     attended over; the unfilled tail of the last block is excluded by
+ *     selection, never by multiplying with zero, so stale NaN/Inf bits in
+ *     unused slots cannot leak (vLLM v0.17.1 release notes, fix #35219).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are described by pa_tensor: a DEVICE pointer, a dtype, and shape
+ *     and strides in elements.  Layouts must be dense row-major (strides
+ *     matching the shape) and the data pointer 16-byte aligned; otherwise
+ *     PA_ERR_LAYOUT / PA_ERR_ALIGN.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     never reads device memory from the host and never synchronises: work is
+ *     queued on `hip_stream` (a hipStream_t; NULL = the null stream) and the
+ *     call returns.  Calls are safe from several host threads.
+ *   - A dtype combination the library was not written for is refused with
+ *     PA_ERR_DTYPE rather than reinterpreted (the dtype-guard lesson of vLLM
+ *     0.25.1, fix #48330, in the vLLM-internals blog, section 4.3).
+ *   - Errors are returned as a pa_status; nothing is printed or thrown.  On an
+ *     error nothing has been queued.
+ *   - Contract on device data (not checked on the host, checked in-kernel):
+ *     0 <= block_tables[s][j] < num_blocks for j < ceil(seq_lens[s] / bs);
+ *     0 <= seq_lens[s] <= max_blocks_per_seq * block_size; slot_mapping
+ *     entries unique and < num_blocks * block_size (negative = skip the token).
+ *     A kernel never reads or writes out of bounds when the contract is broken:
+ *     an out-of-range block id is skipped (its tokens are left out), an
+ *     over-long seq_len is clamped to the table's capacity, an out-of-range
+ *     slot is not written, and if opts->err_flag is set the matching
+ *     PA_DEVERR_* bit is OR-ed into that device word.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_VERSION 1
+
+typedef enum pa_dtype {
+    PA_F32 = 0,       /* IEEE binary32 */
+    PA_BF16 = 1,      /* bfloat16 */
+    PA_FP8_E4M3 = 2,  /* OCP 8-bit E4M3FN (max 448, no infinities, S.1111.111 = NaN) */
+    PA_I32 = 3,
+    PA_I64 = 4
+} pa_dtype;
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,         /* a required descriptor or data pointer is NULL */
+    PA_ERR_DTYPE = 2,        /* dtype or dtype combination not supported */
+    PA_ERR_SHAPE = 3,        /* ranks or sizes inconsistent */
+    PA_ERR_LAYOUT = 4,       /* strides not dense row-major */
+    PA_ERR_ALIGN = 5,        /* data pointer not 16-byte aligned */
+    PA_ERR_UNSUPPORTED = 6,  /* head_dim, block_size, group size or option not supported */
+    PA_ERR_WORKSPACE = 7,    /* split-KV workspace missing or too small */
+    PA_ERR_HIP = 8           /* the HIP runtime reported an error */
+} pa_status;
+
+/* Bits OR-ed into *opts->err_flag by a kernel that met broken device data. */
+#define PA_DEVERR_BLOCK_ID 0x1u  /* block id outside [0, num_blocks): block skipped */
+#define PA_DEVERR_SEQ_LEN 0x2u   /* seq_len > table capacity: clamped */
+#define PA_DEVERR_SLOT 0x4u      /* slot >= num_blocks * block_size: token not written */
+
+typedef struct pa_tensor {
+    void *data;         /* device pointer (16-byte aligned) */
+    int32_t dtype;      /* pa_dtype */
+    int32_t ndim;       /* 1..4 */
+    int64_t shape[4];
+    int64_t stride[4];  /* in elements; must be dense row-major */
+} pa_tensor;
+
+/* Decode kernel families (pa_opts.variant). */
+#define PA_VARIANT_AUTO 0  /* library choice: MFMA where supported, else VALU */
+#define PA_VARIANT_VALU 1  /* vector-ALU kernel: every supported dtype and group size */
+#define PA_VARIANT_MFMA 2  /* matrix-core kernel: bf16 q with a bf16 or fp8 cache */
+
+typedef struct pa_opts {
+    /* Per-tensor scales of an fp8 cache: stored code c means value(c) * scale.
+       Ignored for f32 / bf16 caches.  Must be finite and > 0. */
+    float k_scale;
+    float v_scale;
+    /* Split-KV partition length in tokens: a multiple of block_size, or 0 for
+       the library's choice.  A value >= the table capacity means one pass. */
+    int32_t partition_tokens;
+    int32_t variant;            /* PA_VARIANT_* */
+    void *workspace;            /* device buffer for split-KV partials (pa_decode) */
+    size_t workspace_bytes;
+    uint32_t *err_flag;         /* optional device word, see PA_DEVERR_* */
+    /* Optional pair of hipEvent_t recorded on hip_stream immediately before
+       and after the attention kernel of pa_decode (not the merge), so callers
+       can time that kernel alone.  NULL to skip. */
+    void *kernel_events[2];
+} pa_opts;
+
+/* Fills *opts with the defaults: scales 1.0, library partition choice,
+   automatic variant, no workspace, no error word, no events. */
+void pa_opts_init(pa_opts *opts);
+
+/*
+ * pa_kv_append -- write new key/value rows into their cache slots.
+ *
+ *   k, v          [T, Hkv, D]            rows to write (read only)
+ *   slot_mapping  [T]  PA_I64            slot = block * bs + offset; < 0 = skip
+ *   key_cache,
+ *   value_cache   [NB, bs, Hkv, D]       written in place
+ *   opts          may be NULL (defaults); k_scale / v_scale used for fp8 caches
+ *
+ * Dtypes (k/v -> cache): F32 -> F32 and BF16 -> BF16 are bit copies;
+ * BF16 or F32 -> FP8_E4M3 stores the nearest E4M3FN value of
+ * x * (1.0f / scale), the reciprocal and the product rounded in binary32,
+ * ties to even, NaN kept as NaN, magnitudes beyond 448 saturated to +-448.
+ * D in {64, 128}; bs in {16, 32}.  T = 0 is allowed (nothing is queued).
+ */
+int pa_kv_append(const pa_tensor *k, const pa_tensor *v, const pa_tensor *slot_mapping,
+                 pa_tensor *key_cache, pa_tensor *value_cache, const pa_opts *opts,
+                 void *hip_stream);
+
+/*
+ * pa_decode -- paged decode attention for one new query token per sequence.
+ *
+ *   q             [S, H, D]               F32 or BF16
+ *   key_cache,
+ *   value_cache   [NB, bs, Hkv, D]        same dtype (F32, BF16 or FP8_E4M3)
+ *   block_tables  [S, max_nb]  PA_I32     physical block of each logical block;
+ *                                         entries at j >= ceil(seq_len/bs) unread
+ *   seq_lens      [S]          PA_I32     tokens to attend over (the new token,
+ *                                         already appended, included); 0 gives 0
+ *   scale         multiplies q.k (usually 1/sqrt(D))
+ *   out           [S, H, D]               same dtype as q; rounded to nearest even
+ *   opts          may be NULL when no workspace is needed (see below)
+ *
+ * Supported: (q, cache, out) in {(F32, F32, F32), (BF16, BF16, BF16),
+ * (BF16, FP8_E4M3, BF16)}; D in {64, 128}; bs in {16, 32};
+ * G = H / Hkv in {1, 2, 4, 8}.  The sequence is cut into partitions of
+ * partition_tokens tokens; when the table capacity max_nb * bs exceeds one
+ * partition the partial results go to opts->workspace (size from
+ * pa_decode_workspace_size) and a second kernel merges them by log-sum-exp.
+ * Accumulation is in fp32.
+ */
+int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *value_cache,
+              const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,
+              pa_tensor *out, const pa_opts *opts, void *hip_stream);
+
+/*
+ * pa_decode_workspace_size -- bytes of workspace pa_decode needs for these
+ * descriptors and options (data pointers are not read; 0 means none).  Takes
+ * the same arguments as pa_decode minus the data it does not need; the plan
+ * depends on the current device's compute-unit count, so call it with the
+ * device that will run pa_decode current.
+ */
+int pa_decode_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
+                             const pa_tensor *block_tables, const pa_opts *opts,
+                             size_t *bytes);
+
+/* Static description of a status code. */
+const char *pa_status_string(int status);
+
+/* PA_VERSION of the library. */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PA_H */

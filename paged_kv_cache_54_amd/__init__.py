@@ -1,0 +1,191 @@
+"""paged_kv_cache_54_amd -- paged KV-cache append and paged decode attention
+for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libpa.so`` (include/pa.h): argument
+marshalling only.  Every step of the computation runs in the library's HIP
+kernels; PyTorch supplies device memory and the current stream.  If the
+library has not been built, every call raises ``RuntimeError`` -- there is no
+fallback implementation.
+
+    kv_append(k, v, slot_mapping, key_cache, value_cache, k_scale=1, v_scale=1)
+    decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, ...)
+    decode_workspace_size(q, key_cache, block_tables, ...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = ["kv_append", "decode", "decode_workspace_size", "PaError", "status_string",
+           "version", "library_path", "VARIANT_AUTO", "VARIANT_VALU", "VARIANT_MFMA",
+           "DEVERR_BLOCK_ID", "DEVERR_SEQ_LEN", "DEVERR_SLOT"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_BF16, PA_FP8_E4M3, PA_I32, PA_I64 = 0, 1, 2, 3, 4
+VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
+DEVERR_BLOCK_ID, DEVERR_SEQ_LEN, DEVERR_SLOT = 0x1, 0x2, 0x4
+
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
+           torch.float8_e4m3fn: PA_FP8_E4M3, torch.int32: PA_I32, torch.int64: PA_I64}
+
+
+class PaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class PaOpts(ctypes.Structure):
+    _fields_ = [("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
+                ("partition_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("err_flag", ctypes.c_void_p), ("kernel_events", ctypes.c_void_p * 2)]
+
+
+class PaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python paged_kv_cache_54_amd/build.py")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.POINTER
+        lib.pa_kv_append.restype = ctypes.c_int
+        lib.pa_kv_append.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor), P(PaTensor),
+                                     P(PaTensor), P(PaOpts), ctypes.c_void_p]
+        lib.pa_decode.restype = ctypes.c_int
+        lib.pa_decode.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor), P(PaTensor),
+                                  P(PaTensor), ctypes.c_float, P(PaTensor), P(PaOpts),
+                                  ctypes.c_void_p]
+        lib.pa_decode_workspace_size.restype = ctypes.c_int
+        lib.pa_decode_workspace_size.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor),
+                                                 P(PaOpts), P(ctypes.c_size_t)]
+        lib.pa_opts_init.restype = None
+        lib.pa_opts_init.argtypes = [P(PaOpts)]
+        lib.pa_status_string.restype = ctypes.c_char_p
+        lib.pa_status_string.argtypes = [ctypes.c_int]
+        lib.pa_version.restype = ctypes.c_int
+        lib.pa_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _load().pa_status_string(status).decode()
+
+
+def version() -> int:
+    return _load().pa_version()
+
+
+def describe(t: torch.Tensor) -> PaTensor:
+    """pa_tensor descriptor of a torch tensor (no copy)."""
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    d = PaTensor()
+    d.data = t.data_ptr() if t.numel() else 0
+    d.dtype = _DTYPES[t.dtype]
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _opts(k_scale=1.0, v_scale=1.0, partition_tokens=0, variant=VARIANT_AUTO, workspace=None,
+          err_flag=None, events: Optional[Sequence[int]] = None) -> PaOpts:
+    o = PaOpts()
+    _load().pa_opts_init(ctypes.byref(o))
+    o.k_scale = float(k_scale)
+    o.v_scale = float(v_scale)
+    o.partition_tokens = int(partition_tokens)
+    o.variant = int(variant)
+    if workspace is not None:
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    if err_flag is not None:
+        if err_flag.dtype != torch.int32 or err_flag.numel() < 1 or not err_flag.is_cuda:
+            raise TypeError("err_flag must be a device int32 tensor")
+        o.err_flag = err_flag.data_ptr()
+    if events is not None:
+        o.kernel_events[0] = events[0]
+        o.kernel_events[1] = events[1]
+    return o
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise PaError(fn, rc)
+
+
+def kv_append(k, v, slot_mapping, key_cache, value_cache, k_scale=1.0, v_scale=1.0,
+              err_flag=None, stream=None):
+    """Write rows k, v [T, Hkv, D] into key_cache / value_cache [NB, bs, Hkv, D]
+    at slot_mapping[t] (int64; negative = skip).  fp8 caches (uint8 or
+    float8_e4m3fn tensors) store nearest-e4m3(x * (1/scale))."""
+    lib = _load()
+    o = _opts(k_scale, v_scale, err_flag=err_flag)
+    args = [describe(x) for x in (k, v, slot_mapping, key_cache, value_cache)]
+    _check("pa_kv_append", lib.pa_kv_append(*[ctypes.byref(x) for x in args], ctypes.byref(o),
+                                            _stream(stream)))
+
+
+def decode_workspace_size(q, key_cache, block_tables, partition_tokens=0,
+                          variant=VARIANT_AUTO) -> int:
+    lib = _load()
+    o = _opts(partition_tokens=partition_tokens, variant=variant)
+    n = ctypes.c_size_t(0)
+    _check("pa_decode_workspace_size",
+           lib.pa_decode_workspace_size(ctypes.byref(describe(q)), ctypes.byref(describe(key_cache)),
+                                        ctypes.byref(describe(block_tables)), ctypes.byref(o),
+                                        ctypes.byref(n)))
+    return n.value
+
+
+def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, k_scale=1.0,
+           v_scale=1.0, partition_tokens=0, variant=VARIANT_AUTO, workspace=None,
+           err_flag=None, events=None, stream=None):
+    """Paged decode attention; returns ``out`` [S, H, D] (same dtype as q).
+
+    ``workspace``: optional uint8 device tensor of at least
+    ``decode_workspace_size(...)`` bytes; allocated here (torch caching
+    allocator) when needed and not given.  ``events``: optional pair of raw
+    hipEvent_t handles recorded around the attention kernel."""
+    lib = _load()
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        need = decode_workspace_size(q, key_cache, block_tables, partition_tokens, variant)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events)
+    args = [describe(x) for x in (q, key_cache, value_cache, block_tables, seq_lens)]
+    _check("pa_decode", lib.pa_decode(*[ctypes.byref(x) for x in args], float(scale),
+                                      ctypes.byref(describe(out)), ctypes.byref(o),
+                                      _stream(stream)))
+    return out

@@ -1,0 +1,358 @@
+// pa_api.cpp -- the C ABI of libpa.so (include/pa.h): descriptor validation,
+// launch planning and dispatch to the gfx950 kernels.  Host code only; it
+// never reads device memory and never synchronises.
+#include "pa.h"
+
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+using namespace pa;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool is_dense(const pa_tensor *t)
+{
+    int64_t expect = 1;
+    for (int i = t->ndim - 1; i >= 0; --i) {
+        if (t->shape[i] < 0)
+            return false;
+        if (t->shape[i] != 1 && t->stride[i] != expect)
+            return false;
+        expect *= t->shape[i];
+    }
+    return true;
+}
+
+int64_t numel(const pa_tensor *t)
+{
+    int64_t n = 1;
+    for (int i = 0; i < t->ndim; ++i)
+        n *= t->shape[i];
+    return n;
+}
+
+// Common checks of one descriptor: rank, dtype, dense layout, alignment.
+int check_tensor(const pa_tensor *t, int ndim, uintptr_t align)
+{
+    if (!t)
+        return PA_ERR_NULL;
+    if (t->ndim != ndim)
+        return PA_ERR_SHAPE;
+    if (!is_dense(t))
+        return PA_ERR_LAYOUT;
+    if (numel(t) > 0 && !t->data)
+        return PA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(t->data) % align)
+        return PA_ERR_ALIGN;
+    return PA_OK;
+}
+
+int kv_type_of(int dtype)
+{
+    switch (dtype) {
+    case PA_F32: return KT_F32;
+    case PA_BF16: return KT_BF16;
+    case PA_FP8_E4M3: return KT_E4M3;
+    default: return -1;
+    }
+}
+
+bool supported_head_dim(int64_t d) { return d == 64 || d == 128; }
+bool supported_block_size(int64_t bs) { return bs == 16 || bs == 32; }
+bool supported_group(int64_t g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+// Compute units of the current device, cached per device id.
+int device_cu_count(int *cus)
+{
+    static std::mutex mu;
+    static std::vector<int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return PA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= (int)cache.size())
+        cache.resize(dev + 1, 0);
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return PA_ERR_HIP;
+        cache[dev] = n;
+    }
+    *cus = cache[dev];
+    return PA_OK;
+}
+
+struct DecodePlan {
+    int64_t S, H, Hkv, D, bs, NB, max_nb, G;
+    int q_type, kv_type;
+    int variant;             // PA_VARIANT_VALU or PA_VARIANT_MFMA
+    int64_t part_tokens;     // P
+    int64_t num_parts;       // NP
+    size_t ws_bytes;         // 0 when NP == 1
+};
+
+// Shapes, dtypes and options common to pa_decode and pa_decode_workspace_size.
+int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
+                const pa_opts *opts, DecodePlan *p)
+{
+    if (!q || !kc || !bt)
+        return PA_ERR_NULL;
+    if (q->ndim != 3 || kc->ndim != 4 || bt->ndim != 2)
+        return PA_ERR_SHAPE;
+    if ((q->dtype != PA_F32 && q->dtype != PA_BF16) || bt->dtype != PA_I32)
+        return PA_ERR_DTYPE;
+    const int kvt = kv_type_of(kc->dtype);
+    if (kvt < 0)
+        return PA_ERR_DTYPE;
+    // Supported (q, cache) pairs: (f32, f32), (bf16, bf16), (bf16, e4m3).
+    if (q->dtype == PA_F32 ? kvt != KT_F32 : kvt == KT_F32)
+        return PA_ERR_DTYPE;
+    p->S = q->shape[0];
+    p->H = q->shape[1];
+    p->D = q->shape[2];
+    p->NB = kc->shape[0];
+    p->bs = kc->shape[1];
+    p->Hkv = kc->shape[2];
+    p->max_nb = bt->shape[1];
+    if (kc->shape[3] != p->D || bt->shape[0] != p->S || p->Hkv <= 0 || p->H <= 0 ||
+        p->H % p->Hkv)
+        return PA_ERR_SHAPE;
+    p->G = p->H / p->Hkv;
+    if (!supported_head_dim(p->D) || !supported_block_size(p->bs) || !supported_group(p->G))
+        return PA_ERR_UNSUPPORTED;
+    if (p->S > INT32_MAX || p->NB > INT32_MAX || p->max_nb > INT32_MAX / p->bs)
+        return PA_ERR_UNSUPPORTED;
+    p->q_type = kv_type_of(q->dtype);
+    p->kv_type = kvt;
+
+    const int variant = opts ? opts->variant : PA_VARIANT_AUTO;
+    const bool mfma_ok = mfma_supported(p->q_type, kvt, (int)p->D, (int)p->bs, (int)p->G);
+    if (variant == PA_VARIANT_AUTO)
+        p->variant = mfma_ok ? PA_VARIANT_MFMA : PA_VARIANT_VALU;
+    else if (variant == PA_VARIANT_VALU)
+        p->variant = PA_VARIANT_VALU;
+    else if (variant == PA_VARIANT_MFMA && mfma_ok)
+        p->variant = PA_VARIANT_MFMA;
+    else
+        return PA_ERR_UNSUPPORTED;
+
+    // Partition length P.  Capacity of a table row bounds every sequence.
+    const int64_t cap = p->max_nb * p->bs;
+    int64_t P = opts ? opts->partition_tokens : 0;
+    if (P < 0 || P % p->bs)
+        return PA_ERR_UNSUPPORTED;
+    if (P == 0) {
+        // Aim for about 32 single-wavefront workgroups per compute unit over
+        // the capacity-sized grid, with at least 128 tokens per partition.
+        int cus = 256;
+        if (p->S > 0 && device_cu_count(&cus) != PA_OK)
+            return PA_ERR_HIP;
+        const int64_t units = p->S * p->Hkv;
+        int64_t want_parts = units > 0 ? (32LL * cus + units - 1) / units : 1;
+        if (want_parts < 1)
+            want_parts = 1;
+        P = (cap + want_parts - 1) / want_parts;
+        P = ((P + p->bs - 1) / p->bs) * p->bs;
+        const int64_t min_p = 128 > p->bs ? 128 : p->bs;
+        if (P < min_p)
+            P = min_p;
+    }
+    if (cap == 0 || P >= cap) {
+        p->part_tokens = cap > 0 ? cap : p->bs;
+        p->num_parts = 1;
+    } else {
+        p->part_tokens = P;
+        p->num_parts = (cap + P - 1) / P;
+    }
+    if (p->num_parts > 1)
+        p->ws_bytes = sizeof(float) * (size_t)(p->S * p->H * p->num_parts) * (size_t)(p->D + 2);
+    else
+        p->ws_bytes = 0;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void pa_opts_init(pa_opts *opts)
+{
+    if (!opts)
+        return;
+    memset(opts, 0, sizeof *opts);
+    opts->k_scale = 1.0f;
+    opts->v_scale = 1.0f;
+    opts->variant = PA_VARIANT_AUTO;
+}
+
+int pa_version(void) { return PA_VERSION; }
+
+const char *pa_status_string(int status)
+{
+    switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required descriptor or data pointer is NULL";
+    case PA_ERR_DTYPE: return "dtype or dtype combination not supported";
+    case PA_ERR_SHAPE: return "tensor ranks or sizes are inconsistent";
+    case PA_ERR_LAYOUT: return "tensor strides are not dense row-major";
+    case PA_ERR_ALIGN: return "data pointer not 16-byte aligned";
+    case PA_ERR_UNSUPPORTED: return "head_dim, block_size, group size or option not supported";
+    case PA_ERR_WORKSPACE: return "split-KV workspace missing or too small";
+    case PA_ERR_HIP: return "the HIP runtime reported an error";
+    default: return "unknown status";
+    }
+}
+
+int pa_kv_append(const pa_tensor *k, const pa_tensor *v, const pa_tensor *slot_mapping,
+                 pa_tensor *key_cache, pa_tensor *value_cache, const pa_opts *opts,
+                 void *hip_stream)
+{
+    int rc;
+    if ((rc = check_tensor(k, 3, 16)) || (rc = check_tensor(v, 3, 16)) ||
+        (rc = check_tensor(slot_mapping, 1, 8)) || (rc = check_tensor(key_cache, 4, 16)) ||
+        (rc = check_tensor(value_cache, 4, 16)))
+        return rc;
+    if (slot_mapping->dtype != PA_I64)
+        return PA_ERR_DTYPE;
+    if (k->dtype != v->dtype || key_cache->dtype != value_cache->dtype)
+        return PA_ERR_DTYPE;
+    const int in_t = kv_type_of(k->dtype), cache_t = kv_type_of(key_cache->dtype);
+    if (in_t < 0 || in_t == KT_E4M3 || cache_t < 0)
+        return PA_ERR_DTYPE;
+    if (cache_t != KT_E4M3 && cache_t != in_t)
+        return PA_ERR_DTYPE;
+    for (int i = 0; i < 3; ++i)
+        if (k->shape[i] != v->shape[i])
+            return PA_ERR_SHAPE;
+    for (int i = 0; i < 4; ++i)
+        if (key_cache->shape[i] != value_cache->shape[i])
+            return PA_ERR_SHAPE;
+    const int64_t T = k->shape[0], Hkv = k->shape[1], D = k->shape[2];
+    if (slot_mapping->shape[0] != T || key_cache->shape[2] != Hkv || key_cache->shape[3] != D)
+        return PA_ERR_SHAPE;
+    if (!supported_head_dim(D) || !supported_block_size(key_cache->shape[1]))
+        return PA_ERR_UNSUPPORTED;
+    float ks = opts ? opts->k_scale : 1.0f, vs = opts ? opts->v_scale : 1.0f;
+    if (cache_t == KT_E4M3 && !(isfinite(ks) && ks > 0.0f && isfinite(vs) && vs > 0.0f))
+        return PA_ERR_UNSUPPORTED;
+    if (T == 0)
+        return PA_OK;
+
+    AppendArgs a;
+    a.k = k->data;
+    a.v = v->data;
+    a.slots = static_cast<const int64_t *>(slot_mapping->data);
+    a.key_cache = key_cache->data;
+    a.value_cache = value_cache->data;
+    a.err_flag = opts ? opts->err_flag : nullptr;
+    a.num_tokens = T;
+    a.row_elems = Hkv * D;
+    a.num_slots = key_cache->shape[0] * key_cache->shape[1];
+    a.k_inv_scale = 1.0f / ks;
+    a.v_inv_scale = 1.0f / vs;
+    hipError_t e = launch_kv_append(a, in_t, cache_t, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_decode_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
+                             const pa_tensor *block_tables, const pa_opts *opts, size_t *bytes)
+{
+    if (!bytes)
+        return PA_ERR_NULL;
+    DecodePlan p;
+    int rc = plan_decode(q, key_cache, block_tables, opts, &p);
+    if (rc)
+        return rc;
+    *bytes = p.ws_bytes;
+    return PA_OK;
+}
+
+int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *value_cache,
+              const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,
+              pa_tensor *out, const pa_opts *opts, void *hip_stream)
+{
+    int rc;
+    if ((rc = check_tensor(q, 3, 16)) || (rc = check_tensor(key_cache, 4, 16)) ||
+        (rc = check_tensor(value_cache, 4, 16)) || (rc = check_tensor(block_tables, 2, 4)) ||
+        (rc = check_tensor(seq_lens, 1, 4)) || (rc = check_tensor(out, 3, 16)))
+        return rc;
+    if (value_cache->dtype != key_cache->dtype || out->dtype != q->dtype ||
+        seq_lens->dtype != PA_I32)
+        return PA_ERR_DTYPE;
+    for (int i = 0; i < 4; ++i)
+        if (value_cache->shape[i] != key_cache->shape[i])
+            return PA_ERR_SHAPE;
+    for (int i = 0; i < 3; ++i)
+        if (out->shape[i] != q->shape[i])
+            return PA_ERR_SHAPE;
+    if (seq_lens->shape[0] != q->shape[0])
+        return PA_ERR_SHAPE;
+    if (!isfinite(scale))
+        return PA_ERR_UNSUPPORTED;
+    const bool fp8 = key_cache->dtype == PA_FP8_E4M3;
+    const float ks = (fp8 && opts) ? opts->k_scale : 1.0f;
+    const float vs = (fp8 && opts) ? opts->v_scale : 1.0f;
+    if (fp8 && !(isfinite(ks) && ks > 0.0f && isfinite(vs) && vs > 0.0f))
+        return PA_ERR_UNSUPPORTED;
+    DecodePlan p;
+    if ((rc = plan_decode(q, key_cache, block_tables, opts, &p)))
+        return rc;
+    if (p.S == 0)
+        return PA_OK;
+    if (p.ws_bytes) {
+        if (!opts || !opts->workspace || opts->workspace_bytes < p.ws_bytes)
+            return PA_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(opts->workspace) % 16)
+            return PA_ERR_ALIGN;
+    }
+
+    DecodeArgs a;
+    a.q = q->data;
+    a.key_cache = key_cache->data;
+    a.value_cache = value_cache->data;
+    a.block_tables = static_cast<const int32_t *>(block_tables->data);
+    a.seq_lens = static_cast<const int32_t *>(seq_lens->data);
+    a.out = out->data;
+    a.ws_acc = p.ws_bytes ? static_cast<float *>(opts->workspace) : nullptr;
+    a.ws_ml = p.ws_bytes ? a.ws_acc + p.S * p.H * p.num_parts * p.D : nullptr;
+    a.err_flag = opts ? opts->err_flag : nullptr;
+    a.num_seqs = (int32_t)p.S;
+    a.num_heads = (int32_t)p.H;
+    a.num_kv_heads = (int32_t)p.Hkv;
+    a.max_nb = (int32_t)p.max_nb;
+    a.num_blocks = (int32_t)p.NB;
+    a.part_tokens = (int32_t)p.part_tokens;
+    a.num_parts = (int32_t)p.num_parts;
+    a.qk_scale_log2 = scale * kLog2e * ks;
+    a.v_scale = vs;
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->kernel_events[0]) : nullptr;
+    hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->kernel_events[1]) : nullptr;
+    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess)
+        return PA_ERR_HIP;
+    hipError_t e;
+    if (p.variant == PA_VARIANT_MFMA)
+        e = launch_decode_mfma(a, p.kv_type, (int)p.D, (int)p.bs, (int)p.G, stream);
+    else
+        e = launch_decode_valu(a, p.q_type, p.kv_type, (int)p.D, (int)p.bs, (int)p.G, stream);
+    if (e != hipSuccess)
+        return PA_ERR_HIP;
+    if (ev1 && hipEventRecord(ev1, stream) != hipSuccess)
+        return PA_ERR_HIP;
+    if (p.num_parts > 1) {
+        e = launch_merge(a, p.q_type, (int)p.D, (int)p.bs, stream);
+        if (e != hipSuccess)
+            return PA_ERR_HIP;
+    }
+    return PA_OK;
+}
+
+}  // extern "C"
