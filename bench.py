@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many MiB "
+                         "(3 launches) so hardware byte counters can be scaled against a known size")
     return ap.parse_args()
 
 
@@ -177,6 +180,15 @@ def main():
         sys.exit(1)
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
     b = workloads.make_batch(args.workload, device=dev)
     P = args.partition_tokens if args.partition_tokens is not None else (b.partition_tokens or 0)
     variant = {"auto": pa.VARIANT_AUTO, "valu": pa.VARIANT_VALU, "mfma": pa.VARIANT_MFMA}[args.variant]

@@ -1,13 +1,346 @@
-// decode_mfma.hip -- paged decode attention on the matrix cores (gfx950).
+// decode_mfma.hip -- paged decode attention on the gfx950 matrix cores, for a
+// bf16 query with a bf16 or OCP e4m3 KV cache.
+//
+// What is computed is the same as the vector-ALU kernel (vLLM concept page,
+// "Technical principles": PagedAttention gathers the blocks named by the page
+// table inside one fused kernel and runs scaled-dot-product attention over
+// them; grouped-query heads share a KV head).  Work split, partitions,
+// selection masking and the partial/merge contract are also the same; what
+// differs is how one 16-token tile of one KV head is processed by a wavefront:
+//
+//   loads K and V tiles arrive with 16-byte row-contiguous buffer loads (a
+//         wavefront instruction reads whole 256-byte rows; reading K directly
+//         in MFMA operand order -- 16 rows x 64 bytes per instruction --
+//         measured 15-20 % slower) and are stored to LDS as bf16 rows.
+//   QK^T  v_mfma_f32_16x16x32_bf16, A = K tile (M = 16 tokens, K = 32 dims)
+//         read from LDS, B = Q^T (N = 16 columns; column n is query head
+//         n mod G of the group).  Lane l gets S[token 4*(l/16)+i][column l%16]
+//         in its 4 accumulators.
+//   softmax  per column: max over the lane's 4 tokens and across the four
+//         16-lane groups; running max m, lane-partial sum l, one (lazy)
+//         rescale of the accumulators when some column's max grows.
+//   PV    v_mfma_f32_16x16x16bf16_1k computing O^T = V^T P^T: B = P^T is
+//         exactly the QK accumulator layout (converted to bf16), A = V^T is
+//         read from LDS with ds_read_b64_tr_b16, which transposes 16-bit
+//         elements within each 16-lane group.
+//
+// An e4m3 cache is converted to bf16 (exact) in registers before K and V are
+// stored to LDS; k_scale is folded into the score scale
+// and v_scale applied to the result.  Tokens at or beyond seq_len in the last
+// block are excluded by selection: their scores become -inf and their V rows
+// are stored to LDS as zeros, so stale NaN/Inf bits never enter an MFMA.
 #include "pa_device.h"
 
 namespace pa {
+namespace {
 
-bool mfma_supported(int, int, int, int, int) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-hipError_t launch_decode_mfma(const DecodeArgs &, int, int, int, int, hipStream_t)
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v)
 {
-    return hipErrorNotSupported;
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x4 as_bf16x4(s16x4 v)
+{
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// Two e4m3 codes (byte pair HI of w) -> two packed bf16.  An e4m3 value has
+// at most 4 significant bits, so its binary32 form ends in 16 zero bits and
+// the upper halves are its exact bf16 encoding.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w)
+{
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+}
+
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 v)
+{
+    return make_uint4(e4m3x2_to_bf16x2<false>(v.x), e4m3x2_to_bf16x2<true>(v.x),
+                      e4m3x2_to_bf16x2<false>(v.y), e4m3x2_to_bf16x2<true>(v.y));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+template <int KT, int D, int BS, int G>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
+{
+    constexpr int NC = D / 32;                 // QK MFMAs per 16 tokens
+    constexpr int ND = D / 16;                 // PV MFMAs (16 output dims each) per 16 tokens
+    constexpr int HALVES = BS / 16;            // 16-token tiles per block
+    constexpr int EB = (KT == KT_BF16) ? 2 : 1;
+    constexpr int RCH = D * EB / 16;           // 16-byte chunks of one cache row
+    constexpr int LROWS = 64 / RCH;            // rows one load instruction covers
+    constexpr int NLOAD = BS / LROWS;          // load instructions per block and tensor
+    // K and V tiles in LDS as bf16 rows of D elements plus 16 bytes of padding:
+    // row r starts 4 banks after row r-1, so the row-contiguous stores, the
+    // K operand reads (16 rows x 16 bytes) and the transposed V reads
+    // (16 rows x 32 bytes) all run at the minimum number of bank sweeps, and
+    // every address is a per-lane base plus a constant.
+    constexpr int ROWB = 2 * D + 16;
+    static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group must divide 16");
+
+    __shared__ __attribute__((aligned(16))) uint8_t kt[BS * ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t vt[BS * ROWB];
+
+    const int lane = threadIdx.x;
+    const int g4 = lane >> 4;                  // 16-lane group
+    const int c16 = lane & 15;                 // token row (K operand) / column (output)
+    const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+    const int H = a.num_heads, Hkv = a.num_kv_heads;
+    const int cap = a.max_nb * BS;
+
+    int L = a.seq_lens[s];
+    if (L > cap) {
+        if (part == 0 && kvh == 0 && lane == 0)
+            raise_flag(a.err_flag, PA_DEVERR_SEQ_LEN);
+        L = cap;
+    }
+    const int t0 = part * a.part_tokens;
+    if (L <= 0) {
+        // empty sequence: zero output rows (lanes 0..G-1 each own one head)
+        if (part == 0 && g4 == 0 && c16 < G) {
+            uint16_t *o = static_cast<uint16_t *>(a.out) + ((int64_t)s * H + kvh * G + c16) * D;
+            for (int d = 0; d < D; d += 8)
+                *reinterpret_cast<uint4 *>(o + d) = make_uint4(0, 0, 0, 0);
+        }
+        return;
+    }
+    if (t0 >= L)
+        return;
+    const int t1 = min(t0 + a.part_tokens, L);
+    const bool whole = (t0 == 0) && (t1 == L);
+
+    // Q^T operand: column c16 is query head kvh*G + c16 % G; 8 dims per lane per MFMA.
+    bf16x8 qop[NC];
+    {
+        const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
+                               ((int64_t)s * H + kvh * G + (c16 % G)) * D + 8 * g4;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            qop[c] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * c));
+    }
+
+    f32x4 acc[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+        acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    const int jb0 = t0 / BS, jb1 = (t1 + BS - 1) / BS;
+    BlockIds ids(a.block_tables + (int64_t)s * a.max_nb, jb0, jb1, a.num_blocks, a.err_flag);
+    const int slot_bytes = Hkv * D * EB;
+    const int64_t block_bytes = (int64_t)BS * slot_bytes;
+    // both tensors are read row-contiguously: row i*LROWS + lane/RCH, 16-byte chunk lane%RCH
+    const int l_row = lane / RCH, l_chunk = lane % RCH;
+    const int l_voff = l_row * slot_bytes + kvh * D * EB + l_chunk * 16;
+
+    struct Tile {
+        uint4 k[NLOAD];
+        uint4 v[NLOAD];
+    };
+    auto load_tile = [&](int id, Tile &t) {
+        const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.key_cache, block_bytes, id);
+        const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.value_cache, block_bytes, id);
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            t.k[i] = buf_load16(rk, l_voff, i * LROWS * slot_bytes);
+            t.v[i] = buf_load16(rv, l_voff, i * LROWS * slot_bytes);
+        }
+    };
+    // Store one tensor's rows into an LDS tile as bf16; rows whose token is at
+    // or beyond t1 are stored as zeros when `zero_tail` is set.
+    auto store_tile = [&](uint8_t *tile, const uint4 (&src)[NLOAD], int tok_base, bool zero_tail) {
+#pragma unroll
+        for (int i = 0; i < NLOAD; ++i) {
+            const int row = i * LROWS + l_row;
+            const bool ok = !zero_tail || (tok_base + row < t1);
+            if constexpr (KT == KT_BF16) {
+                *reinterpret_cast<uint4 *>(tile + row * ROWB + l_chunk * 16) =
+                    ok ? src[i] : make_uint4(0, 0, 0, 0);
+            } else {
+                uint4 lo = e4m3x8_to_bf16x8(make_uint2(src[i].x, src[i].y));
+                uint4 hi = e4m3x8_to_bf16x8(make_uint2(src[i].z, src[i].w));
+                if (!ok)
+                    lo = hi = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4 *>(tile + row * ROWB + l_chunk * 32) = lo;
+                *reinterpret_cast<uint4 *>(tile + row * ROWB + l_chunk * 32 + 16) = hi;
+            }
+        }
+    };
+
+    auto process = [&](int j, const Tile &t) {
+        const int tok_base = j * BS;
+        const bool tail = tok_base + BS > t1;
+
+        // K and V -> LDS as bf16; V rows at or beyond t1 become zeros (K rows
+        // there only produce scores that are replaced by -inf below)
+        store_tile(kt, t.k, tok_base, false);
+        store_tile(vt, t.v, tok_base, tail);
+
+        // S = K Q^T for each 16-token half; K operand: token c16, dims 32c + 8*g4
+        f32x4 sc[HALVES];
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) {
+            sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint8_t *krow = kt + (16 * h + c16) * ROWB + 16 * g4;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + 64 * c));
+                sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[c], sc[h], 0, 0, 0);
+            }
+        }
+
+        // scale, mask by selection, block max per column
+        float bm = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = tok_base + 16 * h + 4 * g4 + i < t1;
+                const float v = ok ? sc[h][i] * a.qk_scale_log2 : -INFINITY;
+                sc[h][i] = v;
+                bm = fmaxf(bm, v);
+            }
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(m, bm);
+        if (__ballot(mn > m)) {
+            const float alpha = (mn > m) ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+            l *= alpha;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                acc[d] *= alpha;
+        }
+        m = mn;
+
+        // P = 2^(S - m), summed per lane; bf16 copy is the PV B operand
+        bf16x4 pop[HALVES];
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) {
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = (sc[h][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[h][i] - m);
+                l += p[i];
+            }
+            const uint2 pk = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
+            pop[h] = __builtin_bit_cast(bf16x4, pk);
+        }
+
+        // O^T += V^T P^T, V^T read transposed from LDS
+#pragma unroll
+        for (int h = 0; h < HALVES; ++h) {
+            const int row = 16 * h + 4 * g4 + (c16 >> 2);
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+                const int addr = row * ROWB + 32 * d + 8 * (c16 & 3);
+                const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)((__attribute__((address_space(3))) uint8_t *)vt + addr));
+                acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(raw), pop[h],
+                                                                 acc[d], 0, 0, 0);
+            }
+        }
+    };
+
+    // Two tiles in flight alternately: tile A holds block j while tile B loads j+1.
+    Tile ta, tb;
+    int ida = ids.get(jb0);
+    if (ida >= 0)
+        load_tile(ida, ta);
+    for (int j = jb0; j < jb1; j += 2) {
+        const int idb = (j + 1 < jb1) ? ids.get(j + 1) : -1;
+        if (idb >= 0)
+            load_tile(idb, tb);
+        if (ida >= 0)
+            process(j, ta);
+        if (j + 1 >= jb1)
+            break;
+        ida = (j + 2 < jb1) ? ids.get(j + 2) : -1;
+        if (ida >= 0)
+            load_tile(ida, ta);
+        if (idb >= 0)
+            process(j + 1, tb);
+    }
+
+    // l: sum the four 16-lane groups' partial sums of each column
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (c16 >= G)
+        return;                                // replicated columns
+    const int64_t row = (int64_t)s * H + kvh * G + c16;
+    if (whole) {
+        const float inv = l > 0.f ? a.v_scale / l : 0.f;
+        uint16_t *o = static_cast<uint16_t *>(a.out) + row * D + 4 * g4;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            *reinterpret_cast<uint2 *>(o + 16 * d) =
+                make_uint2(pack_bf16x2(acc[d][0] * inv, acc[d][1] * inv),
+                           pack_bf16x2(acc[d][2] * inv, acc[d][3] * inv));
+    } else {
+        const int64_t pi = row * a.num_parts + part;
+        float *o = a.ws_acc + pi * D + 4 * g4;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            *reinterpret_cast<float4 *>(o + 16 * d) =
+                make_float4(acc[d][0] * a.v_scale, acc[d][1] * a.v_scale, acc[d][2] * a.v_scale,
+                            acc[d][3] * a.v_scale);
+        if (g4 == 0)
+            *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m, l);
+    }
+}
+
+template <int KT, int D, int BS>
+hipError_t launch_g(const DecodeArgs &a, int group, hipStream_t stream)
+{
+    dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs), block(64);
+    switch (group) {
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<KT, D, BS, 1>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_mfma_kernel<KT, D, BS, 2>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<KT, D, BS, 4>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<KT, D, BS, 8>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int KT>
+hipError_t launch_shape(const DecodeArgs &a, int d, int bs, int group, hipStream_t stream)
+{
+    if (d == 64 && bs == 16) return launch_g<KT, 64, 16>(a, group, stream);
+    if (d == 64 && bs == 32) return launch_g<KT, 64, 32>(a, group, stream);
+    if (d == 128 && bs == 16) return launch_g<KT, 128, 16>(a, group, stream);
+    if (d == 128 && bs == 32) return launch_g<KT, 128, 32>(a, group, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool mfma_supported(int q_type, int kv_type, int head_dim, int block_size, int group)
+{
+    return q_type == KT_BF16 && (kv_type == KT_BF16 || kv_type == KT_E4M3) &&
+           (head_dim == 64 || head_dim == 128) && (block_size == 16 || block_size == 32) &&
+           (group == 1 || group == 2 || group == 4 || group == 8);
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs &a, int kv_type, int head_dim, int block_size,
+                              int group, hipStream_t stream)
+{
+    if (kv_type == KT_BF16)
+        return launch_shape<KT_BF16>(a, head_dim, block_size, group, stream);
+    if (kv_type == KT_E4M3)
+        return launch_shape<KT_E4M3>(a, head_dim, block_size, group, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace pa

@@ -103,8 +103,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a)
         const int64_t base = (int64_t)id * BS * slot_elems + lane_elem;
 #pragma unroll
         for (int r = 0; r < PASSES; ++r) {
-            kr[r] = load_raw8<KT>(a.key_cache, base + (int64_t)r * R * slot_elems);
-            vr[r] = load_raw8<KT>(a.value_cache, base + (int64_t)r * R * slot_elems);
+            kr[r] = stream_raw8<KT>(a.key_cache, base + (int64_t)r * R * slot_elems);
+            vr[r] = stream_raw8<KT>(a.value_cache, base + (int64_t)r * R * slot_elems);
         }
     }
 
@@ -116,8 +116,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a)
             const int64_t base = (int64_t)id_next * BS * slot_elems + lane_elem;
 #pragma unroll
             for (int r = 0; r < PASSES; ++r) {
-                kn[r] = load_raw8<KT>(a.key_cache, base + (int64_t)r * R * slot_elems);
-                vn[r] = load_raw8<KT>(a.value_cache, base + (int64_t)r * R * slot_elems);
+                kn[r] = stream_raw8<KT>(a.key_cache, base + (int64_t)r * R * slot_elems);
+                vn[r] = stream_raw8<KT>(a.value_cache, base + (int64_t)r * R * slot_elems);
             }
         }
 

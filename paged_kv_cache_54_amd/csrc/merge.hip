@@ -39,31 +39,38 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a, int block_size)
     if (L <= a.part_tokens)
         return;
     const int n = (L + a.part_tokens - 1) / a.part_tokens;
-    const float *ml = a.ws_ml + row * a.num_parts * 2;
-    const float *acc = a.ws_acc + row * a.num_parts * D;
+    const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + row * a.num_parts;
+    const float *acc = a.ws_acc + row * a.num_parts * D + lane * PER;
 
     float M = -INFINITY;
     for (int i = lane; i < n; i += 64)
-        M = fmaxf(M, ml[2 * i]);
+        M = fmaxf(M, ml[i].x);
     M = wave_max(M);
-    float den = 0.f;
-    for (int i = lane; i < n; i += 64) {
-        const float mi = ml[2 * i];
-        den += (mi == -INFINITY) ? 0.f : exp2f(mi - M) * ml[2 * i + 1];
-    }
-    den = wave_sum(den);
 
-    float o[PER];
+    // Lane i of each 64-partition chunk computes partition i's weight once;
+    // the accumulation loop then broadcasts it with readlane.
+    float o[PER], den = 0.f;
 #pragma unroll
     for (int k = 0; k < PER; ++k)
         o[k] = 0.f;
-    for (int i = 0; i < n; ++i) {
-        const float mi = ml[2 * i];
-        const float w = (mi == -INFINITY) ? 0.f : exp2f(mi - M);
+    for (int c = 0; c < n; c += 64) {
+        float w = 0.f;
+        if (c + lane < n) {
+            const float2 v = ml[c + lane];
+            w = (v.x == -INFINITY) ? 0.f : exp2f(v.x - M);
+            den += w * v.y;
+        }
+        const int cnt = min(64, n - c);
+#pragma unroll 4
+        for (int i = 0; i < cnt; ++i) {
+            const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), i));
+            const float *src = acc + (int64_t)(c + i) * D;
 #pragma unroll
-        for (int k = 0; k < PER; ++k)
-            o[k] = fmaf(w, acc[(int64_t)i * D + lane * PER + k], o[k]);
+            for (int k = 0; k < PER; ++k)
+                o[k] = fmaf(wi, src[k], o[k]);
+        }
     }
+    den = wave_sum(den);
     const float inv = den > 0.f ? 1.f / den : 0.f;
     const int64_t base = row * D + lane * PER;
     if constexpr (OT == KT_F32) {
