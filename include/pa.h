@@ -101,11 +101,17 @@ typedef struct pa_opts {
        Ignored for f32 / bf16 caches.  Must be finite and > 0. */
     float k_scale;
     float v_scale;
-    /* Split-KV partition length in tokens: a multiple of block_size, or 0 for
-       the library's choice.  A value >= the table capacity means one pass. */
+    /* Work split.  The batch's work is the list of (sequence, KV head,
+       logical block) units, sequence-major; it is cut into chunks of
+       consecutive units, one per wavefront, and a KV head's sequence split
+       between chunks is finished by a log-sum-exp merge.  0 (default): as many
+       equal chunks as wavefronts the device holds at once, so every compute
+       unit streams the same number of blocks.  Otherwise: chunks of
+       partition_tokens / block_size units (a multiple of block_size). */
     int32_t partition_tokens;
     int32_t variant;            /* PA_VARIANT_* */
-    void *workspace;            /* device buffer for split-KV partials (pa_decode) */
+    void *workspace;            /* device buffer, pa_decode_workspace_size bytes,
+                                   16-byte aligned; no initial contents needed */
     size_t workspace_bytes;
     uint32_t *err_flag;         /* optional device word, see PA_DEVERR_* */
     /* Optional pair of hipEvent_t recorded on hip_stream immediately before
@@ -153,11 +159,10 @@ int pa_kv_append(const pa_tensor *k, const pa_tensor *v, const pa_tensor *slot_m
  *
  * Supported: (q, cache, out) in {(F32, F32, F32), (BF16, BF16, BF16),
  * (BF16, FP8_E4M3, BF16)}; D in {64, 128}; bs in {16, 32};
- * G = H / Hkv in {1, 2, 4, 8}.  The sequence is cut into partitions of
- * partition_tokens tokens; when the table capacity max_nb * bs exceeds one
- * partition the partial results go to opts->workspace (size from
- * pa_decode_workspace_size) and a second kernel merges them by log-sum-exp.
- * Accumulation is in fp32.
+ * G = H / Hkv in {1, 2, 4, 8}.  opts->workspace (pa_decode_workspace_size
+ * bytes) is required whenever S > 0: it receives the partial results of KV
+ * heads whose sequence is split between chunks (see partition_tokens) and a
+ * second kernel merges them by log-sum-exp.  Accumulation is in fp32.
  */
 int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *value_cache,
               const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,

@@ -4,9 +4,10 @@
 // What is computed is the same as the vector-ALU kernel (vLLM concept page,
 // "Technical principles": PagedAttention gathers the blocks named by the page
 // table inside one fused kernel and runs scaled-dot-product attention over
-// them; grouped-query heads share a KV head).  Work split, partitions,
+// them; grouped-query heads share a KV head).  The work split (equal chunks
+// of the batch's (sequence, KV head, block) list, one per wavefront),
 // selection masking and the partial/merge contract are also the same; what
-// differs is how one 16-token tile of one KV head is processed by a wavefront:
+// differs is how one block of one KV head is processed by a wavefront:
 //
 //   loads K and V tiles arrive with 16-byte row-contiguous buffer loads (a
 //         wavefront instruction reads whole 256-byte rows; reading K directly
@@ -29,6 +30,8 @@
 // and v_scale applied to the result.  Tokens at or beyond seq_len in the last
 // block are excluded by selection: their scores become -inf and their V rows
 // are stored to LDS as zeros, so stale NaN/Inf bits never enter an MFMA.
+#include <type_traits>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -67,9 +70,13 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 v)
                       e4m3x2_to_bf16x2<false>(v.y), e4m3x2_to_bf16x2<true>(v.y));
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair with the hardware converter (v_cvt_pk_bf16_f32,
+// round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 template <int KT, int D, int BS, int G>
@@ -82,122 +89,155 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
     constexpr int RCH = D * EB / 16;           // 16-byte chunks of one cache row
     constexpr int LROWS = 64 / RCH;            // rows one load instruction covers
     constexpr int NLOAD = BS / LROWS;          // load instructions per block and tensor
-    // K and V tiles in LDS as bf16 rows of D elements plus 16 bytes of padding:
-    // row r starts 4 banks after row r-1, so the row-contiguous stores, the
-    // K operand reads (16 rows x 16 bytes) and the transposed V reads
-    // (16 rows x 32 bytes) all run at the minimum number of bank sweeps, and
-    // every address is a per-lane base plus a constant.
-    constexpr int ROWB = 2 * D + 16;
+    // K and V tiles in LDS as bf16 rows of D elements plus padding, chosen so
+    // that each read pattern touches distinct banks: K operand reads take 16
+    // bytes from 16 consecutive rows (rows 4 banks apart: 16-byte pad), the
+    // transposed V reads take 32 bytes from 4 consecutive rows per 16 lanes
+    // (rows 8 banks apart: 32-byte pad).  Every address is a per-lane base
+    // plus a constant.
+    constexpr int KROWB = 2 * D + 16;
+    constexpr int VROWB = 2 * D + 32;
     static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group must divide 16");
 
-    __shared__ __attribute__((aligned(16))) uint8_t kt[BS * ROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t vt[BS * ROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t kt[BS * KROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t vt[BS * VROWB];
 
     const int lane = threadIdx.x;
     const int g4 = lane >> 4;                  // 16-lane group
     const int c16 = lane & 15;                 // token row (K operand) / column (output)
-    const int part = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
     const int H = a.num_heads, Hkv = a.num_kv_heads;
     const int cap = a.max_nb * BS;
+    const int w = blockIdx.x;
 
-    int L = a.seq_lens[s];
-    if (L > cap) {
-        if (part == 0 && kvh == 0 && lane == 0)
-            raise_flag(a.err_flag, PA_DEVERR_SEQ_LEN);
-        L = cap;
-    }
-    const int t0 = part * a.part_tokens;
-    if (L <= 0) {
-        // empty sequence: zero output rows (lanes 0..G-1 each own one head)
-        if (part == 0 && g4 == 0 && c16 < G) {
-            uint16_t *o = static_cast<uint16_t *>(a.out) + ((int64_t)s * H + kvh * G + c16) * D;
-            for (int d = 0; d < D; d += 8)
-                *reinterpret_cast<uint4 *>(o + d) = make_uint4(0, 0, 0, 0);
-        }
+    const Chunk chunk = my_chunk<BS>(a, w, a.num_waves);
+    if (chunk.n == 0)
         return;
-    }
-    if (t0 >= L)
-        return;
-    const int t1 = min(t0 + a.part_tokens, L);
-    const bool whole = (t0 == 0) && (t1 == L);
 
-    // Q^T operand: column c16 is query head kvh*G + c16 % G; 8 dims per lane per MFMA.
-    bf16x8 qop[NC];
-    {
-        const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
-                               ((int64_t)s * H + kvh * G + (c16 % G)) * D + 8 * g4;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-            qop[c] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * c));
-    }
-
-    f32x4 acc[ND];
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-        acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.f;
-
-    const int jb0 = t0 / BS, jb1 = (t1 + BS - 1) / BS;
-    BlockIds ids(a.block_tables + (int64_t)s * a.max_nb, jb0, jb1, a.num_blocks, a.err_flag);
     const int slot_bytes = Hkv * D * EB;
     const int64_t block_bytes = (int64_t)BS * slot_bytes;
     // both tensors are read row-contiguously: row i*LROWS + lane/RCH, 16-byte chunk lane%RCH
     const int l_row = lane / RCH, l_chunk = lane % RCH;
-    const int l_voff = l_row * slot_bytes + kvh * D * EB + l_chunk * 16;
+    const int l_voff = l_row * slot_bytes + l_chunk * 16;
 
     struct Tile {
         uint4 k[NLOAD];
         uint4 v[NLOAD];
     };
-    auto load_tile = [&](int id, Tile &t) {
+    auto load_tile = [&](int id, int kvh, Tile &t) {
         const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.key_cache, block_bytes, id);
         const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.value_cache, block_bytes, id);
+        const int voff = l_voff + kvh * D * EB;
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
-            t.k[i] = buf_load16(rk, l_voff, i * LROWS * slot_bytes);
-            t.v[i] = buf_load16(rv, l_voff, i * LROWS * slot_bytes);
+            t.k[i] = buf_load16(rk, voff, i * LROWS * slot_bytes);
+            t.v[i] = buf_load16(rv, voff, i * LROWS * slot_bytes);
         }
     };
-    // Store one tensor's rows into an LDS tile as bf16; rows whose token is at
-    // or beyond t1 are stored as zeros when `zero_tail` is set.
-    auto store_tile = [&](uint8_t *tile, const uint4 (&src)[NLOAD], int tok_base, bool zero_tail) {
+    // Store one tensor's rows into an LDS tile (row stride ROWB) as bf16; with
+    // MASK, rows whose token is at or beyond t1 are stored as zeros.
+    auto store_tile = [&](auto rowb_c, auto mask_c, uint8_t *tile, const uint4 (&src)[NLOAD],
+                          int tok_base, int t1) {
+        constexpr int ROWB = decltype(rowb_c)::value;
+        constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
             const int row = i * LROWS + l_row;
-            const bool ok = !zero_tail || (tok_base + row < t1);
+            const bool ok = !MASK || (tok_base + row < t1);
             if constexpr (KT == KT_BF16) {
-                *reinterpret_cast<uint4 *>(tile + row * ROWB + l_chunk * 16) =
-                    ok ? src[i] : make_uint4(0, 0, 0, 0);
+                uint4 v = src[i];
+                if (MASK && !ok)
+                    v = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4 *>(tile + row * ROWB + l_chunk * 16) = v;
             } else {
                 uint4 lo = e4m3x8_to_bf16x8(make_uint2(src[i].x, src[i].y));
                 uint4 hi = e4m3x8_to_bf16x8(make_uint2(src[i].z, src[i].w));
-                if (!ok)
+                if (MASK && !ok)
                     lo = hi = make_uint4(0, 0, 0, 0);
                 *reinterpret_cast<uint4 *>(tile + row * ROWB + l_chunk * 32) = lo;
                 *reinterpret_cast<uint4 *>(tile + row * ROWB + l_chunk * 32 + 16) = hi;
             }
         }
     };
+    using KRowB = std::integral_constant<int, KROWB>;
+    using VRowB = std::integral_constant<int, VROWB>;
+    using Plain = std::false_type;
+    using Masked = std::true_type;
 
-    auto process = [&](int j, const Tile &t) {
-        const int tok_base = j * BS;
+    // per-segment state
+    bf16x8 qop[NC];
+    f32x4 acc[ND];
+    float m = -INFINITY, l = 0.f;
+    bool seg_starts = false;
+
+    auto begin_segment = [&](const Cursor &c) {
+        // Q^T operand: column c16 is query head kvh*G + c16 % G; 8 dims per lane per MFMA
+        const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
+                               ((int64_t)c.s * H + c.kvh * G + (c16 % G)) * D + 8 * g4;
+#pragma unroll
+        for (int k = 0; k < NC; ++k)
+            qop[k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * k));
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m = -INFINITY;
+        l = 0.f;
+        seg_starts = c.j == 0;
+    };
+
+    auto finish_segment = [&](const Cursor &c, bool ends) {
+        float lt = l + __shfl_xor(l, 16);      // sum the four 16-lane groups
+        lt += __shfl_xor(lt, 32);
+        const int g = c.s * Hkv + c.kvh;
+        const int slot = w + g;
+        record_segment(a, g, slot, seg_starts, ends);
+        if (c16 >= G)
+            return;                            // replicated columns
+        const int64_t row = (int64_t)c.s * H + c.kvh * G + c16;
+        if (seg_starts && ends) {
+            const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
+            uint16_t *o = static_cast<uint16_t *>(a.out) + row * D + 4 * g4;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                *reinterpret_cast<uint2 *>(o + 16 * d) =
+                    make_uint2(pack_bf16x2(acc[d][0] * inv, acc[d][1] * inv),
+                               pack_bf16x2(acc[d][2] * inv, acc[d][3] * inv));
+        } else {
+            const int64_t pi = (int64_t)slot * G + c16;
+            float *o = a.ws_acc + pi * D + 4 * g4;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                *reinterpret_cast<float4 *>(o + 16 * d) =
+                    make_float4(acc[d][0] * a.v_scale, acc[d][1] * a.v_scale,
+                                acc[d][2] * a.v_scale, acc[d][3] * a.v_scale);
+            if (g4 == 0)
+                *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m, lt);
+        }
+    };
+
+    // One block of the current segment: QK^T, online softmax, PV.
+    auto process = [&](const Cursor &c, const Tile &t) {
+        const int tok_base = c.j * BS;
+        const int t1 = c.L;
         const bool tail = tok_base + BS > t1;
 
         // K and V -> LDS as bf16; V rows at or beyond t1 become zeros (K rows
         // there only produce scores that are replaced by -inf below)
-        store_tile(kt, t.k, tok_base, false);
-        store_tile(vt, t.v, tok_base, tail);
+        store_tile(KRowB{}, Plain{}, kt, t.k, tok_base, t1);
+        if (tail)
+            store_tile(VRowB{}, Masked{}, vt, t.v, tok_base, t1);
+        else
+            store_tile(VRowB{}, Plain{}, vt, t.v, tok_base, t1);
 
-        // S = K Q^T for each 16-token half; K operand: token c16, dims 32c + 8*g4
+        // S = K Q^T for each 16-token half; K operand: token c16, dims 32k + 8*g4
         f32x4 sc[HALVES];
 #pragma unroll
         for (int h = 0; h < HALVES; ++h) {
             sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint8_t *krow = kt + (16 * h + c16) * ROWB + 16 * g4;
+            const uint8_t *krow = kt + (16 * h + c16) * KROWB + 16 * g4;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + 64 * c));
-                sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[c], sc[h], 0, 0, 0);
+            for (int k = 0; k < NC; ++k) {
+                const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + 64 * k));
+                sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[k], sc[h], 0, 0, 0);
             }
         }
 
@@ -244,7 +284,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
             const int row = 16 * h + 4 * g4 + (c16 >> 2);
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
-                const int addr = row * ROWB + 32 * d + 8 * (c16 & 3);
+                const int addr = row * VROWB + 32 * d + 8 * (c16 & 3);
                 const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_s16x4 *)((__attribute__((address_space(3))) uint8_t *)vt + addr));
                 acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(raw), pop[h],
@@ -253,75 +293,82 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
         }
     };
 
-    // Two tiles in flight alternately: tile A holds block j while tile B loads j+1.
-    Tile ta, tb;
-    int ida = ids.get(jb0);
-    if (ida >= 0)
-        load_tile(ida, ta);
-    for (int j = jb0; j < jb1; j += 2) {
-        const int idb = (j + 1 < jb1) ? ids.get(j + 1) : -1;
-        if (idb >= 0)
-            load_tile(idb, tb);
-        if (ida >= 0)
-            process(j, ta);
-        if (j + 1 >= jb1)
-            break;
-        ida = (j + 2 < jb1) ? ids.get(j + 2) : -1;
-        if (ida >= 0)
-            load_tile(ida, ta);
-        if (idb >= 0)
-            process(j + 1, tb);
-    }
+    // Walk the chunk: the load cursor runs one unit ahead of the compute
+    // cursor, alternating between two tiles, across segment boundaries.
+    BlockIds ids(a.block_tables, a.max_nb, a.num_blocks, a.err_flag);
+    Cursor cc = locate<BS>(a.seq_lens, a.num_seqs, Hkv, cap, chunk.u0);
+    Cursor lc = cc;
+    const int n = chunk.n;
 
-    // l: sum the four 16-lane groups' partial sums of each column
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    if (c16 >= G)
-        return;                                // replicated columns
-    const int64_t row = (int64_t)s * H + kvh * G + c16;
-    if (whole) {
-        const float inv = l > 0.f ? a.v_scale / l : 0.f;
-        uint16_t *o = static_cast<uint16_t *>(a.out) + row * D + 4 * g4;
-#pragma unroll
-        for (int d = 0; d < ND; ++d)
-            *reinterpret_cast<uint2 *>(o + 16 * d) =
-                make_uint2(pack_bf16x2(acc[d][0] * inv, acc[d][1] * inv),
-                           pack_bf16x2(acc[d][2] * inv, acc[d][3] * inv));
-    } else {
-        const int64_t pi = row * a.num_parts + part;
-        float *o = a.ws_acc + pi * D + 4 * g4;
-#pragma unroll
-        for (int d = 0; d < ND; ++d)
-            *reinterpret_cast<float4 *>(o + 16 * d) =
-                make_float4(acc[d][0] * a.v_scale, acc[d][1] * a.v_scale, acc[d][2] * a.v_scale,
-                            acc[d][3] * a.v_scale);
-        if (g4 == 0)
-            *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m, l);
+    auto step = [&](int k, int id, const Tile &t) {
+        if (k == 0 || cc.j == 0)
+            begin_segment(cc);
+        if (id >= 0)
+            process(cc, t);
+        const bool ends = cc.j == cc.nb - 1;
+        if (ends || k == n - 1)
+            finish_segment(cc, ends);
+        if (k + 1 < n)
+            advance<BS>(cc, a.seq_lens, Hkv, cap);
+    };
+
+    Tile ta, tb;
+    int ida = ids.get(lc.s, lc.j);
+    if (ida >= 0)
+        load_tile(ida, lc.kvh, ta);
+    for (int k = 0; k < n; k += 2) {
+        int idb = -1;
+        if (k + 1 < n) {
+            advance<BS>(lc, a.seq_lens, Hkv, cap);
+            idb = ids.get(lc.s, lc.j);
+            if (idb >= 0)
+                load_tile(idb, lc.kvh, tb);
+        }
+        step(k, ida, ta);
+        if (k + 1 >= n)
+            break;
+        ida = -1;
+        if (k + 2 < n) {
+            advance<BS>(lc, a.seq_lens, Hkv, cap);
+            ida = ids.get(lc.s, lc.j);
+            if (ida >= 0)
+                load_tile(ida, lc.kvh, ta);
+        }
+        step(k + 1, idb, tb);
     }
 }
 
+typedef void (*DecodeKernel)(DecodeArgs);
+
 template <int KT, int D, int BS>
-hipError_t launch_g(const DecodeArgs &a, int group, hipStream_t stream)
+DecodeKernel pick_g(int group)
 {
-    dim3 grid(a.num_parts, a.num_kv_heads, a.num_seqs), block(64);
     switch (group) {
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<KT, D, BS, 1>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((decode_mfma_kernel<KT, D, BS, 2>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<KT, D, BS, 4>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<KT, D, BS, 8>), grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+    case 1: return decode_mfma_kernel<KT, D, BS, 1>;
+    case 2: return decode_mfma_kernel<KT, D, BS, 2>;
+    case 4: return decode_mfma_kernel<KT, D, BS, 4>;
+    case 8: return decode_mfma_kernel<KT, D, BS, 8>;
+    default: return nullptr;
     }
-    return hipGetLastError();
 }
 
 template <int KT>
-hipError_t launch_shape(const DecodeArgs &a, int d, int bs, int group, hipStream_t stream)
+DecodeKernel pick_shape(int d, int bs, int group)
 {
-    if (d == 64 && bs == 16) return launch_g<KT, 64, 16>(a, group, stream);
-    if (d == 64 && bs == 32) return launch_g<KT, 64, 32>(a, group, stream);
-    if (d == 128 && bs == 16) return launch_g<KT, 128, 16>(a, group, stream);
-    if (d == 128 && bs == 32) return launch_g<KT, 128, 32>(a, group, stream);
-    return hipErrorInvalidValue;
+    if (d == 64 && bs == 16) return pick_g<KT, 64, 16>(group);
+    if (d == 64 && bs == 32) return pick_g<KT, 64, 32>(group);
+    if (d == 128 && bs == 16) return pick_g<KT, 128, 16>(group);
+    if (d == 128 && bs == 32) return pick_g<KT, 128, 32>(group);
+    return nullptr;
+}
+
+DecodeKernel pick(int kv_type, int d, int bs, int group)
+{
+    if (kv_type == KT_BF16)
+        return pick_shape<KT_BF16>(d, bs, group);
+    if (kv_type == KT_E4M3)
+        return pick_shape<KT_E4M3>(d, bs, group);
+    return nullptr;
 }
 
 }  // namespace
@@ -336,11 +383,21 @@ bool mfma_supported(int q_type, int kv_type, int head_dim, int block_size, int g
 hipError_t launch_decode_mfma(const DecodeArgs &a, int kv_type, int head_dim, int block_size,
                               int group, hipStream_t stream)
 {
-    if (kv_type == KT_BF16)
-        return launch_shape<KT_BF16>(a, head_dim, block_size, group, stream);
-    if (kv_type == KT_E4M3)
-        return launch_shape<KT_E4M3>(a, head_dim, block_size, group, stream);
-    return hipErrorInvalidValue;
+    const DecodeKernel k = pick(kv_type, head_dim, block_size, group);
+    if (!k)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k, dim3(a.num_waves), dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t decode_mfma_occupancy(int kv_type, int head_dim, int block_size, int group,
+                                 int *waves_per_cu)
+{
+    const DecodeKernel k = pick(kv_type, head_dim, block_size, group);
+    if (!k)
+        return hipErrorInvalidValue;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(waves_per_cu,
+                                                        reinterpret_cast<const void *>(k), 64, 0);
 }
 
 }  // namespace pa

@@ -93,10 +93,47 @@ struct DecodePlan {
     int64_t S, H, Hkv, D, bs, NB, max_nb, G;
     int q_type, kv_type;
     int variant;             // PA_VARIANT_VALU or PA_VARIANT_MFMA
-    int64_t part_tokens;     // P
-    int64_t num_parts;       // NP
-    size_t ws_bytes;         // 0 when NP == 1
+    int64_t chunk_units;     // units per chunk, 0 = balanced over the waves
+    int64_t waves;           // grid size
+    int64_t slots;           // partial slots = waves + segments
+    size_t ws_bytes;
 };
+
+// Workspace layout: acc [slots, G, D] f32 | ml [slots, G, 2] f32 | seg [S*Hkv, 2] i32
+size_t workspace_bytes(const DecodePlan &p)
+{
+    return sizeof(float) * (size_t)(p.slots * p.G) * (size_t)(p.D + 2) +
+           sizeof(int32_t) * 2 * (size_t)(p.S * p.Hkv);
+}
+
+// Wavefronts of the chosen kernel one compute unit holds at once, cached per
+// (device, kernel instance).
+int resident_waves_per_cu(const DecodePlan &p, int *waves)
+{
+    static std::mutex mu;
+    static std::vector<std::pair<long long, int>> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return PA_ERR_HIP;
+    const long long key = ((((((long long)dev * 4 + p.variant) * 4 + p.q_type) * 4 + p.kv_type) *
+                            256 + p.D) * 64 + p.bs) * 32 + p.G;
+    std::lock_guard<std::mutex> lock(mu);
+    for (auto &kv : cache)
+        if (kv.first == key) {
+            *waves = kv.second;
+            return PA_OK;
+        }
+    int n = 0;
+    hipError_t e = p.variant == PA_VARIANT_MFMA
+                       ? decode_mfma_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G, &n)
+                       : decode_valu_occupancy(p.q_type, p.kv_type, (int)p.D, (int)p.bs,
+                                               (int)p.G, &n);
+    if (e != hipSuccess || n <= 0)
+        return PA_ERR_HIP;
+    cache.emplace_back(key, n);
+    *waves = n;
+    return PA_OK;
+}
 
 // Shapes, dtypes and options common to pa_decode and pa_decode_workspace_size.
 int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
@@ -127,7 +164,8 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
     p->G = p->H / p->Hkv;
     if (!supported_head_dim(p->D) || !supported_block_size(p->bs) || !supported_group(p->G))
         return PA_ERR_UNSUPPORTED;
-    if (p->S > INT32_MAX || p->NB > INT32_MAX || p->max_nb > INT32_MAX / p->bs)
+    if (p->S > INT32_MAX || p->NB > INT32_MAX || p->max_nb > INT32_MAX / p->bs ||
+        p->S * p->Hkv > INT32_MAX / 2)
         return PA_ERR_UNSUPPORTED;
     p->q_type = kv_type_of(q->dtype);
     p->kv_type = kvt;
@@ -143,38 +181,30 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
     else
         return PA_ERR_UNSUPPORTED;
 
-    // Partition length P.  Capacity of a table row bounds every sequence.
-    const int64_t cap = p->max_nb * p->bs;
-    int64_t P = opts ? opts->partition_tokens : 0;
+    // Chunking of the (sequence, KV head, block) work list.
+    const int64_t P = opts ? opts->partition_tokens : 0;
     if (P < 0 || P % p->bs)
         return PA_ERR_UNSUPPORTED;
-    if (P == 0) {
-        // Aim for about 32 single-wavefront workgroups per compute unit over
-        // the capacity-sized grid, with at least 128 tokens per partition.
-        int cus = 256;
-        if (p->S > 0 && device_cu_count(&cus) != PA_OK)
-            return PA_ERR_HIP;
-        const int64_t units = p->S * p->Hkv;
-        int64_t want_parts = units > 0 ? (32LL * cus + units - 1) / units : 1;
-        if (want_parts < 1)
-            want_parts = 1;
-        P = (cap + want_parts - 1) / want_parts;
-        P = ((P + p->bs - 1) / p->bs) * p->bs;
-        const int64_t min_p = 128 > p->bs ? 128 : p->bs;
-        if (P < min_p)
-            P = min_p;
-    }
-    if (cap == 0 || P >= cap) {
-        p->part_tokens = cap > 0 ? cap : p->bs;
-        p->num_parts = 1;
+    const int64_t max_units = p->S * p->Hkv * p->max_nb;
+    if (P > 0) {
+        // fixed chunks: enough wavefronts for the largest possible batch
+        p->chunk_units = P / p->bs;
+        p->waves = max_units > 0 ? (max_units + p->chunk_units - 1) / p->chunk_units : 1;
     } else {
-        p->part_tokens = P;
-        p->num_parts = (cap + P - 1) / P;
+        // balanced: one chunk per wavefront the device holds at once
+        p->chunk_units = 0;
+        p->waves = 1;
+        if (p->S > 0) {
+            int cus = 0, per_cu = 0, rc;
+            if ((rc = device_cu_count(&cus)) || (rc = resident_waves_per_cu(*p, &per_cu)))
+                return rc;
+            p->waves = (int64_t)cus * per_cu;
+        }
     }
-    if (p->num_parts > 1)
-        p->ws_bytes = sizeof(float) * (size_t)(p->S * p->H * p->num_parts) * (size_t)(p->D + 2);
-    else
-        p->ws_bytes = 0;
+    if (p->waves > INT32_MAX / 2 || p->chunk_units > INT32_MAX)
+        return PA_ERR_UNSUPPORTED;
+    p->slots = p->waves + p->S * p->Hkv;
+    p->ws_bytes = p->S > 0 ? workspace_bytes(*p) : 0;
     return PA_OK;
 }
 
@@ -306,12 +336,10 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
         return rc;
     if (p.S == 0)
         return PA_OK;
-    if (p.ws_bytes) {
-        if (!opts || !opts->workspace || opts->workspace_bytes < p.ws_bytes)
-            return PA_ERR_WORKSPACE;
-        if (reinterpret_cast<uintptr_t>(opts->workspace) % 16)
-            return PA_ERR_ALIGN;
-    }
+    if (!opts || !opts->workspace || opts->workspace_bytes < p.ws_bytes)
+        return PA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(opts->workspace) % 16)
+        return PA_ERR_ALIGN;
 
     DecodeArgs a;
     a.q = q->data;
@@ -320,16 +348,17 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
     a.block_tables = static_cast<const int32_t *>(block_tables->data);
     a.seq_lens = static_cast<const int32_t *>(seq_lens->data);
     a.out = out->data;
-    a.ws_acc = p.ws_bytes ? static_cast<float *>(opts->workspace) : nullptr;
-    a.ws_ml = p.ws_bytes ? a.ws_acc + p.S * p.H * p.num_parts * p.D : nullptr;
-    a.err_flag = opts ? opts->err_flag : nullptr;
+    a.ws_acc = static_cast<float *>(opts->workspace);
+    a.ws_ml = a.ws_acc + p.slots * p.G * p.D;
+    a.ws_seg = reinterpret_cast<int32_t *>(a.ws_ml + p.slots * p.G * 2);
+    a.err_flag = opts->err_flag;
     a.num_seqs = (int32_t)p.S;
     a.num_heads = (int32_t)p.H;
     a.num_kv_heads = (int32_t)p.Hkv;
     a.max_nb = (int32_t)p.max_nb;
     a.num_blocks = (int32_t)p.NB;
-    a.part_tokens = (int32_t)p.part_tokens;
-    a.num_parts = (int32_t)p.num_parts;
+    a.chunk_units = (int32_t)p.chunk_units;
+    a.num_waves = (int32_t)p.waves;
     a.qk_scale_log2 = scale * kLog2e * ks;
     a.v_scale = vs;
 
@@ -347,11 +376,9 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
         return PA_ERR_HIP;
     if (ev1 && hipEventRecord(ev1, stream) != hipSuccess)
         return PA_ERR_HIP;
-    if (p.num_parts > 1) {
-        e = launch_merge(a, p.q_type, (int)p.D, (int)p.bs, stream);
-        if (e != hipSuccess)
-            return PA_ERR_HIP;
-    }
+    e = launch_merge(a, p.q_type, (int)p.D, (int)p.bs, stream);
+    if (e != hipSuccess)
+        return PA_ERR_HIP;
     return PA_OK;
 }
 

@@ -220,33 +220,136 @@ __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, int voff, i
     return make_uint2(v.x, v.y);
 }
 
-// Physical block ids of logical blocks [jb0, jb1) of one sequence, read 64 at
-// a time by the lanes of the wavefront and handed out wave-uniformly, so the
-// walk does not wait on a dependent scalar load per block.  An id outside
-// [0, num_blocks) comes back as -1 and raises PA_DEVERR_BLOCK_ID.
+// ---------------------------------------------------------------- work list
+// The decode work of a batch is the flattened list of units (s, kvh, j): for
+// each sequence s, each KV head kvh, each logical block j < nb_s, with
+// nb_s = ceil(min(max(L_s, 0), capacity) / bs).  Segment g = s * Hkv + kvh is
+// the run of units of one (sequence, KV head).  The list is cut into chunks
+// of consecutive units, one chunk per wavefront; a chunk may start or end
+// inside a segment.  The partial result of chunk c for segment g goes to slot
+// c + g: slots are unique (a later chunk never touches an earlier segment)
+// and the slots of one segment are consecutive, [c_first + g, c_last + g].
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+__device__ __forceinline__ int wave_sum_i(int x)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        x += __shfl_xor(x, off);
+    return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int x)
+{
+    const int lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off)
+            x += y;
+    }
+    return x;
+}
+
+template <int BS>
+__device__ __forceinline__ int seq_blocks(int L, int cap)
+{
+    L = min(L, cap);
+    return L > 0 ? (L + BS - 1) / BS : 0;
+}
+
+// Units of the whole batch; raises PA_DEVERR_SEQ_LEN through `flag` (if
+// non-null) when some seq_len exceeds the capacity.
+template <int BS>
+__device__ int64_t total_units(const int32_t *lens, int S, int Hkv, int cap, uint32_t *flag)
+{
+    int64_t total = 0;
+    bool over = false;
+    for (int c = 0; c < S; c += 64) {
+        const int s = c + lane_id();
+        const int L = s < S ? lens[s] : 0;
+        over |= L > cap;
+        total += wave_sum_i(seq_blocks<BS>(L, cap));
+    }
+    if (flag && __ballot(over))
+        raise_flag(flag, PA_DEVERR_SEQ_LEN);
+    return total * Hkv;
+}
+
+// Position of a wavefront in the work list.
+struct Cursor {
+    int s, kvh, j;     // sequence, KV head, logical block
+    int nb, L;         // blocks and (clamped) tokens of sequence s
+};
+
+// Cursor of unit u (< total units).
+template <int BS>
+__device__ Cursor locate(const int32_t *lens, int S, int Hkv, int cap, int64_t u)
+{
+    int64_t base = 0;
+    for (int c = 0; c < S; c += 64) {
+        const int s = c + lane_id();
+        const int L = s < S ? min(lens[s], cap) : 0;
+        const int nb = seq_blocks<BS>(L, cap);
+        const int incl = wave_incl_scan_i(nb * Hkv);
+        const uint64_t hit = __ballot(base + incl > u);
+        if (hit) {
+            const int f = __builtin_ctzll(hit);
+            Cursor cur;
+            cur.s = c + f;
+            cur.nb = __builtin_amdgcn_readlane(nb, f);
+            cur.L = __builtin_amdgcn_readlane(L, f);
+            const int64_t r = u - (base + __builtin_amdgcn_readlane(incl, f) - cur.nb * Hkv);
+            cur.kvh = (int)(r / cur.nb);
+            cur.j = (int)(r % cur.nb);
+            return cur;
+        }
+        base += __builtin_amdgcn_readlane(incl, 63);
+    }
+    return Cursor{S, 0, 0, 0, 0};   // not reached for u < total units
+}
+
+// Next unit; only called when one exists, so a non-empty sequence lies ahead.
+template <int BS>
+__device__ __forceinline__ void advance(Cursor &c, const int32_t *lens, int Hkv, int cap)
+{
+    if (++c.j < c.nb)
+        return;
+    c.j = 0;
+    if (++c.kvh < Hkv)
+        return;
+    c.kvh = 0;
+    do {
+        ++c.s;
+        c.L = __builtin_amdgcn_readfirstlane(min(lens[c.s], cap));
+        c.nb = seq_blocks<BS>(c.L, cap);
+    } while (c.nb == 0);
+}
+
+// Physical block id of a cursor position, wave-uniform; ids of one sequence
+// are read 64 at a time by the lanes and handed out with readlane.  An id
+// outside [0, num_blocks) comes back as -1 and raises PA_DEVERR_BLOCK_ID.
 struct BlockIds {
-    const int32_t *row;
-    int jb1, base, ids, num_blocks;
+    const int32_t *tables;
+    int max_nb, num_blocks;
     uint32_t *err;
+    int s = -1, base = 0, ids = 0;
 
-    __device__ __forceinline__ BlockIds(const int32_t *row_, int jb0, int jb1_, int nblocks,
+    __device__ __forceinline__ BlockIds(const int32_t *tables_, int max_nb_, int nblocks,
                                         uint32_t *err_)
-        : row(row_), jb1(jb1_), base(jb0), num_blocks(nblocks), err(err_)
+        : tables(tables_), max_nb(max_nb_), num_blocks(nblocks), err(err_)
     {
-        fetch(jb0);
     }
 
-    __device__ __forceinline__ void fetch(int j0)
+    __device__ __forceinline__ int get(int s_, int j)
     {
-        base = j0;
-        const int j = j0 + (int)threadIdx.x % 64;
-        ids = j < jb1 ? row[j] : 0;
-    }
-
-    __device__ __forceinline__ int get(int j)
-    {
-        if (j - base >= 64)
-            fetch(j);
+        if (s_ != s || j < base || j >= base + 64) {
+            s = s_;
+            base = j;
+            const int jj = j + lane_id();
+            ids = jj < max_nb ? tables[(int64_t)s_ * max_nb + jj] : 0;
+        }
         const int id = __builtin_amdgcn_readlane(ids, j - base);
         const bool bad = id < 0 || id >= num_blocks;
         if (bad)
@@ -254,5 +357,40 @@ struct BlockIds {
         return __builtin_amdgcn_readfirstlane(bad ? -1 : id);
     }
 };
+
+// Chunk [u0, u0 + n) of the work list for wavefront w of W, or n = 0.
+struct Chunk {
+    int64_t u0;
+    int n;
+};
+
+template <int BS>
+__device__ __forceinline__ Chunk my_chunk(const DecodeArgs &a, int w, int W)
+{
+    const int cap = a.max_nb * BS;
+    const int64_t U = total_units<BS>(a.seq_lens, a.num_seqs, a.num_kv_heads, cap,
+                                      w == 0 ? a.err_flag : nullptr);
+    const int64_t cl = a.chunk_units > 0 ? a.chunk_units : (U + W - 1) / W;
+    const int64_t u0 = (int64_t)w * cl;
+    if (u0 >= U)
+        return Chunk{0, 0};
+    return Chunk{u0, (int)min(cl, U - u0)};
+}
+
+// Slot of chunk w's result for segment g, and the record the merge reads:
+// seg_slots[g] = (first slot, last slot) of the segment.  The chunk that
+// starts a segment writes the first entry, the one that ends it the last;
+// first == last means one chunk held the whole segment and wrote the output.
+__device__ __forceinline__ void record_segment(const DecodeArgs &a, int g, int slot, bool starts,
+                                               bool ends)
+{
+    if (lane_id() != 0)
+        return;
+    int *rec = a.ws_seg + 2 * (int64_t)g;
+    if (starts)
+        rec[0] = slot;
+    if (ends)
+        rec[1] = slot;
+}
 
 }  // namespace pa

@@ -15,6 +15,9 @@ namespace pa {
 enum KvType : int { KT_F32 = 0, KT_BF16 = 1, KT_E4M3 = 2 };
 
 // Everything a decode kernel needs; passed by value as the kernel argument.
+// The work of a call is the flattened list of (sequence, KV head, block)
+// units, cut into chunks of `chunk_units` units (0: ceil(total / waves)), one
+// per wavefront of the grid.
 struct DecodeArgs {
     const void *q;               // [S, H, D]
     const void *key_cache;       // [NB, bs, Hkv, D]
@@ -22,12 +25,13 @@ struct DecodeArgs {
     const int32_t *block_tables; // [S, max_nb]
     const int32_t *seq_lens;     // [S]
     void *out;                   // [S, H, D]
-    float *ws_acc;               // [S, H, NP, D]  unnormalised partial outputs
-    float *ws_ml;                // [S, H, NP, 2]  (running max in log2 units, sum)
+    float *ws_acc;               // [slots, G, D]  unnormalised partial outputs
+    float *ws_ml;                // [slots, G, 2]  (running max in log2 units, sum)
+    int32_t *ws_seg;             // [S * Hkv, 2]   first and last slot of each segment
     uint32_t *err_flag;          // optional
     int32_t num_seqs, num_heads, num_kv_heads, max_nb, num_blocks;
-    int32_t part_tokens;         // P: tokens per partition (multiple of bs)
-    int32_t num_parts;           // NP = ceil(max_nb * bs / P)
+    int32_t chunk_units;         // units per chunk, 0 = balanced over the grid
+    int32_t num_waves;           // grid size (one wavefront per workgroup)
     float qk_scale_log2;         // scale * log2(e) * k_scale (k_scale = 1 unless fp8)
     float v_scale;               // 1 unless fp8
 };
@@ -51,7 +55,7 @@ struct AppendArgs {
 hipError_t launch_kv_append(const AppendArgs &a, int in_type, int cache_type,
                             hipStream_t stream);
 
-// Vector-ALU decode: grid (NP, Hkv, S) of one wavefront each.
+// Vector-ALU decode: one wavefront per chunk.
 hipError_t launch_decode_valu(const DecodeArgs &a, int q_type, int kv_type, int head_dim,
                               int block_size, int group, hipStream_t stream);
 
@@ -60,7 +64,16 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, int kv_type, int head_dim, in
                               int group, hipStream_t stream);
 bool mfma_supported(int q_type, int kv_type, int head_dim, int block_size, int group);
 
-// Log-sum-exp merge of split-KV partials: grid (S * H) of one wavefront.
+// Wavefronts (one-wavefront workgroups) of the matching decode kernel that one
+// compute unit holds at once.
+hipError_t decode_valu_occupancy(int q_type, int kv_type, int head_dim, int block_size, int group,
+                                 int *waves_per_cu);
+hipError_t decode_mfma_occupancy(int kv_type, int head_dim, int block_size, int group,
+                                 int *waves_per_cu);
+
+// Log-sum-exp merge of the chunk partials of every segment that more than
+// one chunk touched; zero rows for empty sequences.  Grid (S * H) of one
+// wavefront.
 hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int block_size,
                         hipStream_t stream);
 

@@ -135,25 +135,32 @@ def test_decode_validation_errors():
     assert call_decode(decode_args(), opts(variant=2)) == PA_ERR_UNSUPPORTED   # no MFMA for f32
     assert call_decode(decode_args(qd=BF16, kd=FP8), opts(k_scale=0.0)) == PA_ERR_UNSUPPORTED
     assert call_decode(decode_args(), scale=float("nan")) == PA_ERR_UNSUPPORTED
-    # a split plan needs a workspace
+    # every call with work needs a workspace of the planned size
     assert call_decode(decode_args(), opts(partition_tokens=16)) == PA_ERR_WORKSPACE
+    assert call_decode(decode_args(), opts(partition_tokens=1024)) == PA_ERR_WORKSPACE
     o = opts(partition_tokens=16, workspace=FAKE, workspace_bytes=100)
     assert call_decode(decode_args(), o) == PA_ERR_WORKSPACE
+
+
+def ws_bytes(S, H, Hkv, D, max_nb, chunk_units):
+    """Workspace of a fixed-chunk plan: partial slots = chunks + segments, each
+    holding G rows of D accumulators plus (max, sum); two ints per segment."""
+    G = H // Hkv
+    chunks = -(-S * Hkv * max_nb // chunk_units)
+    slots = chunks + S * Hkv
+    return 4 * slots * G * (D + 2) + 8 * S * Hkv
 
 
 def test_workspace_size_formula():
     a = decode_args(S=3, H=8, Hkv=2, D=64, bs=16, max_nb=10)
     n = ctypes.c_size_t(1)
-    rc = lib().pa_decode_workspace_size(ctypes.byref(a["q"]), ctypes.byref(a["kc"]),
-                                        ctypes.byref(a["bt"]),
-                                        ctypes.byref(opts(partition_tokens=32)), ctypes.byref(n))
-    assert rc == PA_OK
-    NP = -(-10 * 16 // 32)
-    assert n.value == 3 * 8 * NP * (64 + 2) * 4
-    rc = lib().pa_decode_workspace_size(ctypes.byref(a["q"]), ctypes.byref(a["kc"]),
-                                        ctypes.byref(a["bt"]),
-                                        ctypes.byref(opts(partition_tokens=160)), ctypes.byref(n))
-    assert rc == PA_OK and n.value == 0                  # one partition covers the capacity
+    for P in (32, 160, 16 * 64):
+        rc = lib().pa_decode_workspace_size(ctypes.byref(a["q"]), ctypes.byref(a["kc"]),
+                                            ctypes.byref(a["bt"]),
+                                            ctypes.byref(opts(partition_tokens=P)),
+                                            ctypes.byref(n))
+        assert rc == PA_OK
+        assert n.value == ws_bytes(3, 8, 2, 64, 10, P // 16)
     assert lib().pa_decode_workspace_size(None, ctypes.byref(a["kc"]), ctypes.byref(a["bt"]),
                                           None, ctypes.byref(n)) == PA_ERR_NULL
 
