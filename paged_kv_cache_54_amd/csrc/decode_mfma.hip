@@ -9,7 +9,8 @@
 // selection masking and the partial/merge contract are also the same; what
 // differs is how one block of one KV head is processed by a wavefront:
 //
-//   loads K and V tiles arrive with 16-byte row-contiguous buffer loads (a
+//   loads K and V arrive in 16-token tiles (a 32-token block is two tiles)
+//         through 16-byte row-contiguous buffer loads (a
 //         wavefront instruction reads whole 256-byte rows; reading K directly
 //         in MFMA operand order -- 16 rows x 64 bytes per instruction --
 //         measured 15-20 % slower) and are stored to LDS as bf16 rows.
@@ -82,13 +83,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 template <int KT, int D, int BS, int G>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
 {
+    constexpr int EB = (KT == KT_BF16) ? 2 : 1;
     constexpr int NC = D / 32;                 // QK MFMAs per 16 tokens
     constexpr int ND = D / 16;                 // PV MFMAs (16 output dims each) per 16 tokens
-    constexpr int HALVES = BS / 16;            // 16-token tiles per block
-    constexpr int EB = (KT == KT_BF16) ? 2 : 1;
+    // A tile is 8 KB of one KV head (K and V): 16 bf16 or 32 e4m3 tokens,
+    // never more than a block; MT 16-token MFMA tiles, BS/TILE tiles a block.
+    constexpr int TILE = (32 / EB < BS) ? 32 / EB : BS;
+    constexpr int MT = TILE / 16;
+    constexpr int HALVES = BS / TILE;
     constexpr int RCH = D * EB / 16;           // 16-byte chunks of one cache row
     constexpr int LROWS = 64 / RCH;            // rows one load instruction covers
-    constexpr int NLOAD = BS / LROWS;          // load instructions per block and tensor
+    constexpr int NLOAD = TILE / LROWS;        // load instructions per tile and tensor
     // K and V tiles in LDS as bf16 rows of D elements plus padding, chosen so
     // that each read pattern touches distinct banks: K operand reads take 16
     // bytes from 16 consecutive rows (rows 4 banks apart: 16-byte pad), the
@@ -98,9 +103,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
     constexpr int KROWB = 2 * D + 16;
     constexpr int VROWB = 2 * D + 32;
     static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group must divide 16");
+#ifdef PA_EXP_PINGPONG_ALL
+    constexpr bool PINGPONG = true;
+#elif defined(PA_EXP_SINGLE_ALL)
+    constexpr bool PINGPONG = false;
+#else
+    constexpr bool PINGPONG = KT == KT_BF16;
+#endif
 
-    __shared__ __attribute__((aligned(16))) uint8_t kt[BS * KROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t vt[BS * VROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t kt[TILE * KROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t vt[TILE * VROWB];
 
     const int lane = threadIdx.x;
     const int g4 = lane >> 4;                  // 16-lane group
@@ -123,14 +135,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
         uint4 k[NLOAD];
         uint4 v[NLOAD];
     };
-    auto load_tile = [&](int id, int kvh, Tile &t) {
+    // tile `half` (tokens 16*half .. 16*half+15) of block `id`
+    auto load_tile = [&](int id, int kvh, int half, Tile &t) {
         const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.key_cache, block_bytes, id);
         const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.value_cache, block_bytes, id);
         const int voff = l_voff + kvh * D * EB;
+        const int soff = half * TILE * slot_bytes;
 #pragma unroll
         for (int i = 0; i < NLOAD; ++i) {
-            t.k[i] = buf_load16(rk, voff, i * LROWS * slot_bytes);
-            t.v[i] = buf_load16(rv, voff, i * LROWS * slot_bytes);
+            t.k[i] = buf_load16(rk, voff, soff + i * LROWS * slot_bytes);
+            t.v[i] = buf_load16(rv, voff, soff + i * LROWS * slot_bytes);
         }
     };
     // Store one tensor's rows into an LDS tile (row stride ROWB) as bf16; with
@@ -214,24 +228,28 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
         }
     };
 
-    // One block of the current segment: QK^T, online softmax, PV.
-    auto process = [&](const Cursor &c, const Tile &t) {
-        const int tok_base = c.j * BS;
+    // Stage a 16-token tile of the current segment into LDS as bf16; V rows at
+    // or beyond t1 become zeros (K rows there only produce scores that are
+    // replaced by -inf below).
+    auto stage = [&](const Cursor &c, int half, const Tile &t) {
+        const int tok_base = c.j * BS + half * TILE;
         const int t1 = c.L;
-        const bool tail = tok_base + BS > t1;
-
-        // K and V -> LDS as bf16; V rows at or beyond t1 become zeros (K rows
-        // there only produce scores that are replaced by -inf below)
         store_tile(KRowB{}, Plain{}, kt, t.k, tok_base, t1);
-        if (tail)
+        if (tok_base + TILE > t1)
             store_tile(VRowB{}, Masked{}, vt, t.v, tok_base, t1);
         else
             store_tile(VRowB{}, Plain{}, vt, t.v, tok_base, t1);
+    };
 
-        // S = K Q^T for each 16-token half; K operand: token c16, dims 32k + 8*g4
-        f32x4 sc[HALVES];
+    // QK^T, online softmax and PV of the staged tile.
+    auto process = [&](const Cursor &c, int half) {
+        const int tok_base = c.j * BS + half * TILE;
+        const int t1 = c.L;
+
+        // S = K Q^T per 16-token sub-tile; K operand: token c16, dims 32k + 8*g4
+        f32x4 sc[MT];
 #pragma unroll
-        for (int h = 0; h < HALVES; ++h) {
+        for (int h = 0; h < MT; ++h) {
             sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
             const uint8_t *krow = kt + (16 * h + c16) * KROWB + 16 * g4;
 #pragma unroll
@@ -241,10 +259,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
             }
         }
 
-        // scale, mask by selection, block max per column
+        // scale, mask by selection, tile max per column
         float bm = -INFINITY;
 #pragma unroll
-        for (int h = 0; h < HALVES; ++h)
+        for (int h = 0; h < MT; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool ok = tok_base + 16 * h + 4 * g4 + i < t1;
@@ -265,22 +283,22 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
         m = mn;
 
         // P = 2^(S - m), summed per lane; bf16 copy is the PV B operand
-        bf16x4 pop[HALVES];
+        bf16x4 pop[MT];
 #pragma unroll
-        for (int h = 0; h < HALVES; ++h) {
+        for (int h = 0; h < MT; ++h) {
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 p[i] = (sc[h][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[h][i] - m);
                 l += p[i];
             }
-            const uint2 pk = make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
-            pop[h] = __builtin_bit_cast(bf16x4, pk);
+            pop[h] = __builtin_bit_cast(
+                bf16x4, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
         }
 
         // O^T += V^T P^T, V^T read transposed from LDS
 #pragma unroll
-        for (int h = 0; h < HALVES; ++h) {
+        for (int h = 0; h < MT; ++h) {
             const int row = 16 * h + 4 * g4 + (c16 >> 2);
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
@@ -293,48 +311,93 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
         }
     };
 
-    // Walk the chunk: the load cursor runs one unit ahead of the compute
-    // cursor, alternating between two tiles, across segment boundaries.
+    // Walk the chunk tile by tile: the load cursor runs one tile ahead of the
+    // compute cursor, across block and segment boundaries.
     BlockIds ids(a.block_tables, a.max_nb, a.num_blocks, a.err_flag);
     Cursor cc = locate<BS>(a.seq_lens, a.num_seqs, Hkv, cap, chunk.u0);
     Cursor lc = cc;
-    const int n = chunk.n;
+    const int n = chunk.n;                     // units (blocks)
+    const int steps = n * HALVES;              // tiles
 
-    auto step = [&](int k, int id, const Tile &t) {
-        if (k == 0 || cc.j == 0)
-            begin_segment(cc);
-        if (id >= 0)
-            process(cc, t);
-        const bool ends = cc.j == cc.nb - 1;
-        if (ends || k == n - 1)
-            finish_segment(cc, ends);
-        if (k + 1 < n)
-            advance<BS>(cc, a.seq_lens, Hkv, cap);
+    int l_half = 0;
+    int l_id = ids.get(lc.s, lc.j);
+    auto next_load = [&]() {
+        if (++l_half == HALVES) {
+            l_half = 0;
+            advance<BS>(lc, a.seq_lens, Hkv, cap);
+            l_id = ids.get(lc.s, lc.j);
+        }
     };
 
-    Tile ta, tb;
-    int ida = ids.get(lc.s, lc.j);
-    if (ida >= 0)
-        load_tile(ida, lc.kvh, ta);
-    for (int k = 0; k < n; k += 2) {
-        int idb = -1;
-        if (k + 1 < n) {
-            advance<BS>(lc, a.seq_lens, Hkv, cap);
-            idb = ids.get(lc.s, lc.j);
-            if (idb >= 0)
-                load_tile(idb, lc.kvh, tb);
+    auto step = [&](int k, int id, int half, const Tile &t, auto issue_next) {
+        const int unit = k / HALVES;
+        if (half == 0 && (unit == 0 || cc.j == 0))
+            begin_segment(cc);
+        if (id >= 0)
+            stage(cc, half, t);
+        issue_next();
+        if (id >= 0)
+            process(cc, half);
+        if (half == HALVES - 1) {
+            const bool ends = cc.j == cc.nb - 1;
+            if (ends || unit == n - 1)
+                finish_segment(cc, ends);
+            if (unit + 1 < n)
+                advance<BS>(cc, a.seq_lens, Hkv, cap);
         }
-        step(k, ida, ta);
-        if (k + 1 >= n)
-            break;
-        ida = -1;
-        if (k + 2 < n) {
-            advance<BS>(lc, a.seq_lens, Hkv, cap);
-            ida = ids.get(lc.s, lc.j);
-            if (ida >= 0)
-                load_tile(ida, lc.kvh, ta);
+    };
+
+    if constexpr (PINGPONG) {
+        // Two register tiles: tile k+1 is loaded into the other tile before
+        // tile k is waited on, so two tiles are in flight at the wait.
+        Tile ta, tb;
+        int ida = l_id, ha = l_half;
+        if (ida >= 0)
+            load_tile(ida, lc.kvh, ha, ta);
+        for (int k = 0; k < steps; k += 2) {
+            int idb = -1, hb = 0;
+            if (k + 1 < steps) {
+                next_load();
+                idb = l_id;
+                hb = l_half;
+                if (idb >= 0)
+                    load_tile(idb, lc.kvh, hb, tb);
+            }
+            step(k, ida, ha, ta, [] {});
+            if (k + 1 >= steps)
+                break;
+            ida = -1;
+            if (k + 2 < steps) {
+                next_load();
+                ida = l_id;
+                ha = l_half;
+                if (ida >= 0)
+                    load_tile(ida, lc.kvh, ha, ta);
+            }
+            step(k + 1, idb, hb, tb, [] {});
         }
-        step(k + 1, idb, tb);
+    } else {
+        // One register tile: tile k is staged into LDS, then the loads of tile
+        // k+1 are issued into the same registers and stay in flight while
+        // tile k is computed from LDS.
+        Tile t;
+        int id = l_id, half = l_half;
+        if (id >= 0)
+            load_tile(id, lc.kvh, half, t);
+        for (int k = 0; k < steps; ++k) {
+            int id_next = -1, half_next = 0;
+            step(k, id, half, t, [&] {
+                if (k + 1 < steps) {
+                    next_load();
+                    id_next = l_id;
+                    half_next = l_half;
+                    if (id_next >= 0)
+                        load_tile(id_next, lc.kvh, half_next, t);
+                }
+            });
+            id = id_next;
+            half = half_next;
+        }
     }
 }
 
