@@ -30,20 +30,26 @@ __device__ __forceinline__ float wave_sum(float x)
     return x;
 }
 
+constexpr int kMergeThreads = 256;
+
 template <int OT, int D>
-__global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a, int block_size)
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int block_size)
 {
-    constexpr int PER = D / 64;                  // output elements per lane
-    const int lane = threadIdx.x;
+    constexpr int NT = kMergeThreads;
+    constexpr int LPP = D / 4;                   // threads per partial row (4 floats each)
+    constexpr int NSUB = NT / LPP;               // partial rows read per pass
+    __shared__ float wts[NT];
+    __shared__ float red[NT / 64];
+    __shared__ float4 part[NSUB][LPP];
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int sub = t / LPP, col = (t % LPP) * 4;
     const int64_t row = blockIdx.x;              // s * H + h
     const int H = a.num_heads, G = a.num_heads / a.num_kv_heads;
     const int s = (int)(row / H), h = (int)(row % H);
-    const int64_t obase = row * D + lane * PER;
     const int L = min(a.seq_lens[s], a.max_nb * block_size);
-    float o[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k)
-        o[k] = 0.f;
+
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     float inv = 0.f;
     if (L > 0) {
         const int g = s * a.num_kv_heads + h / G;
@@ -54,44 +60,71 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a, int block_size)
         const int hig = h % G;
         // partial p of this row lives at slot first + p, head hig
         const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (int64_t)first * G + hig;
-        const float *acc = a.ws_acc + ((int64_t)first * G + hig) * D + lane * PER;
+        const float *acc = a.ws_acc + ((int64_t)first * G + hig) * D + col;
 
         float M = -INFINITY;
-        for (int i = lane; i < n; i += 64)
+        for (int i = t; i < n; i += NT)
             M = fmaxf(M, ml[(int64_t)i * G].x);
         M = wave_max(M);
+        if (lane == 0)
+            red[wave] = M;
+        __syncthreads();
+        M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();
 
-        // Lane i of each 64-partial chunk computes partial i's weight once;
-        // the accumulation loop then broadcasts it with readlane.
+        // Thread i of each NT-partial chunk computes partial i's weight once;
+        // all threads then read it from LDS while accumulating 16-byte pieces.
         float den = 0.f;
-        for (int c = 0; c < n; c += 64) {
+        for (int c = 0; c < n; c += NT) {
             float wgt = 0.f;
-            if (c + lane < n) {
-                const float2 v = ml[(int64_t)(c + lane) * G];
+            if (c + t < n) {
+                const float2 v = ml[(int64_t)(c + t) * G];
                 wgt = (v.x == -INFINITY) ? 0.f : exp2f(v.x - M);
                 den += wgt * v.y;
             }
-            const int cnt = min(64, n - c);
+            wts[t] = wgt;
+            __syncthreads();
+            const int cnt = min(NT, n - c);
 #pragma unroll 4
-            for (int i = 0; i < cnt; ++i) {
-                const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), i));
-                const float *src = acc + (int64_t)(c + i) * G * D;
-#pragma unroll
-                for (int k = 0; k < PER; ++k)
-                    o[k] = fmaf(wi, src[k], o[k]);
+            for (int i = sub; i < cnt; i += NSUB) {
+                const float wi = wts[i];
+                const float4 x = *reinterpret_cast<const float4 *>(acc + (int64_t)(c + i) * G * D);
+                o.x = fmaf(wi, x.x, o.x);
+                o.y = fmaf(wi, x.y, o.y);
+                o.z = fmaf(wi, x.z, o.z);
+                o.w = fmaf(wi, x.w, o.w);
             }
+            __syncthreads();
         }
         den = wave_sum(den);
+        if (lane == 0)
+            red[wave] = den;
+        part[sub][t % LPP] = o;
+        __syncthreads();
+        den = red[0] + red[1] + red[2] + red[3];
         inv = den > 0.f ? 1.f / den : 0.f;
+        if (sub != 0)
+            return;
+#pragma unroll
+        for (int k = 1; k < NSUB; ++k) {
+            const float4 y = part[k][t];
+            o.x += y.x;
+            o.y += y.y;
+            o.z += y.z;
+            o.w += y.w;
+        }
+    } else if (sub != 0) {
+        return;
     }
+    const int64_t obase = row * D + col;
+    const float r[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
     if constexpr (OT == KT_F32) {
-#pragma unroll
-        for (int k = 0; k < PER; ++k)
-            static_cast<float *>(a.out)[obase + k] = o[k] * inv;
+        *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + obase) =
+            make_float4(r[0], r[1], r[2], r[3]);
     } else {
-#pragma unroll
-        for (int k = 0; k < PER; ++k)
-            static_cast<uint16_t *>(a.out)[obase + k] = (uint16_t)f32_to_bf16(o[k] * inv);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + obase) =
+            make_uint2(f32_to_bf16(r[0]) | (f32_to_bf16(r[1]) << 16),
+                       f32_to_bf16(r[2]) | (f32_to_bf16(r[3]) << 16));
     }
 }
 
@@ -100,7 +133,7 @@ __global__ __launch_bounds__(64) void merge_kernel(DecodeArgs a, int block_size)
 hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int block_size,
                         hipStream_t stream)
 {
-    dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_heads)), block(64);
+    dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_heads)), block(kMergeThreads);
     if (out_type == KT_F32 && head_dim == 64)
         hipLaunchKernelGGL((merge_kernel<KT_F32, 64>), grid, block, 0, stream, a, block_size);
     else if (out_type == KT_F32 && head_dim == 128)

@@ -72,8 +72,8 @@ hipError_t decode_mfma_occupancy(int kv_type, int head_dim, int block_size, int 
                                  int *waves_per_cu);
 
 // Log-sum-exp merge of the chunk partials of every segment that more than
-// one chunk touched; zero rows for empty sequences.  Grid (S * H) of one
-// wavefront.
+// one chunk touched; zero rows for empty sequences.  Grid (S * H) of
+// 256-thread workgroups.
 hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int block_size,
                         hipStream_t stream);
 
