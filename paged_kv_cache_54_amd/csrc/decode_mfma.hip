@@ -314,14 +314,20 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
     // Walk the chunk tile by tile: the load cursor runs one tile ahead of the
     // compute cursor, across block and segment boundaries.
     BlockIds ids(a.block_tables, a.max_nb, a.num_blocks, a.err_flag);
-    Cursor cc = locate<BS>(a.seq_lens, a.num_seqs, Hkv, cap, chunk.u0);
+    Cursor cc = chunk.start;
     Cursor lc = cc;
     const int n = chunk.n;                     // units (blocks)
     const int steps = n * HALVES;              // tiles
 
+    // next_load moves the load cursor to tile `k`; past the chunk's last tile
+    // it yields no block (id -1), whose loads read nothing.
     int l_half = 0;
     int l_id = ids.get(lc.s, lc.j);
-    auto next_load = [&]() {
+    auto next_load = [&](int k) {
+        if (k >= steps) {
+            l_id = -1;
+            return;
+        }
         if (++l_half == HALVES) {
             l_half = 0;
             advance<BS>(lc, a.seq_lens, Hkv, cap);
@@ -329,10 +335,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
         }
     };
 
-    auto step = [&](int k, int id, int half, const Tile &t, auto issue_next) {
+    // A tile's segment is started (its query rows loaded) before the loads of
+    // the following tile are issued: loads retire in order, so query loads
+    // issued after them would make the tile wait for the following one.
+    auto pre_step = [&](int k, int half) {
         const int unit = k / HALVES;
         if (half == 0 && (unit == 0 || cc.j == 0))
             begin_segment(cc);
+    };
+    auto step = [&](int k, int id, int half, const Tile &t, auto issue_next) {
+        const int unit = k / HALVES;
         if (id >= 0)
             stage(cc, half, t);
         issue_next();
@@ -347,33 +359,27 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
         }
     };
 
+    // Loads are issued unconditionally (a missing block reads nothing), so the
+    // wait before staging a tile counts exactly the loads issued after it.
     if constexpr (PINGPONG) {
         // Two register tiles: tile k+1 is loaded into the other tile before
         // tile k is waited on, so two tiles are in flight at the wait.
         Tile ta, tb;
         int ida = l_id, ha = l_half;
-        if (ida >= 0)
-            load_tile(ida, lc.kvh, ha, ta);
+        load_tile(ida, lc.kvh, ha, ta);
         for (int k = 0; k < steps; k += 2) {
-            int idb = -1, hb = 0;
-            if (k + 1 < steps) {
-                next_load();
-                idb = l_id;
-                hb = l_half;
-                if (idb >= 0)
-                    load_tile(idb, lc.kvh, hb, tb);
-            }
+            pre_step(k, ha);
+            next_load(k + 1);
+            const int idb = l_id, hb = l_half;
+            load_tile(idb, lc.kvh, hb, tb);
             step(k, ida, ha, ta, [] {});
             if (k + 1 >= steps)
                 break;
-            ida = -1;
-            if (k + 2 < steps) {
-                next_load();
-                ida = l_id;
-                ha = l_half;
-                if (ida >= 0)
-                    load_tile(ida, lc.kvh, ha, ta);
-            }
+            pre_step(k + 1, hb);
+            next_load(k + 2);
+            ida = l_id;
+            ha = l_half;
+            load_tile(ida, lc.kvh, ha, ta);
             step(k + 1, idb, hb, tb, [] {});
         }
     } else {
@@ -382,18 +388,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
         // tile k is computed from LDS.
         Tile t;
         int id = l_id, half = l_half;
-        if (id >= 0)
-            load_tile(id, lc.kvh, half, t);
+        load_tile(id, lc.kvh, half, t);
         for (int k = 0; k < steps; ++k) {
             int id_next = -1, half_next = 0;
+            pre_step(k, half);
             step(k, id, half, t, [&] {
-                if (k + 1 < steps) {
-                    next_load();
-                    id_next = l_id;
-                    half_next = l_half;
-                    if (id_next >= 0)
-                        load_tile(id_next, lc.kvh, half_next, t);
-                }
+                next_load(k + 1);
+                id_next = l_id;
+                half_next = l_half;
+                load_tile(id_next, lc.kvh, half_next, t);
             });
             id = id_next;
             half = half_next;

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a)
 
     // Walk the chunk; the next block's loads are issued before this one is used.
     BlockIds ids(a.block_tables, a.max_nb, a.num_blocks, a.err_flag);
-    Cursor cc = locate<BS>(a.seq_lens, a.num_seqs, Hkv, cap, chunk.u0);
+    Cursor cc = chunk.start;
     Cursor lc = cc;
     const int n = chunk.n;
 

@@ -198,13 +198,16 @@ __device__ __forceinline__ void raise_flag(uint32_t *flag, uint32_t bit)
 // ---------------------------------------------------------------- block walk
 // Buffer resource over one pool block: the block base is wave-uniform, so the
 // descriptor lives in scalar registers and every lane addresses its rows with
-// one loop-invariant 32-bit offset.  Loads past `bytes` return zero.
+// one loop-invariant 32-bit offset.  Loads past the record size return zero
+// without touching memory; id < 0 gives a zero-size resource, so a pipeline
+// can issue the loads of a block that does not exist unconditionally (and the
+// compiler can count outstanding loads exactly).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void *cache, int64_t block_bytes,
                                                              int id)
 {
-    const char *p = static_cast<const char *>(cache) + (int64_t)id * block_bytes;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), 0, (int)block_bytes,
-                                             0x00020000);
+    const char *p = static_cast<const char *>(cache) + (int64_t)(id < 0 ? 0 : id) * block_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(p), 0,
+                                             id < 0 ? 0 : (int)block_bytes, 0x00020000);
 }
 
 // Streaming (nontemporal) buffer loads: voffset per lane, soffset uniform.
@@ -358,23 +361,71 @@ struct BlockIds {
     }
 };
 
-// Chunk [u0, u0 + n) of the work list for wavefront w of W, or n = 0.
+// Chunk [u0, u0 + n) of the work list for wavefront w of W (n = 0: none) and
+// the cursor of its first unit.  Batches of up to 256 sequences read their
+// lengths once, with independent loads, and derive both the total and the
+// start position from registers; larger batches take two passes.
 struct Chunk {
     int64_t u0;
     int n;
+    Cursor start;
 };
 
 template <int BS>
-__device__ __forceinline__ Chunk my_chunk(const DecodeArgs &a, int w, int W)
+__device__ Chunk my_chunk(const DecodeArgs &a, int w, int W)
 {
+    const int S = a.num_seqs, Hkv = a.num_kv_heads;
     const int cap = a.max_nb * BS;
-    const int64_t U = total_units<BS>(a.seq_lens, a.num_seqs, a.num_kv_heads, cap,
-                                      w == 0 ? a.err_flag : nullptr);
+    uint32_t *flag = w == 0 ? a.err_flag : nullptr;
+    if (S > 256) {
+        const int64_t U = total_units<BS>(a.seq_lens, S, Hkv, cap, flag);
+        const int64_t cl = a.chunk_units > 0 ? a.chunk_units : (U + W - 1) / W;
+        const int64_t u0 = (int64_t)w * cl;
+        if (u0 >= U)
+            return Chunk{0, 0, Cursor{}};
+        return Chunk{u0, (int)min(cl, U - u0), locate<BS>(a.seq_lens, S, Hkv, cap, u0)};
+    }
+    const int lane = lane_id();
+    int L[4], nb[4], incl[4], tot[4];
+    bool over = false;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int s = 64 * k + lane;
+        L[k] = (64 * k < S && s < S) ? a.seq_lens[s] : 0;
+    }
+    int64_t U = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        over |= L[k] > cap;
+        L[k] = min(L[k], cap);
+        nb[k] = seq_blocks<BS>(L[k], cap);
+        incl[k] = wave_incl_scan_i(nb[k] * Hkv);
+        tot[k] = __builtin_amdgcn_readlane(incl[k], 63);
+        U += tot[k];
+    }
+    if (flag && __ballot(over))
+        raise_flag(flag, PA_DEVERR_SEQ_LEN);
     const int64_t cl = a.chunk_units > 0 ? a.chunk_units : (U + W - 1) / W;
     const int64_t u0 = (int64_t)w * cl;
     if (u0 >= U)
-        return Chunk{0, 0};
-    return Chunk{u0, (int)min(cl, U - u0)};
+        return Chunk{0, 0, Cursor{}};
+    Cursor cur{S, 0, 0, 0, 0};
+    int64_t base = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (base + tot[k] > u0) {
+            const int f = __builtin_ctzll(__ballot(base + incl[k] > u0));
+            cur.s = 64 * k + f;
+            cur.nb = __builtin_amdgcn_readlane(nb[k], f);
+            cur.L = __builtin_amdgcn_readlane(L[k], f);
+            const int64_t r = u0 - (base + __builtin_amdgcn_readlane(incl[k], f) - cur.nb * Hkv);
+            cur.kvh = (int)(r / cur.nb);
+            cur.j = (int)(r % cur.nb);
+            break;
+        }
+        base += tot[k];
+    }
+    return Chunk{u0, (int)min(cl, U - u0), cur};
 }
 
 // Slot of chunk w's result for segment g, and the record the merge reads:
