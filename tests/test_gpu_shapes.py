@@ -101,3 +101,24 @@ def test_repeated_calls_reuse_workspace():
                                partition_tokens=P, workspace=ws)
             torch.cuda.synchronize()
             assert torch.equal(fresh, reused)
+
+
+@pytest.mark.parametrize("variant", [pa.VARIANT_VALU, pa.VARIANT_MFMA])
+def test_segments_split_into_many_parts(variant):
+    """One-block chunks over sequences of up to 313 blocks: the merge combines
+    more partials per row than it has threads (several passes over its
+    weights), next to a short sequence that one chunk covers."""
+    b = workloads.make_batch("llama3_8b_bf16", device=DEV, num_seqs=3, num_heads=8,
+                             num_kv_heads=2, lens=("fixed", 5000), max_len=5008,
+                             poison=True, seed=41)
+    lens = torch.tensor([5000, 7, 4113], dtype=torch.int32)    # shortened: tables stay valid
+    b.seq_lens.copy_(lens.to(DEV))
+    ref = oracle.decode(b.q.cpu(), b.key_pool.cpu(), b.value_pool.cpu(), b.block_tables.cpu(),
+                        lens, b.scale)
+    for P in (16, 32, 0):
+        print("CASE many parts variant", variant, "P", P, flush=True)
+        out = torch.full_like(b.q, float("nan"))
+        pa.decode(b.q, b.key_pool, b.value_pool, b.block_tables, b.seq_lens, b.scale, out=out,
+                  variant=variant, partition_tokens=P)
+        torch.cuda.synchronize()
+        check_close(out, ref, "bf16", f"many parts v{variant} P{P}")
