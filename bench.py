@@ -113,6 +113,7 @@ class HipEvents:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.ev = []
         for _ in range(n):
             e = ctypes.c_void_p()
@@ -126,6 +127,10 @@ class HipEvents:
         if rc != 0:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
+
+    def record(self, k, stream):
+        if self.lib.hipEventRecord(ctypes.c_void_p(self.ev[k]), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def close(self):
         for e in self.ev:
@@ -169,6 +174,106 @@ def cpu_baseline(b, budget_s):
                       f"{t_total:.1f} s; fp64 C oracle, OpenMP over query rows"}
 
 
+def block_cpu_baseline(case, budget_s):
+    """The block oracle, as it stands, on a bounded sample: whole calls over a
+    prefix of the regions, repeated until about budget_s seconds; GB/s of the
+    bytes the GPU kernel moves for the same work."""
+    import oracle.blocks as ob
+    R = min(len(case.regions), 4)
+    regs = [r.cpu().numpy().reshape(-1) for r in case.regions[:R]]
+    items = case.items.numpy()
+    per_region = len(items) * case.block_bytes * (1 if case.op == "zero" else 2)
+    done, t_total = 0, 0.0
+    while t_total < budget_s and done < 1000:
+        t0 = time.perf_counter()
+        if case.op == "zero":
+            ob.zero_blocks(regs, items, case.block_bytes, case.block_bytes, case.num_blocks)
+        else:
+            ob.copy_blocks(regs, regs, items, case.block_bytes, case.block_bytes,
+                           case.num_blocks, case.num_blocks)
+        t_total += time.perf_counter() - t0
+        done += 1
+    return {"value": round(done * R * per_region / t_total / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} whole calls over {R} of the {len(case.regions)} regions in "
+                      f"{t_total:.1f} s; numpy slicing, one thread"}
+
+
+def bench_blocks(args):
+    """One launch of pa_zero_blocks / pa_copy_blocks per step over the block
+    workload; value = bytes the op must move (written, plus read for a copy)
+    per second of wall time."""
+    import torch
+
+    import paged_kv_cache_54_amd as pa
+    import workloads
+
+    dev = "cuda:0"
+    case = workloads.make_block_case(args.workload, device=dev)
+    regs = pa.region_table(case.regions)
+    items = case.items.to(dev)
+    lib = pa._load()
+    stream = torch.cuda.current_stream().cuda_stream
+    n = case.items.shape[0]
+    R = len(case.regions)
+    nbytes = n * R * case.block_bytes * (1 if case.op == "zero" else 2)
+    ev = HipEvents(2 * args.steps)
+    o = pa._opts()
+    by = ctypes.byref
+
+    def step(k=None):
+        if k is not None:
+            ev.record(2 * k, stream)
+        if case.op == "zero":
+            rc = lib.pa_zero_blocks(items.data_ptr(), n, regs.bases.data_ptr(), R,
+                                    regs.block_stride, regs.block_bytes, regs.num_blocks, by(o),
+                                    stream)
+        else:
+            rc = lib.pa_copy_blocks(items.data_ptr(), n, regs.bases.data_ptr(),
+                                    regs.bases.data_ptr(), R, regs.block_stride,
+                                    regs.block_bytes, regs.num_blocks, regs.num_blocks, by(o),
+                                    stream)
+        if rc:
+            raise pa.PaError("block op", rc)
+        if k is not None:
+            ev.record(2 * k + 1, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(ev.elapsed_ms(2 * k, 2 * k + 1) for k in range(args.steps)) / args.steps
+    ev.close()
+    ms = wall / args.steps * 1e3
+    value = nbytes / (ms * 1e-3) / 1e9
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    kname = "block_op_kernel<true>" if case.op == "copy" else "block_op_kernel<false>"
+    res = {
+        "metric": f"block {'clear' if case.op == 'zero' else 'copy'}: achieved HBM GB/s "
+                  f"({'bytes written' if case.op == 'zero' else 'bytes read + written'})",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": args.workload, "op": case.op, "items": n, "regions": R,
+                   "block_bytes": case.block_bytes, "num_blocks": case.num_blocks},
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel_ms": round(kernel_ms, 5),
+                     "kernel_ms_from": f"HIP events around each of the {args.steps} launches",
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    res["cpu_baseline"] = None if args.no_cpu_baseline else block_cpu_baseline(
+        case, args.cpu_budget_s)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -193,6 +298,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
+    if args.workload in workloads.BLOCK_CONFIGS:
+        bench_blocks(args)
         return
     b = workloads.make_batch(args.workload, device=dev)
     P = args.partition_tokens if args.partition_tokens is not None else (b.partition_tokens or 0)

@@ -82,6 +82,7 @@ typedef enum pa_status {
 #define PA_DEVERR_BLOCK_ID 0x1u  /* block id outside [0, num_blocks): block skipped */
 #define PA_DEVERR_SEQ_LEN 0x2u   /* seq_len > table capacity: clamped */
 #define PA_DEVERR_SLOT 0x4u      /* slot >= num_blocks * block_size: token not written */
+#define PA_DEVERR_REGION 0x8u    /* block-op region base NULL or not 16-byte aligned: skipped */
 
 typedef struct pa_tensor {
     void *data;         /* device pointer (16-byte aligned) */
@@ -178,6 +179,62 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
 int pa_decode_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
                              const pa_tensor *block_tables, const pa_opts *opts,
                              size_t *bytes);
+
+/*
+ * Block maintenance.  A "region" is one cache of the pool layout, for example
+ * the K cache or the V cache of one layer: block b of region r occupies the
+ * bytes [region_bases[r] + b * block_stride, + block_bytes).  Every region of
+ * one call has the same block geometry.  For the caches of this library
+ * ([NB, bs, Hkv, D], dense) block_stride = block_bytes = bs * Hkv * D * elt.
+ *
+ * The id and base arrays are read by the kernel, not by the host: they may be
+ * device memory or host memory the device can read (hipHostMalloc /
+ * pinned), which hands freshly chosen ids to the GPU with no copy and no
+ * synchronisation.  They must stay unchanged until the queued work has run.
+ * Alignment: ids 4 bytes (pairs 8 bytes), bases 8 bytes; every region base
+ * must be 16-byte aligned (a NULL or misaligned base is skipped and raises
+ * PA_DEVERR_REGION).  block_stride and block_bytes are multiples of 16, with
+ * 0 < block_bytes <= block_stride.  An id outside [0, num_blocks) is skipped
+ * and raises PA_DEVERR_BLOCK_ID.  opts may be NULL; only err_flag is used.
+ * num_ids (num_pairs) == 0 or num_regions == 0 queues nothing.
+ */
+
+/*
+ * pa_zero_blocks -- clear (write zero bytes over) every listed block in every
+ * region, in one launch.  A block that another layer type used before can
+ * hold bit patterns that are NaN/Inf in the cache dtype; clearing newly
+ * allocated blocks before attention uses them keeps such bits out of any
+ * kernel that masks by multiplying with zero (vLLM v0.17.1 release notes,
+ * fix #35219: batched clearing over precomputed cache segment addresses,
+ * block ids passed through pinned memory, no synchronisation).
+ *
+ *   block_ids     [num_ids] int32; duplicates allowed
+ */
+int pa_zero_blocks(const int32_t *block_ids, int64_t num_ids, void *const *region_bases,
+                   int32_t num_regions, int64_t block_stride, int64_t block_bytes,
+                   int64_t num_blocks, const pa_opts *opts, void *hip_stream);
+
+/*
+ * pa_copy_blocks -- copy whole blocks: for each pair (src, dst), block src of
+ * src region r is copied over block dst of dst region r, for every region.
+ * Uses: copy-on-write of a block shared by a common prefix before one
+ * sequence writes into it (vLLM internals blog, section 1, the page-table
+ * analogy and figure 1), and moving a preempted sequence's blocks between the
+ * GPU pool and a host pool and back (swap out / swap in, vLLM concept page,
+ * "15-minute deep dive", scheduler item); a host pool must be device-readable
+ * (and -writable for swap out) pinned memory, and that traffic is bound by
+ * the host link.
+ *
+ *   block_pairs   [num_pairs, 2] int32: (src block, dst block); src ids are
+ *                 checked against src_num_blocks, dst ids against dst_num_blocks
+ *   src_bases, dst_bases  [num_regions] each
+ * Contract: no dst block of a call is also a src block or a second dst block
+ * of that call in the same memory (the order of the copies is unspecified).
+ */
+int pa_copy_blocks(const int32_t *block_pairs, int64_t num_pairs, const void *const *src_bases,
+                   void *const *dst_bases, int32_t num_regions, int64_t block_stride,
+                   int64_t block_bytes, int64_t src_num_blocks, int64_t dst_num_blocks,
+                   const pa_opts *opts, void *hip_stream);
 
 /* Static description of a status code. */
 const char *pa_status_string(int status);

@@ -10,6 +10,9 @@ fallback implementation.
     kv_append(k, v, slot_mapping, key_cache, value_cache, k_scale=1, v_scale=1)
     decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, ...)
     decode_workspace_size(q, key_cache, block_tables, ...)
+    zero_blocks(block_ids, regions)
+    copy_blocks(block_pairs, src_regions, dst_regions)
+    region_table(caches, device)
 """
 from __future__ import annotations
 
@@ -19,16 +22,17 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["kv_append", "decode", "decode_workspace_size", "PaError", "status_string",
-           "version", "library_path", "VARIANT_AUTO", "VARIANT_VALU", "VARIANT_MFMA",
-           "DEVERR_BLOCK_ID", "DEVERR_SEQ_LEN", "DEVERR_SLOT"]
+__all__ = ["kv_append", "decode", "decode_workspace_size", "zero_blocks", "copy_blocks",
+           "region_table", "Regions", "PaError", "status_string", "version", "library_path",
+           "VARIANT_AUTO", "VARIANT_VALU", "VARIANT_MFMA", "DEVERR_BLOCK_ID", "DEVERR_SEQ_LEN",
+           "DEVERR_SLOT", "DEVERR_REGION"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3, PA_I32, PA_I64 = 0, 1, 2, 3, 4
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
-DEVERR_BLOCK_ID, DEVERR_SEQ_LEN, DEVERR_SLOT = 0x1, 0x2, 0x4
+DEVERR_BLOCK_ID, DEVERR_SEQ_LEN, DEVERR_SLOT, DEVERR_REGION = 0x1, 0x2, 0x4, 0x8
 
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
            torch.float8_e4m3fn: PA_FP8_E4M3, torch.int32: PA_I32, torch.int64: PA_I64}
@@ -83,6 +87,11 @@ def _load():
         lib.pa_status_string.argtypes = [ctypes.c_int]
         lib.pa_version.restype = ctypes.c_int
         lib.pa_version.argtypes = []
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        lib.pa_zero_blocks.restype = ctypes.c_int
+        lib.pa_zero_blocks.argtypes = [vp, i64, vp, i32, i64, i64, i64, P(PaOpts), vp]
+        lib.pa_copy_blocks.restype = ctypes.c_int
+        lib.pa_copy_blocks.argtypes = [vp, i64, vp, vp, i32, i64, i64, i64, i64, P(PaOpts), vp]
         _lib = lib
     return _lib
 
@@ -189,3 +198,77 @@ def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, k
                                       ctypes.byref(describe(out)), ctypes.byref(o),
                                       _stream(stream)))
     return out
+
+
+class Regions:
+    """A set of caches with one block geometry, as the block operations see
+    it: ``bases`` is an int64 tensor of the caches' block-0 addresses (on the
+    device, or in pinned host memory), ``block_stride`` and ``block_bytes`` in
+    bytes, ``num_blocks`` blocks per cache.  Keeps the caches alive."""
+
+    def __init__(self, bases, block_stride, block_bytes, num_blocks, caches=()):
+        self.bases = bases
+        self.block_stride = int(block_stride)
+        self.block_bytes = int(block_bytes)
+        self.num_blocks = int(num_blocks)
+        self.caches = tuple(caches)
+
+
+def region_table(caches, device=None, pin=False) -> Regions:
+    """Regions of cache tensors [NB, ...] that share a shape and dtype (block b
+    = index b of dim 0, contiguous).  The address table goes to ``device``
+    (default: the caches' device) or, with ``pin=True``, to pinned host
+    memory."""
+    caches = list(caches)
+    if not caches:
+        raise ValueError("no caches")
+    c0 = caches[0]
+    for c in caches:
+        if c.shape != c0.shape or c.dtype != c0.dtype or not c.is_contiguous():
+            raise ValueError("caches must be contiguous and share shape and dtype")
+    stride = c0[0].numel() * c0.element_size()
+    addrs = torch.tensor([c.data_ptr() for c in caches], dtype=torch.int64)
+    if pin:
+        bases = addrs.pin_memory()
+    else:
+        bases = addrs.to(device if device is not None else c0.device)
+    return Regions(bases, stride, stride, c0.shape[0], caches)
+
+
+def _dev_ptr(t: torch.Tensor, what: str) -> int:
+    if not (t.is_cuda or t.is_pinned()):
+        raise TypeError(f"{what} must be device memory or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t.data_ptr()
+
+
+def zero_blocks(block_ids: torch.Tensor, regions: Regions, err_flag=None, stream=None):
+    """Clear blocks ``block_ids`` (int32, device or pinned host) in every region."""
+    if block_ids.dtype != torch.int32:
+        raise TypeError("block_ids must be int32")
+    lib = _load()
+    o = _opts(err_flag=err_flag)
+    _check("pa_zero_blocks",
+           lib.pa_zero_blocks(_dev_ptr(block_ids, "block_ids"), block_ids.numel(),
+                              _dev_ptr(regions.bases, "region bases"), regions.bases.numel(),
+                              regions.block_stride, regions.block_bytes, regions.num_blocks,
+                              ctypes.byref(o), _stream(stream)))
+
+
+def copy_blocks(block_pairs: torch.Tensor, src: Regions, dst: Regions, err_flag=None,
+                stream=None):
+    """Copy block pairs[i, 0] of ``src`` over block pairs[i, 1] of ``dst``, in
+    every region (``src`` and ``dst`` share the geometry)."""
+    if block_pairs.dtype != torch.int32 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise TypeError("block_pairs must be int32 [n, 2]")
+    if (src.block_stride, src.block_bytes) != (dst.block_stride, dst.block_bytes) or \
+            src.bases.numel() != dst.bases.numel():
+        raise ValueError("src and dst regions differ in geometry")
+    lib = _load()
+    o = _opts(err_flag=err_flag)
+    _check("pa_copy_blocks",
+           lib.pa_copy_blocks(_dev_ptr(block_pairs, "block_pairs"), block_pairs.shape[0],
+                              _dev_ptr(src.bases, "src bases"), _dev_ptr(dst.bases, "dst bases"),
+                              dst.bases.numel(), dst.block_stride, dst.block_bytes,
+                              src.num_blocks, dst.num_blocks, ctypes.byref(o), _stream(stream)))

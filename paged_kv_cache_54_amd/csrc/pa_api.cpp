@@ -208,6 +208,62 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
     return PA_OK;
 }
 
+// Shared validation and launch of pa_zero_blocks (src_bases == NULL) and
+// pa_copy_blocks.
+int block_op(const int32_t *ids, int64_t n, const void *const *src_bases,
+             void *const *dst_bases, int32_t num_regions, int64_t block_stride,
+             int64_t block_bytes, int64_t src_num_blocks, int64_t dst_num_blocks,
+             const pa_opts *opts, void *hip_stream)
+{
+    const bool copy = src_bases != nullptr;
+    if (n < 0 || num_regions < 0)
+        return PA_ERR_SHAPE;
+    if (n == 0 || num_regions == 0)
+        return PA_OK;
+    if (!ids || !dst_bases)
+        return PA_ERR_NULL;
+    if (block_stride <= 0 || block_bytes <= 0 || block_bytes > block_stride ||
+        dst_num_blocks <= 0)
+        return PA_ERR_SHAPE;
+    if (block_stride % 16 || block_bytes % 16)
+        return PA_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(ids) % (copy ? 8 : 4) ||
+        reinterpret_cast<uintptr_t>(dst_bases) % 8 ||
+        reinterpret_cast<uintptr_t>(src_bases) % 8)
+        return PA_ERR_ALIGN;
+    // every addressed byte offset must fit int64
+    const int64_t max_blocks = dst_num_blocks > src_num_blocks ? dst_num_blocks : src_num_blocks;
+    if (max_blocks > INT64_MAX / block_stride)
+        return PA_ERR_UNSUPPORTED;
+
+    BlockOpArgs a;
+    a.ids = ids;
+    a.dst_bases = dst_bases;
+    a.src_bases = src_bases;
+    a.err_flag = opts ? opts->err_flag : nullptr;
+    a.num_items = n;
+    a.block_stride = block_stride;
+    a.block_bytes = block_bytes;
+    a.dst_num_blocks = dst_num_blocks;
+    a.src_num_blocks = copy ? src_num_blocks : 0;
+    a.chunks = (block_bytes + block_op_chunk_bytes() - 1) / block_op_chunk_bytes();
+    a.num_regions = num_regions;
+    // Items per workgroup: enough workgroups to fill the device several times
+    // over, but each reads its ids (possibly from host memory) only once.
+    int cus = 0, rc;
+    if ((rc = device_cu_count(&cus)))
+        return rc;
+    const int64_t units = n * num_regions * a.chunks;
+    const int64_t target = 8 * (int64_t)cus;
+    int64_t g = units / target;
+    a.group_items = (int32_t)(g < 1 ? 1 : (g > kMaxGroupItems ? kMaxGroupItems : g));
+    const int64_t groups = (n + a.group_items - 1) / a.group_items;
+    if (groups > INT32_MAX / ((int64_t)num_regions * a.chunks))
+        return PA_ERR_UNSUPPORTED;
+    hipError_t e = launch_block_op(a, copy, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -289,6 +345,27 @@ int pa_kv_append(const pa_tensor *k, const pa_tensor *v, const pa_tensor *slot_m
     a.v_inv_scale = 1.0f / vs;
     hipError_t e = launch_kv_append(a, in_t, cache_t, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+int pa_zero_blocks(const int32_t *block_ids, int64_t num_ids, void *const *region_bases,
+                   int32_t num_regions, int64_t block_stride, int64_t block_bytes,
+                   int64_t num_blocks, const pa_opts *opts, void *hip_stream)
+{
+    return block_op(block_ids, num_ids, nullptr, region_bases, num_regions, block_stride,
+                    block_bytes, 0, num_blocks, opts, hip_stream);
+}
+
+int pa_copy_blocks(const int32_t *block_pairs, int64_t num_pairs, const void *const *src_bases,
+                   void *const *dst_bases, int32_t num_regions, int64_t block_stride,
+                   int64_t block_bytes, int64_t src_num_blocks, int64_t dst_num_blocks,
+                   const pa_opts *opts, void *hip_stream)
+{
+    if (num_pairs > 0 && num_regions > 0 && !src_bases)
+        return PA_ERR_NULL;
+    if (src_num_blocks <= 0 && num_pairs > 0)
+        return PA_ERR_SHAPE;
+    return block_op(block_pairs, num_pairs, src_bases, dst_bases, num_regions, block_stride,
+                    block_bytes, src_num_blocks, dst_num_blocks, opts, hip_stream);
 }
 
 int pa_decode_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,

@@ -50,6 +50,26 @@ struct AppendArgs {
     float v_inv_scale;
 };
 
+// Whole-block clear or copy over a set of regions (caches): block b of region
+// r is bytes [bases[r] + b * block_stride, + block_bytes).  Items are block ids
+// (clear) or (src, dst) id pairs (copy); each workgroup handles up to
+// group_items consecutive items x one region x one chunk of the block.
+constexpr int kMaxGroupItems = 64;
+
+struct BlockOpArgs {
+    const int32_t *ids;          // [num_items] or [num_items, 2]; device-readable
+    void *const *dst_bases;      // [num_regions]; device-readable
+    const void *const *src_bases;// [num_regions] (copy only)
+    uint32_t *err_flag;
+    int64_t num_items;
+    int64_t block_stride;        // bytes
+    int64_t block_bytes;         // bytes per block per region, multiple of 16
+    int64_t dst_num_blocks, src_num_blocks;
+    int64_t chunks;              // ceil(block_bytes / chunk bytes)
+    int32_t num_regions;
+    int32_t group_items;         // 1 .. kMaxGroupItems
+};
+
 // Launchers (defined in the .hip translation units).  Each returns a
 // hipError_t from hipGetLastError() after the launch.
 hipError_t launch_kv_append(const AppendArgs &a, int in_type, int cache_type,
@@ -76,5 +96,9 @@ hipError_t decode_mfma_occupancy(int kv_type, int head_dim, int block_size, int 
 // 256-thread workgroups.
 hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int block_size,
                         hipStream_t stream);
+
+// Block clear (copy = false) or copy; chunk bytes per workgroup pass.
+hipError_t launch_block_op(const BlockOpArgs &a, bool copy, hipStream_t stream);
+int64_t block_op_chunk_bytes();
 
 }  // namespace pa

@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["pa_kv_append", "pa_decode", "pa_decode_workspace_size", "pa_opts_init",
-         "pa_status_string", "pa_version"])
+         "pa_status_string", "pa_version", "pa_zero_blocks", "pa_copy_blocks"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -193,3 +193,28 @@ def test_append_validation_errors():
     assert call_append(k, k, slots, c8, c8, opts(v_scale=float("inf"))) == PA_ERR_UNSUPPORTED
     assert call_append(desc([4, 2, 64], BF16, data=FAKE + 2), k, slots, cache, cache) \
         == PA_ERR_ALIGN
+
+
+def test_block_op_validation_errors():
+    L = lib()
+    ids, bases = FAKE, FAKE + 64
+    # nothing to do: no ids or no regions
+    assert L.pa_zero_blocks(ids, 0, bases, 4, 4096, 4096, 100, None, None) == PA_OK
+    assert L.pa_zero_blocks(ids, 5, bases, 0, 4096, 4096, 100, None, None) == PA_OK
+    assert L.pa_copy_blocks(ids, 0, bases, bases, 4, 4096, 4096, 100, 100, None, None) == PA_OK
+    assert L.pa_zero_blocks(None, 5, bases, 4, 4096, 4096, 100, None, None) == PA_ERR_NULL
+    assert L.pa_zero_blocks(ids, 5, None, 4, 4096, 4096, 100, None, None) == PA_ERR_NULL
+    assert L.pa_copy_blocks(ids, 5, None, bases, 4, 4096, 4096, 100, 100, None, None) \
+        == PA_ERR_NULL
+    assert L.pa_zero_blocks(ids, -1, bases, 4, 4096, 4096, 100, None, None) == PA_ERR_SHAPE
+    assert L.pa_zero_blocks(ids, 5, bases, 4, 0, 16, 100, None, None) == PA_ERR_SHAPE
+    assert L.pa_zero_blocks(ids, 5, bases, 4, 4096, 8192, 100, None, None) == PA_ERR_SHAPE
+    assert L.pa_zero_blocks(ids, 5, bases, 4, 4096, 4096, 0, None, None) == PA_ERR_SHAPE
+    assert L.pa_copy_blocks(ids, 5, bases, bases, 4, 4096, 4096, 0, 100, None, None) \
+        == PA_ERR_SHAPE
+    assert L.pa_zero_blocks(ids, 5, bases, 4, 4096, 4008, 100, None, None) == PA_ERR_ALIGN
+    assert L.pa_zero_blocks(ids, 5, bases, 4, 4100, 4096, 100, None, None) == PA_ERR_ALIGN
+    assert L.pa_zero_blocks(ids + 2, 5, bases, 4, 4096, 4096, 100, None, None) == PA_ERR_ALIGN
+    assert L.pa_copy_blocks(ids + 4, 5, bases, bases, 4, 4096, 4096, 100, 100, None, None) \
+        == PA_ERR_ALIGN                                                  # pairs need 8 bytes
+    assert L.pa_zero_blocks(ids, 5, bases + 4, 4, 4096, 4096, 100, None, None) == PA_ERR_ALIGN

@@ -273,3 +273,73 @@ def _poison(key_pool, value_pool, tables, lens, bs):
     mask = mask.to(key_pool.device)
     key_pool[mask] = float("nan")
     value_pool[mask] = float("nan")
+
+
+# --------------------------------------------------------------------------
+# Block-maintenance workloads: clearing newly allocated blocks and copying
+# blocks.  A workload is a set of regions (caches) that share one block
+# geometry -- ``layers`` layers x {K, V}, each a pool of ``num_blocks`` blocks of
+# block_size x kv_heads x head_dim elements -- and a list of block ids (clear)
+# or (src, dst) pairs (copy).
+#
+# The clearing sizes follow the vLLM v0.17.1 notes (fix #35219), which give
+# only totals: ~515 blocks (~920 MiB) cleared for a prefill step, ~30 for a
+# decode step.  The geometry is a reading chosen to match ~1.8 MiB per block:
+# 15 attention layers x {K, V} x 64 tokens x 2 KV heads x 256 dims in bf16
+# (64 KiB per cache block, 1.875 MiB per block over all caches).
+# Copy-on-write uses the Llama-3-8B-shaped cache (32 layers x {K, V}, 16 tokens
+# x 8 KV heads x 128 dims, bf16: 32 KiB per cache block), one copied block per
+# sequence of a 256-sequence batch.
+# --------------------------------------------------------------------------
+BLOCK_CONFIGS = {
+    "block_zero_prefill": dict(op="zero", layers=15, block_size=64, kv_heads=2, head_dim=256,
+                               elem_bytes=2, num_blocks=2048, items=515),
+    "block_zero_decode": dict(op="zero", layers=15, block_size=64, kv_heads=2, head_dim=256,
+                              elem_bytes=2, num_blocks=2048, items=30),
+    "block_copy_cow": dict(op="copy", layers=32, block_size=16, kv_heads=8, head_dim=128,
+                           elem_bytes=2, num_blocks=4096, items=256),
+}
+BLOCK_SEEDS = {name: len(CONFIGS) + i + 1 for i, name in enumerate(BLOCK_CONFIGS)}
+
+
+@dataclasses.dataclass
+class BlockCase:
+    name: str
+    op: str                       # "zero" or "copy"
+    regions: list                 # uint8 tensors [num_blocks, block_bytes], one per cache
+    items: torch.Tensor           # int32 [n] block ids, or [n, 2] (src, dst) pairs
+    block_bytes: int
+    num_blocks: int
+
+    @property
+    def region_count(self) -> int:
+        return len(self.regions)
+
+
+def make_block_case(name: str, seed: Optional[int] = None, device="cpu",
+                    **overrides) -> BlockCase:
+    """Draw the regions (random bytes, no zero byte, so a cleared byte is
+    always visible) and the items of block workload ``name``.  Clear: distinct
+    random ids.  Copy: distinct sources and distinct destinations, disjoint
+    from each other."""
+    cfg = dict(BLOCK_CONFIGS[name])
+    cfg.update(overrides)
+    seed = BLOCK_SEEDS.get(name, 0) if seed is None else seed
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    NB, n = cfg["num_blocks"], cfg["items"]
+    block_bytes = cfg["block_size"] * cfg["kv_heads"] * cfg["head_dim"] * cfg["elem_bytes"]
+    perm = torch.randperm(NB, generator=gen)
+    if cfg["op"] == "zero":
+        if n > NB:
+            raise ValueError("more ids than blocks")
+        items = perm[:n].to(torch.int32)
+    else:
+        if 2 * n > NB:
+            raise ValueError("more pairs than fit the pool")
+        items = torch.stack([perm[:n], perm[n:2 * n]], dim=1).to(torch.int32).contiguous()
+    regions = []
+    dev_gen = torch.Generator(device=device).manual_seed(seed + 1000)
+    for _ in range(2 * cfg["layers"]):
+        regions.append(torch.randint(1, 256, (NB, block_bytes), dtype=torch.uint8,
+                                     device=device, generator=dev_gen))
+    return BlockCase(name, cfg["op"], regions, items, block_bytes, NB)
