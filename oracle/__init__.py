@@ -14,6 +14,10 @@ file's header:
                  principles"): concatenate the blocks the page table names, cut
                  to seq_len rows, softmax(scale * q.K^T).V in fp64; query head h
                  reads KV head h // (H / Hkv).
+  decode_multi -- several new query tokens per sequence (speculative
+                 decoding's verify step): token i of the sequence's q_len new
+                 tokens attends causally to the first L - q_len + i + 1
+                 positions; each row is ``decode`` over that prefix.
   kv_append   -- write each new row at block = slot // bs, offset = slot % bs
                  (bit copy; e4m3 caches store nearest-e4m3(x *f32 (1/scale))).
   e4m3_*      -- OCP E4M3FN codec from the format definition.
@@ -50,6 +54,10 @@ def _load():
         lib.oracle_decode.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_dbl, c_dbl, c_vp, c_i64,
                                       c_vp, c_i64, c_i64, c_i64, c_i64, c_i64, c_i64, c_dbl,
                                       c_vp, c_i64, c_vp, c_vp, c_i64]
+        lib.oracle_decode_multi.restype = c_i32
+        lib.oracle_decode_multi.argtypes = [c_vp, c_i32, c_vp, c_vp, c_i32, c_dbl, c_dbl, c_vp,
+                                            c_i64, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_i64,
+                                            c_i64, c_i64, c_dbl, c_vp, c_i64, c_vp]
         lib.oracle_kv_append.restype = c_i32
         lib.oracle_kv_append.argtypes = [c_vp, c_vp, c_i32, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
                                          c_i32, c_i64, c_i64, ctypes.c_float, ctypes.c_float]
@@ -136,6 +144,45 @@ def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, k_scale=1.0
     if rows is None:
         out = out.reshape(S, H, D)
     return (out, w) if with_weights else out
+
+
+def decode_multi(q, query_start_loc, key_cache, value_cache, block_tables, seq_lens, scale,
+                 k_scale=1.0, v_scale=1.0, rows=None):
+    """fp64 paged attention for several new query tokens per sequence.
+
+    q [T, H, D]; query_start_loc int32 [S+1] (sequence s owns tokens
+    qsl[s] .. qsl[s+1]-1, its last q_len positions, each attending causally);
+    the rest as in ``decode``.  ``rows``: optional flat ids token*H + h.
+    Returns float64 [T, H, D] (or [len(rows), D])."""
+    lib = _load()
+    qa, q_dt = _as_host_array(q)
+    ka, kv_dt = _as_host_array(key_cache)
+    va, kv_dt2 = _as_host_array(value_cache)
+    if kv_dt != kv_dt2:
+        raise TypeError("key and value caches differ in dtype")
+    host = lambda x: np.ascontiguousarray(np.asarray(x.cpu() if torch.is_tensor(x) else x,
+                                                     dtype=np.int32))
+    bt, sl, qsl = host(block_tables), host(seq_lens), host(query_start_loc)
+    T, H, D = qa.shape
+    NB, bs, Hkv, D2 = ka.shape
+    S = sl.shape[0]
+    if D2 != D or va.shape != ka.shape or bt.shape[0] != S or qsl.shape != (S + 1,):
+        raise ValueError("shape mismatch")
+    if rows is None:
+        n_rows, rows_arr = T * H, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n_rows = rows_arr.size
+    out = np.zeros((n_rows, D), dtype=np.float64)
+    rc = lib.oracle_decode_multi(_ptr(qa), q_dt, _ptr(ka), _ptr(va), kv_dt, float(k_scale),
+                                 float(v_scale), _ptr(bt), bt.shape[1], _ptr(sl), _ptr(qsl), S, T,
+                                 H, Hkv, D, bs, NB, float(scale),
+                                 None if rows_arr is None else _ptr(rows_arr), n_rows, _ptr(out))
+    if rc:
+        raise ValueError(f"oracle_decode_multi: {_ERRORS.get(rc, rc)}")
+    if rows is None:
+        out = out.reshape(T, H, D)
+    return out
 
 
 def kv_append(k, v, slot_mapping, key_cache, value_cache, k_scale=1.0, v_scale=1.0):

@@ -23,6 +23,11 @@
  *     named on the concept page).  Everything is done in double precision,
  *     with the softmax taken as exp(z - max z) / sum exp(z - max z).
  *
+ *   oracle_decode_multi -- several new query tokens per sequence (the verify
+ *     step of speculative decoding): query token i of a sequence with q_len
+ *     new tokens attends causally to the first L - q_len + i + 1 tokens; each
+ *     row is oracle_decode over that prefix.
+ *
  *   oracle_kv_append -- write each new token's K and V row into the slot that
  *     slot_mapping names (block = slot / block_size, offset = slot %
  *     block_size): a bit copy for f32 and bf16 caches; for an 8-bit cache the
@@ -264,6 +269,71 @@ int oracle_decode(const void *q, int q_dtype, const void *key_cache, const void 
         free(K);
         free(V);
         free(z);
+    }
+    return status;
+}
+
+/* ---------------------------------------------------------------- multi-token decode */
+
+/*
+ * Several new query tokens per sequence (speculative decoding's verify step,
+ * P-EAGLE page: the target model checks K drafted tokens in one pass).
+ * query_start_loc [S+1]: sequence s owns query tokens qsl[s] .. qsl[s+1]-1 of
+ * q [T, H, D]; they are the sequence's last q_len = qsl[s+1] - qsl[s]
+ * positions, so query token i (0-based within the sequence) sits at position
+ * L - q_len + i and attends to positions 0 .. L - q_len + i (causal language
+ * modelling: a token sees itself and everything before it).  Each output row
+ * is exactly oracle_decode of that one query row over the sequence cut to
+ * L - q_len + i + 1 tokens.  rows: flat ids token * H + h (NULL = all T * H).
+ */
+int oracle_decode_multi(const void *q, int q_dtype, const void *key_cache, const void *value_cache,
+                        int kv_dtype, double k_scale, double v_scale, const int32_t *block_tables,
+                        int64_t max_nb, const int32_t *seq_lens, const int32_t *query_start_loc,
+                        int64_t S, int64_t T, int64_t H, int64_t Hkv, int64_t D, int64_t bs,
+                        int64_t NB, double scale, const int64_t *rows, int64_t n_rows, double *out)
+{
+    if (S < 0 || T < 0 || H <= 0 || D <= 0)
+        return OR_EARG;
+    if (query_start_loc[0] != 0 || query_start_loc[S] != T)
+        return OR_EARG;
+    for (int64_t s = 0; s < S; ++s)
+        if (query_start_loc[s + 1] < query_start_loc[s])
+            return OR_EARG;
+    if (rows == NULL)
+        n_rows = T * H;
+    const size_t qelt = q_dtype == OR_F32 ? 4 : 2;
+    int status = OR_OK;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t row = rows ? rows[r] : r;
+        if (row < 0 || row >= T * H) {
+#pragma omp atomic write
+            status = OR_EARG;
+            continue;
+        }
+        const int64_t tok = row / H, h = row % H;
+        int64_t s = 0;
+        while (query_start_loc[s + 1] <= tok)      /* the sequence owning this token */
+            ++s;
+        const int64_t i = tok - query_start_loc[s];
+        const int64_t q_len = query_start_loc[s + 1] - query_start_loc[s];
+        const int64_t L = seq_lens[s];
+        if (q_len > L) {
+#pragma omp atomic write
+            status = OR_ELEN;
+            continue;
+        }
+        const int32_t visible = (int32_t)(L - q_len + i + 1);
+        const int64_t one_row = h;   /* row h of a one-sequence batch */
+        const int rc = oracle_decode((const char *)q + (size_t)(tok * H * D) * qelt, q_dtype,
+                                     key_cache, value_cache, kv_dtype, k_scale, v_scale,
+                                     block_tables + s * max_nb, max_nb, &visible, 1, H, Hkv, D,
+                                     bs, NB, scale, &one_row, 1, out + r * D, NULL, 0);
+        if (rc) {
+#pragma omp atomic write
+            status = rc;
+        }
     }
     return status;
 }

@@ -34,10 +34,16 @@ MUTANTS = {
     "bf16_shift": ("(uint32_t)h << 16", "(uint32_t)h << 15"),
     "append_slot_split": ("blk = slot / bs, off = slot % bs", "blk = slot % NB, off = slot / NB"),
     "append_skips_scale": ("float yk = xk * k_inv;", "float yk = xk;"),
+    "multi_excludes_self": ("(int32_t)(L - q_len + i + 1)", "(int32_t)(L - q_len + i)"),
+    "multi_not_causal": ("(int32_t)(L - q_len + i + 1)", "(int32_t)(L)"),
+    "multi_token_not_relative": ("const int64_t i = tok - query_start_loc[s];",
+                                 "const int64_t i = tok - query_start_loc[0];"),
+    "multi_wrong_sequence": ("while (query_start_loc[s + 1] <= tok)",
+                             "while (query_start_loc[s + 1] < tok)"),
 }
 
 PIN_FILES = ["tests/test_oracle_decode.py", "tests/test_oracle_append.py",
-             "tests/test_oracle_codecs.py"]
+             "tests/test_oracle_codecs.py", "tests/test_oracle_decode_multi.py"]
 
 
 @pytest.mark.slow
