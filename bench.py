@@ -26,9 +26,14 @@ METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + decode seqs/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "valu": ["paged_kv_cache_54_amd/csrc/decode_valu.hip", "paged_kv_cache_54_amd/csrc/pa_device.h"],
-    "mfma": ["paged_kv_cache_54_amd/csrc/decode_mfma.hip", "paged_kv_cache_54_amd/csrc/pa_device.h"],
+    "mfma": ["paged_kv_cache_54_amd/csrc/decode_mfma.hip", "paged_kv_cache_54_amd/csrc/mfma_common.h",
+             "paged_kv_cache_54_amd/csrc/pa_device.h"],
+    "mfma_multi": ["paged_kv_cache_54_amd/csrc/decode_mfma_multi.hip",
+                   "paged_kv_cache_54_amd/csrc/mfma_common.h",
+                   "paged_kv_cache_54_amd/csrc/pa_device.h"],
 }
-KERNEL_NAMES = {"valu": "decode_valu_kernel", "mfma": "decode_mfma_kernel"}
+KERNEL_NAMES = {"valu": "decode_valu_kernel", "mfma": "decode_mfma_kernel",
+                "mfma_multi": "decode_mfma_multi_kernel"}
 
 
 def parse():
@@ -74,11 +79,14 @@ def algorithmic_bytes(b):
             blk = int(tables[s, j])
             seen[blk] = max(seen.get(blk, 0), n)
     unique_tokens = sum(seen.values())
-    qo = 2 * b.num_seqs * b.num_heads * D * b.q_elem_bytes
+    T = b.q.shape[0]                                        # query tokens (S, or more)
+    qo = 2 * T * b.num_heads * D * b.q_elem_bytes
     meta = 4 * int(sum(cdiv(int(x), bs) for x in lens)) + 4 * b.num_seqs
+    if b.query_start_loc is not None:
+        meta += 4 * (b.num_seqs + 1)
     decode = unique_tokens * kv_tok + qo + meta
     in_elt = 4 if b.cache_dtype == "f32" else 2
-    append = b.num_seqs * Hkv * D * 2 * (in_elt + b.kv_elem_bytes) + 8 * b.num_seqs
+    append = T * Hkv * D * 2 * (in_elt + b.kv_elem_bytes) + 8 * T
     return dict(decode=decode, append=append, step=decode + append,
                 logical_decode=logical_tokens * kv_tok + qo + meta,
                 unique_tokens=unique_tokens, logical_tokens=logical_tokens)
@@ -155,16 +163,25 @@ def cpu_baseline(b, budget_s):
     lens = b.seq_lens.cpu().numpy()
     G = b.group_size
     groups = np.random.default_rng(0).permutation(b.num_seqs * Hkv)
+    qsl = None if b.query_start_loc is None else b.query_start_loc.cpu().numpy()
     done, nbytes, t_total = 0, 0, 0.0
     per_tok = D * b.kv_elem_bytes * 2
     while t_total < budget_s:
         g = int(groups[done % len(groups)])
         s, kvh = divmod(g, Hkv)
-        rows = [s * b.num_heads + kvh * G + i for i in range(G)]
+        if qsl is None:
+            rows = [s * b.num_heads + kvh * G + i for i in range(G)]
+        else:
+            rows = [tok * b.num_heads + kvh * G + i for tok in range(qsl[s], qsl[s + 1])
+                    for i in range(G)]
         t0 = time.perf_counter()
-        oracle.decode(q, kc, vc, tables, lens, b.scale, b.k_scale, b.v_scale, rows=rows)
+        if qsl is None:
+            oracle.decode(q, kc, vc, tables, lens, b.scale, b.k_scale, b.v_scale, rows=rows)
+        else:
+            oracle.decode_multi(q, b.query_start_loc.cpu(), kc, vc, tables, lens, b.scale,
+                                b.k_scale, b.v_scale, rows=rows)
         t_total += time.perf_counter() - t0
-        nbytes += int(lens[s]) * per_tok + 2 * G * D * b.q_elem_bytes
+        nbytes += int(lens[s]) * per_tok + 2 * len(rows) * D * b.q_elem_bytes
         done += 1
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": cores,
@@ -316,7 +333,12 @@ def main():
     else:
         kc, vc = b.key_pool.clone(), b.value_pool.clone()
     out = torch.empty_like(b.q)
-    ws_bytes = pa.decode_workspace_size(b.q, kc, b.block_tables, P, variant)
+    multi = b.query_start_loc is not None
+    if multi:
+        ws_bytes = pa.decode_multi_workspace_size(b.q, b.max_query_len, kc, b.block_tables, P,
+                                                  variant)
+    else:
+        ws_bytes = pa.decode_workspace_size(b.q, kc, b.block_tables, P, variant)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     # descriptors built once; each step is two C calls
@@ -324,6 +346,7 @@ def main():
     d_k, d_v, d_slot = describe(b.k_new), describe(b.v_new), describe(b.slot_mapping)
     d_q, d_kc, d_vc = describe(b.q), describe(kc), describe(vc)
     d_bt, d_len, d_out = describe(b.block_tables), describe(b.seq_lens), describe(out)
+    d_qsl = describe(b.query_start_loc) if multi else None
     o = PaOpts()
     lib.pa_opts_init(ctypes.byref(o))
     o.k_scale, o.v_scale = b.k_scale, b.v_scale
@@ -342,8 +365,13 @@ def main():
         else:
             o.kernel_events[0], o.kernel_events[1] = ev.ev[2 * k], ev.ev[2 * k + 1]
         rc = lib.pa_kv_append(by(d_k), by(d_v), by(d_slot), by(d_kc), by(d_vc), by(o), stream)
-        rc = rc or lib.pa_decode(by(d_q), by(d_kc), by(d_vc), by(d_bt), by(d_len),
-                                 ctypes.c_float(b.scale), by(d_out), by(o), stream)
+        if multi:
+            rc = rc or lib.pa_decode_multi(by(d_q), by(d_qsl), b.max_query_len, by(d_kc),
+                                           by(d_vc), by(d_bt), by(d_len), ctypes.c_float(b.scale),
+                                           by(d_out), by(o), stream)
+        else:
+            rc = rc or lib.pa_decode(by(d_q), by(d_kc), by(d_vc), by(d_bt), by(d_len),
+                                     ctypes.c_float(b.scale), by(d_out), by(o), stream)
         if rc:
             raise pa.PaError("step", rc)
 
@@ -361,7 +389,7 @@ def main():
     nbytes = algorithmic_bytes(b)
     ms_per_step = wall / args.steps * 1e3
     value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
-    used = "mfma" if (variant == pa.VARIANT_MFMA or (
+    used = "mfma_multi" if multi else "mfma" if (variant == pa.VARIANT_MFMA or (
         variant == pa.VARIANT_AUTO and _mfma_ok(pa, b, kc))) else "valu"
     achieved = nbytes["decode"] / (kernel_ms * 1e-3) / 1e9
     traffic = traffic_for(used, args.workload)
@@ -383,7 +411,9 @@ def main():
                    "block_size": b.block_size, "num_blocks": b.num_blocks,
                    "mean_seq_len": round(nbytes["logical_tokens"] / b.num_seqs, 1),
                    "q_dtype": b.q_dtype, "cache_dtype": b.cache_dtype,
-                   "partition_tokens": P or "auto", "variant": used},
+                   "partition_tokens": P or "auto", "variant": used,
+                   **({"query_tokens": b.q.shape[0], "max_query_len": b.max_query_len}
+                      if multi else {})},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "decode_seqs_per_s": round(b.num_seqs / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": nbytes["step"],

@@ -83,6 +83,9 @@ typedef enum pa_status {
 #define PA_DEVERR_SEQ_LEN 0x2u   /* seq_len > table capacity: clamped */
 #define PA_DEVERR_SLOT 0x4u      /* slot >= num_blocks * block_size: token not written */
 #define PA_DEVERR_REGION 0x8u    /* block-op region base NULL or not 16-byte aligned: skipped */
+#define PA_DEVERR_QUERY 0x10u    /* query_start_loc outside [0, T] or decreasing, or a sequence
+                                    with more query tokens than max_query_len or seq_len: its
+                                    query count clamped, rows beyond left unwritten */
 
 typedef struct pa_tensor {
     void *data;         /* device pointer (16-byte aligned) */
@@ -179,6 +182,37 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
 int pa_decode_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
                              const pa_tensor *block_tables, const pa_opts *opts,
                              size_t *bytes);
+
+/*
+ * pa_decode_multi -- paged attention for several new query tokens per
+ * sequence: the verify step of speculative decoding, where the target model
+ * checks the K tokens a draft model proposed in one pass (P-EAGLE page:
+ * parallel drafting of K tokens, verified together).  Sequence s owns query
+ * tokens query_start_loc[s] .. query_start_loc[s+1]-1 of q; they are its last
+ * q_len positions (their K/V rows already appended, so seq_lens counts them),
+ * and query token i attends to positions 0 .. L - q_len + i: causal within
+ * the new tokens, everything before them.  With q_len = 1 everywhere this is
+ * pa_decode.
+ *
+ *   q, out           [T, H, D] BF16          T = total query tokens
+ *   query_start_loc  [S + 1] PA_I32          0 = qsl[0] <= qsl[1] <= ... <= qsl[S] = T
+ *   max_query_len    >= every q_len, 1 .. 16, with G * max_query_len <= 64
+ *   key_cache, value_cache, block_tables, seq_lens, scale, opts: as pa_decode
+ *                    (S = block_tables rows); caches BF16 or FP8_E4M3
+ * Matrix-core kernel only: opts->variant PA_VARIANT_VALU is refused with
+ * PA_ERR_UNSUPPORTED, as are f32 tensors.  Device contract: q_len <= seq_len;
+ * a violation raises PA_DEVERR_QUERY (see there).  Workspace:
+ * pa_decode_multi_workspace_size bytes.
+ */
+int pa_decode_multi(const pa_tensor *q, const pa_tensor *query_start_loc, int32_t max_query_len,
+                    const pa_tensor *key_cache, const pa_tensor *value_cache,
+                    const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,
+                    pa_tensor *out, const pa_opts *opts, void *hip_stream);
+
+/* Workspace bytes of pa_decode_multi (same rules as pa_decode_workspace_size). */
+int pa_decode_multi_workspace_size(const pa_tensor *q, int32_t max_query_len,
+                                   const pa_tensor *key_cache, const pa_tensor *block_tables,
+                                   const pa_opts *opts, size_t *bytes);
 
 /*
  * Block maintenance.  A "region" is one cache of the pool layout, for example

@@ -271,13 +271,19 @@ def fill_cache(batch, rows_k, rows_v, slots=None):
 def reference_step(batch):
     """Oracle result of one decode step of ``batch``: the pool (quantised by the
     oracle's own append for an e4m3 cache), the new rows appended at their
-    slots, then decode.  Returns (out fp64 [S, H, D], key_cache, value_cache)."""
+    slots, then decode (of several query tokens per sequence for a batch that
+    has them).  Returns (out fp64 [S or T, H, D], key_cache, value_cache)."""
     NB, bs, Hkv, D = batch.num_blocks, batch.block_size, batch.num_kv_heads, batch.head_dim
     kp = batch.key_pool.cpu().reshape(NB * bs, Hkv, D)
     vp = batch.value_pool.cpu().reshape(NB * bs, Hkv, D)
     kc, vc = fill_cache(batch, kp, vp)
     kv_append(batch.k_new.cpu(), batch.v_new.cpu(), batch.slot_mapping.cpu(), kc, vc,
               batch.k_scale, batch.v_scale)
-    out = decode(batch.q.cpu(), kc, vc, batch.block_tables.cpu(), batch.seq_lens.cpu(),
-                 batch.scale, batch.k_scale, batch.v_scale)
+    if getattr(batch, "query_start_loc", None) is not None:
+        out = decode_multi(batch.q.cpu(), batch.query_start_loc.cpu(), kc, vc,
+                           batch.block_tables.cpu(), batch.seq_lens.cpu(), batch.scale,
+                           batch.k_scale, batch.v_scale)
+    else:
+        out = decode(batch.q.cpu(), kc, vc, batch.block_tables.cpu(), batch.seq_lens.cpu(),
+                     batch.scale, batch.k_scale, batch.v_scale)
     return out, kc, vc

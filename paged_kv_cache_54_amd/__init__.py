@@ -10,6 +10,8 @@ fallback implementation.
     kv_append(k, v, slot_mapping, key_cache, value_cache, k_scale=1, v_scale=1)
     decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, ...)
     decode_workspace_size(q, key_cache, block_tables, ...)
+    decode_multi(q, query_start_loc, max_query_len, key_cache, value_cache, ...)
+    decode_multi_workspace_size(q, max_query_len, key_cache, block_tables, ...)
     zero_blocks(block_ids, regions)
     copy_blocks(block_pairs, src_regions, dst_regions)
     region_table(caches, device)
@@ -22,17 +24,18 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["kv_append", "decode", "decode_workspace_size", "zero_blocks", "copy_blocks",
+__all__ = ["kv_append", "decode", "decode_workspace_size", "decode_multi",
+           "decode_multi_workspace_size", "zero_blocks", "copy_blocks",
            "region_table", "Regions", "PaError", "status_string", "version", "library_path",
            "VARIANT_AUTO", "VARIANT_VALU", "VARIANT_MFMA", "DEVERR_BLOCK_ID", "DEVERR_SEQ_LEN",
-           "DEVERR_SLOT", "DEVERR_REGION"]
+           "DEVERR_SLOT", "DEVERR_REGION", "DEVERR_QUERY"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3, PA_I32, PA_I64 = 0, 1, 2, 3, 4
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
-DEVERR_BLOCK_ID, DEVERR_SEQ_LEN, DEVERR_SLOT, DEVERR_REGION = 0x1, 0x2, 0x4, 0x8
+DEVERR_BLOCK_ID, DEVERR_SEQ_LEN, DEVERR_SLOT, DEVERR_REGION, DEVERR_QUERY = 0x1, 0x2, 0x4, 0x8, 0x10
 
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
            torch.float8_e4m3fn: PA_FP8_E4M3, torch.int32: PA_I32, torch.int64: PA_I64}
@@ -78,6 +81,14 @@ def _load():
         lib.pa_decode.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor), P(PaTensor),
                                   P(PaTensor), ctypes.c_float, P(PaTensor), P(PaOpts),
                                   ctypes.c_void_p]
+        lib.pa_decode_multi.restype = ctypes.c_int
+        lib.pa_decode_multi.argtypes = [P(PaTensor), P(PaTensor), ctypes.c_int32, P(PaTensor),
+                                        P(PaTensor), P(PaTensor), P(PaTensor), ctypes.c_float,
+                                        P(PaTensor), P(PaOpts), ctypes.c_void_p]
+        lib.pa_decode_multi_workspace_size.restype = ctypes.c_int
+        lib.pa_decode_multi_workspace_size.argtypes = [P(PaTensor), ctypes.c_int32, P(PaTensor),
+                                                       P(PaTensor), P(PaOpts),
+                                                       P(ctypes.c_size_t)]
         lib.pa_decode_workspace_size.restype = ctypes.c_int
         lib.pa_decode_workspace_size.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor),
                                                  P(PaOpts), P(ctypes.c_size_t)]
@@ -197,6 +208,42 @@ def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, k
     _check("pa_decode", lib.pa_decode(*[ctypes.byref(x) for x in args], float(scale),
                                       ctypes.byref(describe(out)), ctypes.byref(o),
                                       _stream(stream)))
+    return out
+
+
+def decode_multi_workspace_size(q, max_query_len, key_cache, block_tables, partition_tokens=0,
+                                variant=VARIANT_AUTO) -> int:
+    lib = _load()
+    o = _opts(partition_tokens=partition_tokens, variant=variant)
+    n = ctypes.c_size_t(0)
+    _check("pa_decode_multi_workspace_size",
+           lib.pa_decode_multi_workspace_size(ctypes.byref(describe(q)), int(max_query_len),
+                                              ctypes.byref(describe(key_cache)),
+                                              ctypes.byref(describe(block_tables)),
+                                              ctypes.byref(o), ctypes.byref(n)))
+    return n.value
+
+
+def decode_multi(q, query_start_loc, max_query_len, key_cache, value_cache, block_tables,
+                 seq_lens, scale, out=None, k_scale=1.0, v_scale=1.0, partition_tokens=0,
+                 variant=VARIANT_AUTO, workspace=None, err_flag=None, events=None, stream=None):
+    """Paged attention of several new query tokens per sequence (causal within
+    them); q, out [T, H, D] bf16, query_start_loc int32 [S+1]."""
+    lib = _load()
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        need = decode_multi_workspace_size(q, max_query_len, key_cache, block_tables,
+                                           partition_tokens, variant)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events)
+    d_q, d_qsl = describe(q), describe(query_start_loc)
+    args = [describe(x) for x in (key_cache, value_cache, block_tables, seq_lens)]
+    _check("pa_decode_multi",
+           lib.pa_decode_multi(ctypes.byref(d_q), ctypes.byref(d_qsl), int(max_query_len),
+                               *[ctypes.byref(x) for x in args], float(scale),
+                               ctypes.byref(describe(out)), ctypes.byref(o), _stream(stream)))
     return out
 
 

@@ -17,8 +17,8 @@ LIB = os.path.join(HERE, "libpa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "kv_append.hip", "decode_valu.hip", "decode_mfma.hip", "merge.hip",
-           "blocks.hip"]
+SOURCES = ["pa_api.cpp", "kv_append.hip", "decode_valu.hip", "decode_mfma.hip",
+           "decode_mfma_multi.hip", "merge.hip", "blocks.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
@@ -29,7 +29,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
 # Per-source extra flags.  The matrix-core decode kernel rescales its MFMA
 # accumulators with vector instructions, so it keeps them in VGPRs rather than
 # copying them between AGPRs and VGPRs on every rescale.
-EXTRA = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "decode_mfma_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

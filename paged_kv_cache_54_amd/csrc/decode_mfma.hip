@@ -31,77 +31,18 @@
 // and v_scale applied to the result.  Tokens at or beyond seq_len in the last
 // block are excluded by selection: their scores become -inf and their V rows
 // are stored to LDS as zeros, so stale NaN/Inf bits never enter an MFMA.
-#include <type_traits>
-
-#include "pa_device.h"
+#include "mfma_common.h"
 
 namespace pa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v)
-{
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ bf16x4 as_bf16x4(s16x4 v)
-{
-    return __builtin_bit_cast(bf16x4, v);
-}
-
-// Two e4m3 codes (byte pair HI of w) -> two packed bf16.  An e4m3 value has
-// at most 4 significant bits, so its binary32 form ends in 16 zero bits and
-// the upper halves are its exact bf16 encoding.
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w)
-{
-    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
-}
-
-__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 v)
-{
-    return make_uint4(e4m3x2_to_bf16x2<false>(v.x), e4m3x2_to_bf16x2<true>(v.x),
-                      e4m3x2_to_bf16x2<false>(v.y), e4m3x2_to_bf16x2<true>(v.y));
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Two floats -> packed bf16 pair with the hardware converter (v_cvt_pk_bf16_f32,
-// round to nearest even).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
-
 template <int KT, int D, int BS, int G>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
 {
-    constexpr int EB = (KT == KT_BF16) ? 2 : 1;
-    constexpr int NC = D / 32;                 // QK MFMAs per 16 tokens
-    constexpr int ND = D / 16;                 // PV MFMAs (16 output dims each) per 16 tokens
-    // A tile is 8 KB of one KV head (K and V): 16 bf16 or 32 e4m3 tokens,
-    // never more than a block; MT 16-token MFMA tiles, BS/TILE tiles a block.
-    constexpr int TILE = (32 / EB < BS) ? 32 / EB : BS;
-    constexpr int MT = TILE / 16;
-    constexpr int HALVES = BS / TILE;
-    constexpr int RCH = D * EB / 16;           // 16-byte chunks of one cache row
-    constexpr int LROWS = 64 / RCH;            // rows one load instruction covers
-    constexpr int NLOAD = TILE / LROWS;        // load instructions per tile and tensor
-    // K and V tiles in LDS as bf16 rows of D elements plus padding, chosen so
-    // that each read pattern touches distinct banks: K operand reads take 16
-    // bytes from 16 consecutive rows (rows 4 banks apart: 16-byte pad), the
-    // transposed V reads take 32 bytes from 4 consecutive rows per 16 lanes
-    // (rows 8 banks apart: 32-byte pad).  Every address is a per-lane base
-    // plus a constant.
-    constexpr int KROWB = 2 * D + 16;
-    constexpr int VROWB = 2 * D + 32;
+    using Geo = MfmaGeo<KT, D, BS>;
+    constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
+    constexpr int HALVES = Geo::HALVES;
+    constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
     static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group must divide 16");
 #ifdef PA_EXP_PINGPONG_ALL
     constexpr bool PINGPONG = true;
@@ -125,57 +66,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
     if (chunk.n == 0)
         return;
 
-    const int slot_bytes = Hkv * D * EB;
-    const int64_t block_bytes = (int64_t)BS * slot_bytes;
-    // both tensors are read row-contiguously: row i*LROWS + lane/RCH, 16-byte chunk lane%RCH
-    const int l_row = lane / RCH, l_chunk = lane % RCH;
-    const int l_voff = l_row * slot_bytes + l_chunk * 16;
-
-    struct Tile {
-        uint4 k[NLOAD];
-        uint4 v[NLOAD];
-    };
-    // tile `half` (tokens 16*half .. 16*half+15) of block `id`
-    auto load_tile = [&](int id, int kvh, int half, Tile &t) {
-        const __amdgpu_buffer_rsrc_t rk = block_rsrc(a.key_cache, block_bytes, id);
-        const __amdgpu_buffer_rsrc_t rv = block_rsrc(a.value_cache, block_bytes, id);
-        const int voff = l_voff + kvh * D * EB;
-        const int soff = half * TILE * slot_bytes;
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            t.k[i] = buf_load16(rk, voff, soff + i * LROWS * slot_bytes);
-            t.v[i] = buf_load16(rv, voff, soff + i * LROWS * slot_bytes);
-        }
-    };
-    // Store one tensor's rows into an LDS tile (row stride ROWB) as bf16; with
-    // MASK, rows whose token is at or beyond t1 are stored as zeros.
-    auto store_tile = [&](auto rowb_c, auto mask_c, uint8_t *tile, const uint4 (&src)[NLOAD],
-                          int tok_base, int t1) {
-        constexpr int ROWB = decltype(rowb_c)::value;
-        constexpr bool MASK = decltype(mask_c)::value;
-#pragma unroll
-        for (int i = 0; i < NLOAD; ++i) {
-            const int row = i * LROWS + l_row;
-            const bool ok = !MASK || (tok_base + row < t1);
-            if constexpr (KT == KT_BF16) {
-                uint4 v = src[i];
-                if (MASK && !ok)
-                    v = make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4 *>(tile + row * ROWB + l_chunk * 16) = v;
-            } else {
-                uint4 lo = e4m3x8_to_bf16x8(make_uint2(src[i].x, src[i].y));
-                uint4 hi = e4m3x8_to_bf16x8(make_uint2(src[i].z, src[i].w));
-                if (MASK && !ok)
-                    lo = hi = make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4 *>(tile + row * ROWB + l_chunk * 32) = lo;
-                *reinterpret_cast<uint4 *>(tile + row * ROWB + l_chunk * 32 + 16) = hi;
-            }
-        }
-    };
-    using KRowB = std::integral_constant<int, KROWB>;
-    using VRowB = std::integral_constant<int, VROWB>;
-    using Plain = std::false_type;
-    using Masked = std::true_type;
+    const MfmaLoader<Geo> loader(a, lane);
+    using Tile = MfmaTile<Geo>;
+    auto load_tile = [&](int id, int kvh, int half, Tile &t) { loader.load(id, kvh, half, t); };
 
     // per-segment state
     bf16x8 qop[NC];
@@ -228,17 +121,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
         }
     };
 
-    // Stage a 16-token tile of the current segment into LDS as bf16; V rows at
-    // or beyond t1 become zeros (K rows there only produce scores that are
-    // replaced by -inf below).
+    // Stage a tile of the current segment into LDS as bf16 (V rows past the
+    // sequence end as zeros).
     auto stage = [&](const Cursor &c, int half, const Tile &t) {
-        const int tok_base = c.j * BS + half * TILE;
-        const int t1 = c.L;
-        store_tile(KRowB{}, Plain{}, kt, t.k, tok_base, t1);
-        if (tok_base + TILE > t1)
-            store_tile(VRowB{}, Masked{}, vt, t.v, tok_base, t1);
-        else
-            store_tile(VRowB{}, Plain{}, vt, t.v, tok_base, t1);
+        stage_tile<Geo>(loader, kt, vt, t, c.j * BS + half * TILE, c.L);
     };
 
     // QK^T, online softmax and PV of the staged tile.

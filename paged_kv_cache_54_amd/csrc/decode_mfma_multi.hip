@@ -1,0 +1,304 @@
+// decode_mfma_multi.hip -- paged attention for several new query tokens per
+// sequence on the gfx950 matrix cores (bf16 query; bf16 or e4m3 cache): the
+// verify step of speculative decoding, where the target model checks K
+// drafted tokens in one pass (P-EAGLE page).
+//
+// Sequence s owns query tokens query_start_loc[s] .. query_start_loc[s+1]-1;
+// they are its last q_len positions (already appended to the cache), and
+// query token i attends to positions 0 .. L - q_len + i (causal within the
+// new tokens).  Everything else -- the work list of (sequence, KV head,
+// block) units cut into equal chunks, the gather through the block table,
+// bf16 LDS tiles, online softmax in log2 units, selection masking, partials
+// and the log-sum-exp merge -- is the single-token matrix-core kernel's.  The
+// difference is the MFMA column space: a KV head's query rows are the
+// (query token, head of the group) pairs, column c = i * G + g, and there are
+// NT tiles of 16 columns.  Each K operand read from LDS feeds the QK MFMAs of
+// all NT column tiles, each transposed V operand the PV MFMAs of all NT, so
+// the KV bytes of a block are read once for all q_len * G query rows.
+// Causality is one more bound per column: column c sees tokens below
+// lim_c = L - q_len + i + 1, applied by selection like the sequence end.
+#include "mfma_common.h"
+
+namespace pa {
+namespace {
+
+template <int KT, int D, int BS, int NT>
+__global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
+{
+    using Geo = MfmaGeo<KT, D, BS>;
+    constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
+    constexpr int HALVES = Geo::HALVES;
+    constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
+
+    __shared__ __attribute__((aligned(16))) uint8_t kt[TILE * KROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t vt[TILE * VROWB];
+
+    const int lane = threadIdx.x;
+    const int g4 = lane >> 4;                  // 16-lane group
+    const int c16 = lane & 15;                 // token row (K operand) / column (output)
+    const int H = a.num_heads, Hkv = a.num_kv_heads;
+    const int G = H / Hkv, lg = a.log2_group;  // G = 2^lg
+    const int RPS = a.rows_per_slot;           // partial rows per slot: G * max_query_len
+    const int cap = a.max_nb * BS;
+    const int w = blockIdx.x;
+
+    const Chunk chunk = my_chunk<BS>(a, w, a.num_waves);
+    if (chunk.n == 0)
+        return;
+
+    const MfmaLoader<Geo> loader(a, lane);
+    using Tile = MfmaTile<Geo>;
+    auto load_tile = [&](int id, int kvh, int half, Tile &t) { loader.load(id, kvh, half, t); };
+
+    // per-segment state, per column tile: Q^T operand, accumulators, running
+    // max and lane-partial sum, the causal bound and the output row
+    bf16x8 qop[NT][NC];
+    f32x4 acc[NT][ND];
+    float m[NT], l[NT];
+    int lim[NT];                               // tokens [0, lim) visible; 0 = unused column
+    int64_t orow[NT];                          // (token * H + head), -1 = unused column
+    bool seg_starts = false;
+
+    auto begin_segment = [&](const Cursor &c) {
+        int qs, ql;
+        query_span(a, c.s, c.L, &qs, &ql, c.kvh == 0 && lane == 0 ? a.err_flag : nullptr);
+        qs = __builtin_amdgcn_readfirstlane(qs);
+        ql = __builtin_amdgcn_readfirstlane(ql);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = 16 * nt + c16;
+            const int i = col >> lg, g = col & (G - 1);
+            const bool valid = i < ql;
+            lim[nt] = valid ? c.L - ql + i + 1 : 0;
+            orow[nt] = valid ? (int64_t)(qs + i) * H + c.kvh * G + g : -1;
+            const uint16_t *qrow =
+                static_cast<const uint16_t *>(a.q) + (valid ? orow[nt] : 0) * D + 8 * g4;
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+                qop[nt][k] = valid ? as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * k))
+                                   : as_bf16x8(make_uint4(0, 0, 0, 0));
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                acc[nt][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+            m[nt] = -INFINITY;
+            l[nt] = 0.f;
+        }
+        seg_starts = c.j == 0;
+    };
+
+    auto finish_segment = [&](const Cursor &c, bool ends) {
+        const int g = c.s * Hkv + c.kvh;
+        const int slot = w + g;
+        record_segment(a, g, slot, seg_starts, ends);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            float lt = l[nt] + __shfl_xor(l[nt], 16);    // sum the four 16-lane groups
+            lt += __shfl_xor(lt, 32);
+            if (orow[nt] < 0)
+                continue;
+            if (seg_starts && ends) {
+                const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
+                uint16_t *o = static_cast<uint16_t *>(a.out) + orow[nt] * D + 4 * g4;
+#pragma unroll
+                for (int d = 0; d < ND; ++d)
+                    *reinterpret_cast<uint2 *>(o + 16 * d) =
+                        make_uint2(pack_bf16x2(acc[nt][d][0] * inv, acc[nt][d][1] * inv),
+                                   pack_bf16x2(acc[nt][d][2] * inv, acc[nt][d][3] * inv));
+            } else {
+                const int64_t pi = (int64_t)slot * RPS + 16 * nt + c16;
+                float *o = a.ws_acc + pi * D + 4 * g4;
+#pragma unroll
+                for (int d = 0; d < ND; ++d)
+                    *reinterpret_cast<float4 *>(o + 16 * d) =
+                        make_float4(acc[nt][d][0] * a.v_scale, acc[nt][d][1] * a.v_scale,
+                                    acc[nt][d][2] * a.v_scale, acc[nt][d][3] * a.v_scale);
+                if (g4 == 0)
+                    *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m[nt], lt);
+            }
+        }
+    };
+
+    auto stage = [&](const Cursor &c, int half, const Tile &t) {
+        stage_tile<Geo>(loader, kt, vt, t, c.j * BS + half * TILE, c.L);
+    };
+
+    // QK^T for every column tile, online softmax per column, PV.
+    auto process = [&](const Cursor &c, int half) {
+        const int tok_base = c.j * BS + half * TILE;
+        f32x4 sc[MT][NT];
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                sc[h][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint8_t *krow = kt + (16 * h + c16) * KROWB + 16 * g4;
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+                const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + 64 * k));
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    sc[h][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[nt][k],
+                                                                      sc[h][nt], 0, 0, 0);
+            }
+        }
+
+        bf16x4 pop[MT][NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            // scale, mask (sequence end and causality) by selection, column max
+            float bm = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < MT; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ok = tok_base + 16 * h + 4 * g4 + i < lim[nt];
+                    const float v = ok ? sc[h][nt][i] * a.qk_scale_log2 : -INFINITY;
+                    sc[h][nt][i] = v;
+                    bm = fmaxf(bm, v);
+                }
+            bm = fmaxf(bm, __shfl_xor(bm, 16));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            const float mn = fmaxf(m[nt], bm);
+            if (__ballot(mn > m[nt])) {
+                const float alpha = (mn > m[nt]) ? __builtin_amdgcn_exp2f(m[nt] - mn) : 1.f;
+                l[nt] *= alpha;
+#pragma unroll
+                for (int d = 0; d < ND; ++d)
+                    acc[nt][d] *= alpha;
+            }
+            m[nt] = mn;
+#pragma unroll
+            for (int h = 0; h < MT; ++h) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = (sc[h][nt][i] == -INFINITY) ? 0.f
+                                                       : __builtin_amdgcn_exp2f(sc[h][nt][i] - mn);
+                    l[nt] += p[i];
+                }
+                pop[h][nt] = __builtin_bit_cast(
+                    bf16x4, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+            }
+        }
+
+        // O^T += V^T P^T per column tile, each V^T operand read once from LDS
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const int row = 16 * h + 4 * g4 + (c16 >> 2);
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+                const int addr = row * VROWB + 32 * d + 8 * (c16 & 3);
+                const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)((__attribute__((address_space(3))) uint8_t *)vt + addr));
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    acc[nt][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        as_bf16x4(raw), pop[h][nt], acc[nt][d], 0, 0, 0);
+            }
+        }
+    };
+
+    // Walk the chunk tile by tile with one register tile in flight: tile k is
+    // staged into LDS, then the loads of tile k+1 are issued into the same
+    // registers and stay in flight while tile k is computed from LDS.
+    BlockIds ids(a.block_tables, a.max_nb, a.num_blocks, a.err_flag);
+    Cursor cc = chunk.start;
+    Cursor lc = cc;
+    const int n = chunk.n;
+    const int steps = n * HALVES;
+
+    int l_half = 0;
+    int l_id = ids.get(lc.s, lc.j);
+    auto next_load = [&](int k) {
+        if (k >= steps) {
+            l_id = -1;
+            return;
+        }
+        if (++l_half == HALVES) {
+            l_half = 0;
+            advance<BS>(lc, a.seq_lens, Hkv, cap);
+            l_id = ids.get(lc.s, lc.j);
+        }
+    };
+
+    Tile t;
+    int id = l_id, half = l_half;
+    load_tile(id, lc.kvh, half, t);
+    for (int k = 0; k < steps; ++k) {
+        const int unit = k / HALVES;
+        if (half == 0 && (unit == 0 || cc.j == 0))
+            begin_segment(cc);
+        if (id >= 0)
+            stage(cc, half, t);
+        next_load(k + 1);
+        const int id_next = l_id, half_next = l_half;
+        load_tile(id_next, lc.kvh, half_next, t);
+        if (id >= 0)
+            process(cc, half);
+        if (half == HALVES - 1) {
+            const bool ends = cc.j == cc.nb - 1;
+            if (ends || unit == n - 1)
+                finish_segment(cc, ends);
+            if (unit + 1 < n)
+                advance<BS>(cc, a.seq_lens, Hkv, cap);
+        }
+        id = id_next;
+        half = half_next;
+    }
+}
+
+typedef void (*DecodeKernel)(DecodeArgs);
+
+template <int KT, int D, int BS>
+DecodeKernel pick_nt(int nt)
+{
+    switch (nt) {
+    case 1: return decode_mfma_multi_kernel<KT, D, BS, 1>;
+    case 2: return decode_mfma_multi_kernel<KT, D, BS, 2>;
+    case 4: return decode_mfma_multi_kernel<KT, D, BS, 4>;
+    default: return nullptr;
+    }
+}
+
+template <int KT>
+DecodeKernel pick_shape(int d, int bs, int nt)
+{
+    if (d == 64 && bs == 16) return pick_nt<KT, 64, 16>(nt);
+    if (d == 64 && bs == 32) return pick_nt<KT, 64, 32>(nt);
+    if (d == 128 && bs == 16) return pick_nt<KT, 128, 16>(nt);
+    if (d == 128 && bs == 32) return pick_nt<KT, 128, 32>(nt);
+    return nullptr;
+}
+
+DecodeKernel pick(int kv_type, int d, int bs, int nt)
+{
+    if (kv_type == KT_BF16)
+        return pick_shape<KT_BF16>(d, bs, nt);
+    if (kv_type == KT_E4M3)
+        return pick_shape<KT_E4M3>(d, bs, nt);
+    return nullptr;
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma_multi(const DecodeArgs &a, int kv_type, int head_dim,
+                                    int block_size, int col_tiles, hipStream_t stream)
+{
+    const DecodeKernel k = pick(kv_type, head_dim, block_size, col_tiles);
+    if (!k)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k, dim3(a.num_waves), dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t decode_mfma_multi_occupancy(int kv_type, int head_dim, int block_size, int col_tiles,
+                                       int *waves_per_cu)
+{
+    const DecodeKernel k = pick(kv_type, head_dim, block_size, col_tiles);
+    if (!k)
+        return hipErrorInvalidValue;
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(waves_per_cu,
+                                                        reinterpret_cast<const void *>(k), 64, 0);
+}
+
+}  // namespace pa

@@ -1,6 +1,7 @@
 // merge.hip -- second pass of paged decode: combine, by log-sum-exp, the
-// partial results of every (sequence, query head) whose KV segment was split
-// between several chunks, and write the zero rows of empty sequences.
+// partial results of every query row (sequence or query token, head) whose KV
+// segment was split between several chunks, and write the zero rows of empty
+// sequences.
 //
 // A chunk's partial for one head holds acc_p = sum_t 2^(z_t - m_p) v_t,
 // l_p = sum_t 2^(z_t - m_p) and m_p (scores z in log2 units).  With
@@ -44,10 +45,34 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int sub = t / LPP, col = (t % LPP) * 4;
-    const int64_t row = blockIdx.x;              // s * H + h
     const int H = a.num_heads, G = a.num_heads / a.num_kv_heads;
-    const int s = (int)(row / H), h = (int)(row % H);
-    const int L = min(a.seq_lens[s], a.max_nb * block_size);
+    const int RPS = a.rows_per_slot;
+    // Output row and the row of its partials within a slot: one query token
+    // per sequence -- workgroup s * H + h, partial row h % G; several --
+    // workgroup (s * max_query_len + i) * H + h for query token i, partial
+    // row i * G + h % G (absent when the sequence has at most i tokens).
+    int s, h, prow;
+    int64_t row;
+    int L;
+    if (a.query_start_loc) {
+        const int64_t r = blockIdx.x;
+        h = (int)(r % H);
+        const int i = (int)((r / H) % a.max_query_len);
+        s = (int)(r / ((int64_t)H * a.max_query_len));
+        L = min(a.seq_lens[s], a.max_nb * block_size);
+        int qs, ql;
+        query_span(a, s, max(L, 0), &qs, &ql, nullptr);
+        if (i >= ql)
+            return;
+        row = (int64_t)(qs + i) * H + h;
+        prow = i * G + h % G;
+    } else {
+        row = blockIdx.x;
+        s = (int)(row / H);
+        h = (int)(row % H);
+        L = min(a.seq_lens[s], a.max_nb * block_size);
+        prow = h % G;
+    }
 
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     float inv = 0.f;
@@ -57,14 +82,13 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
         if (first == last)
             return;                              // one chunk wrote the output
         const int n = last - first + 1;
-        const int hig = h % G;
-        // partial p of this row lives at slot first + p, head hig
-        const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (int64_t)first * G + hig;
-        const float *acc = a.ws_acc + ((int64_t)first * G + hig) * D + col;
+        // partial p of this row lives at slot first + p, row prow
+        const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (int64_t)first * RPS + prow;
+        const float *acc = a.ws_acc + ((int64_t)first * RPS + prow) * D + col;
 
         float M = -INFINITY;
         for (int i = t; i < n; i += NT)
-            M = fmaxf(M, ml[(int64_t)i * G].x);
+            M = fmaxf(M, ml[(int64_t)i * RPS].x);
         M = wave_max(M);
         if (lane == 0)
             red[wave] = M;
@@ -78,7 +102,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
         for (int c = 0; c < n; c += NT) {
             float wgt = 0.f;
             if (c + t < n) {
-                const float2 v = ml[(int64_t)(c + t) * G];
+                const float2 v = ml[(int64_t)(c + t) * RPS];
                 wgt = (v.x == -INFINITY) ? 0.f : exp2f(v.x - M);
                 den += wgt * v.y;
             }
@@ -88,7 +112,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
 #pragma unroll 4
             for (int i = sub; i < cnt; i += NSUB) {
                 const float wi = wts[i];
-                const float4 x = *reinterpret_cast<const float4 *>(acc + (int64_t)(c + i) * G * D);
+                const float4 x = *reinterpret_cast<const float4 *>(acc + (int64_t)(c + i) * RPS * D);
                 o.x = fmaf(wi, x.x, o.x);
                 o.y = fmaf(wi, x.y, o.y);
                 o.z = fmaf(wi, x.z, o.z);
@@ -133,7 +157,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
 hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int block_size,
                         hipStream_t stream)
 {
-    dim3 grid((unsigned)((int64_t)a.num_seqs * a.num_heads)), block(kMergeThreads);
+    const int64_t rows = (int64_t)a.num_seqs * a.num_heads *
+                         (a.query_start_loc ? a.max_query_len : 1);
+    if (rows > INT32_MAX)
+        return hipErrorInvalidValue;
+    dim3 grid((unsigned)rows), block(kMergeThreads);
     if (out_type == KT_F32 && head_dim == 64)
         hipLaunchKernelGGL((merge_kernel<KT_F32, 64>), grid, block, 0, stream, a, block_size);
     else if (out_type == KT_F32 && head_dim == 128)

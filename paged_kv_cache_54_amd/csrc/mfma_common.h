@@ -1,0 +1,160 @@
+// mfma_common.h -- pieces shared by the gfx950 matrix-core decode kernels
+// (one query token per sequence, and several): operand types, e4m3 -> bf16
+// conversion, the tile geometry, the buffer loads of a KV tile and its staging
+// into LDS as bf16 rows.
+#pragma once
+
+#include <type_traits>
+
+#include "pa_device.h"
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v)
+{
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x4 as_bf16x4(s16x4 v)
+{
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+// Two e4m3 codes (byte pair HI of w) -> two packed bf16.  An e4m3 value has
+// at most 4 significant bits, so its binary32 form ends in 16 zero bits and
+// the upper halves are its exact bf16 encoding.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w)
+{
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+}
+
+__device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 v)
+{
+    return make_uint4(e4m3x2_to_bf16x2<false>(v.x), e4m3x2_to_bf16x2<true>(v.x),
+                      e4m3x2_to_bf16x2<false>(v.y), e4m3x2_to_bf16x2<true>(v.y));
+}
+
+// Two floats -> packed bf16 pair with the hardware converter (v_cvt_pk_bf16_f32,
+// round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// Tile geometry of one KV head's rows for a cache of element type KT.
+template <int KT_, int D_, int BS_>
+struct MfmaGeo {
+    static constexpr int KT = KT_, D = D_, BS = BS_;
+    static constexpr int EB = (KT == KT_BF16) ? 2 : 1;
+    static constexpr int NC = D / 32;          // QK MFMAs per 16 tokens
+    static constexpr int ND = D / 16;          // PV MFMAs (16 output dims each) per 16 tokens
+    // A tile is 8 KB of one KV head (K and V): 16 bf16 or 32 e4m3 tokens,
+    // never more than a block; MT 16-token MFMA tiles, BS/TILE tiles a block.
+    static constexpr int TILE = (32 / EB < BS) ? 32 / EB : BS;
+    static constexpr int MT = TILE / 16;
+    static constexpr int HALVES = BS / TILE;
+    static constexpr int RCH = D * EB / 16;    // 16-byte chunks of one cache row
+    static constexpr int LROWS = 64 / RCH;     // rows one load instruction covers
+    static constexpr int NLOAD = TILE / LROWS; // load instructions per tile and tensor
+    // K and V tiles in LDS as bf16 rows of D elements plus padding, chosen so
+    // that each read pattern touches distinct banks: K operand reads take 16
+    // bytes from 16 consecutive rows (rows 4 banks apart: 16-byte pad), the
+    // transposed V reads take 32 bytes from 4 consecutive rows per 16 lanes
+    // (rows 8 banks apart: 32-byte pad).  Every address is a per-lane base
+    // plus a constant.
+    static constexpr int KROWB = 2 * D + 16;
+    static constexpr int VROWB = 2 * D + 32;
+};
+
+template <class Geo>
+struct MfmaTile {
+    uint4 k[Geo::NLOAD];
+    uint4 v[Geo::NLOAD];
+};
+
+// Row-contiguous loads of a tile: load instruction i reads row
+// i * LROWS + lane / RCH, 16-byte chunk lane % RCH, of both tensors, through a
+// buffer resource over the block (a missing block, id < 0, reads nothing).
+template <class Geo>
+struct MfmaLoader {
+    const void *key_cache, *value_cache;
+    int slot_bytes;
+    int64_t block_bytes;
+    int l_row, l_chunk, l_voff;
+
+    __device__ __forceinline__ MfmaLoader(const DecodeArgs &a, int lane)
+        : key_cache(a.key_cache), value_cache(a.value_cache),
+          slot_bytes(a.num_kv_heads * Geo::D * Geo::EB),
+          block_bytes((int64_t)Geo::BS * a.num_kv_heads * Geo::D * Geo::EB),
+          l_row(lane / Geo::RCH), l_chunk(lane % Geo::RCH),
+          l_voff((lane / Geo::RCH) * a.num_kv_heads * Geo::D * Geo::EB + (lane % Geo::RCH) * 16)
+    {
+    }
+
+    // tile `half` (tokens TILE*half ..) of block `id`, KV head kvh
+    __device__ __forceinline__ void load(int id, int kvh, int half, MfmaTile<Geo> &t) const
+    {
+        const __amdgpu_buffer_rsrc_t rk = block_rsrc(key_cache, block_bytes, id);
+        const __amdgpu_buffer_rsrc_t rv = block_rsrc(value_cache, block_bytes, id);
+        const int voff = l_voff + kvh * Geo::D * Geo::EB;
+        const int soff = half * Geo::TILE * slot_bytes;
+#pragma unroll
+        for (int i = 0; i < Geo::NLOAD; ++i) {
+            t.k[i] = buf_load16(rk, voff, soff + i * Geo::LROWS * slot_bytes);
+            t.v[i] = buf_load16(rv, voff, soff + i * Geo::LROWS * slot_bytes);
+        }
+    }
+};
+
+// Store one tensor's rows into an LDS tile (row stride ROWB) as bf16; with
+// MASK, rows whose token is at or beyond t1 are stored as zeros.
+template <class Geo, int ROWB, bool MASK>
+__device__ __forceinline__ void store_rows(const MfmaLoader<Geo> &ld, uint8_t *tile,
+                                           const uint4 (&src)[Geo::NLOAD], int tok_base, int t1)
+{
+#pragma unroll
+    for (int i = 0; i < Geo::NLOAD; ++i) {
+        const int row = i * Geo::LROWS + ld.l_row;
+        const bool ok = !MASK || (tok_base + row < t1);
+        if constexpr (Geo::KT == KT_BF16) {
+            uint4 v = src[i];
+            if (MASK && !ok)
+                v = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(tile + row * ROWB + ld.l_chunk * 16) = v;
+        } else {
+            uint4 lo = e4m3x8_to_bf16x8(make_uint2(src[i].x, src[i].y));
+            uint4 hi = e4m3x8_to_bf16x8(make_uint2(src[i].z, src[i].w));
+            if (MASK && !ok)
+                lo = hi = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4 *>(tile + row * ROWB + ld.l_chunk * 32) = lo;
+            *reinterpret_cast<uint4 *>(tile + row * ROWB + ld.l_chunk * 32 + 16) = hi;
+        }
+    }
+}
+
+// Stage a tile whose first token is tok_base into the K and V LDS tiles; V
+// rows at or beyond t1 (the sequence length) become zeros, so stale NaN/Inf
+// bits past the end never enter an MFMA (K rows there only produce scores
+// that the kernels replace by -inf).
+template <class Geo>
+__device__ __forceinline__ void stage_tile(const MfmaLoader<Geo> &ld, uint8_t *kt, uint8_t *vt,
+                                           const MfmaTile<Geo> &t, int tok_base, int t1)
+{
+    store_rows<Geo, Geo::KROWB, false>(ld, kt, t.k, tok_base, t1);
+    if (tok_base + Geo::TILE > t1)
+        store_rows<Geo, Geo::VROWB, true>(ld, vt, t.v, tok_base, t1);
+    else
+        store_rows<Geo, Geo::VROWB, false>(ld, vt, t.v, tok_base, t1);
+}
+
+}  // namespace pa

@@ -91,6 +91,10 @@ int device_cu_count(int *cus)
 
 struct DecodePlan {
     int64_t S, H, Hkv, D, bs, NB, max_nb, G;
+    int64_t T;               // query rows of q: S, or the total query tokens
+    int64_t QM;              // 0: one query token per sequence; else max_query_len
+    int64_t col_tiles;       // multi-token: 16-column tiles of (token, head) pairs
+    int64_t rows;            // partial rows per slot: G, or G * QM
     int q_type, kv_type;
     int variant;             // PA_VARIANT_VALU or PA_VARIANT_MFMA
     int64_t chunk_units;     // units per chunk, 0 = balanced over the waves
@@ -99,10 +103,10 @@ struct DecodePlan {
     size_t ws_bytes;
 };
 
-// Workspace layout: acc [slots, G, D] f32 | ml [slots, G, 2] f32 | seg [S*Hkv, 2] i32
+// Workspace layout: acc [slots, rows, D] f32 | ml [slots, rows, 2] f32 | seg [S*Hkv, 2] i32
 size_t workspace_bytes(const DecodePlan &p)
 {
-    return sizeof(float) * (size_t)(p.slots * p.G) * (size_t)(p.D + 2) +
+    return sizeof(float) * (size_t)(p.slots * p.rows) * (size_t)(p.D + 2) +
            sizeof(int32_t) * 2 * (size_t)(p.S * p.Hkv);
 }
 
@@ -115,8 +119,8 @@ int resident_waves_per_cu(const DecodePlan &p, int *waves)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return PA_ERR_HIP;
-    const long long key = ((((((long long)dev * 4 + p.variant) * 4 + p.q_type) * 4 + p.kv_type) *
-                            256 + p.D) * 64 + p.bs) * 32 + p.G;
+    const long long key = (((((((long long)dev * 4 + p.variant) * 4 + p.q_type) * 4 + p.kv_type) *
+                             256 + p.D) * 64 + p.bs) * 32 + p.G) * 8 + p.col_tiles;
     std::lock_guard<std::mutex> lock(mu);
     for (auto &kv : cache)
         if (kv.first == key) {
@@ -124,10 +128,12 @@ int resident_waves_per_cu(const DecodePlan &p, int *waves)
             return PA_OK;
         }
     int n = 0;
-    hipError_t e = p.variant == PA_VARIANT_MFMA
-                       ? decode_mfma_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G, &n)
-                       : decode_valu_occupancy(p.q_type, p.kv_type, (int)p.D, (int)p.bs,
-                                               (int)p.G, &n);
+    hipError_t e =
+        p.QM > 0 ? decode_mfma_multi_occupancy(p.kv_type, (int)p.D, (int)p.bs,
+                                               (int)p.col_tiles, &n)
+        : p.variant == PA_VARIANT_MFMA
+            ? decode_mfma_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G, &n)
+            : decode_valu_occupancy(p.q_type, p.kv_type, (int)p.D, (int)p.bs, (int)p.G, &n);
     if (e != hipSuccess || n <= 0)
         return PA_ERR_HIP;
     cache.emplace_back(key, n);
@@ -135,9 +141,11 @@ int resident_waves_per_cu(const DecodePlan &p, int *waves)
     return PA_OK;
 }
 
-// Shapes, dtypes and options common to pa_decode and pa_decode_workspace_size.
+// Shapes, dtypes and options common to the decode entry points and their
+// workspace queries.  qm = 0: one query token per sequence (q [S, H, D]);
+// qm > 0: several per sequence, at most qm (q [T, H, D], S from the tables).
 int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
-                const pa_opts *opts, DecodePlan *p)
+                const pa_opts *opts, int64_t qm, DecodePlan *p)
 {
     if (!q || !kc || !bt)
         return PA_ERR_NULL;
@@ -151,7 +159,9 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
     // Supported (q, cache) pairs: (f32, f32), (bf16, bf16), (bf16, e4m3).
     if (q->dtype == PA_F32 ? kvt != KT_F32 : kvt == KT_F32)
         return PA_ERR_DTYPE;
-    p->S = q->shape[0];
+    p->T = q->shape[0];
+    p->S = qm > 0 ? bt->shape[0] : q->shape[0];
+    p->QM = qm;
     p->H = q->shape[1];
     p->D = q->shape[2];
     p->NB = kc->shape[0];
@@ -165,13 +175,23 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
     if (!supported_head_dim(p->D) || !supported_block_size(p->bs) || !supported_group(p->G))
         return PA_ERR_UNSUPPORTED;
     if (p->S > INT32_MAX || p->NB > INT32_MAX || p->max_nb > INT32_MAX / p->bs ||
-        p->S * p->Hkv > INT32_MAX / 2)
+        p->S * p->Hkv > INT32_MAX / 2 || p->T > INT32_MAX / p->H)
         return PA_ERR_UNSUPPORTED;
     p->q_type = kv_type_of(q->dtype);
     p->kv_type = kvt;
 
     const int variant = opts ? opts->variant : PA_VARIANT_AUTO;
     const bool mfma_ok = mfma_supported(p->q_type, kvt, (int)p->D, (int)p->bs, (int)p->G);
+    p->col_tiles = 0;
+    p->rows = p->G;
+    if (qm > 0) {
+        // (query token, head) columns in tiles of 16, matrix cores only
+        if (!mfma_ok || variant == PA_VARIANT_VALU || qm > 16 || p->G * qm > 64)
+            return PA_ERR_UNSUPPORTED;
+        const int64_t cols = p->G * qm;
+        p->col_tiles = cols <= 16 ? 1 : (cols <= 32 ? 2 : 4);
+        p->rows = cols;
+    }
     if (variant == PA_VARIANT_AUTO)
         p->variant = mfma_ok ? PA_VARIANT_MFMA : PA_VARIANT_VALU;
     else if (variant == PA_VARIANT_VALU)
@@ -262,6 +282,95 @@ int block_op(const int32_t *ids, int64_t n, const void *const *src_bases,
         return PA_ERR_UNSUPPORTED;
     hipError_t e = launch_block_op(a, copy, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// pa_decode (qsl == NULL, qm == 0) and pa_decode_multi.
+int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_tensor *key_cache,
+               const pa_tensor *value_cache, const pa_tensor *block_tables,
+               const pa_tensor *seq_lens, float scale, pa_tensor *out, const pa_opts *opts,
+               void *hip_stream)
+{
+    int rc;
+    if ((rc = check_tensor(q, 3, 16)) || (rc = check_tensor(key_cache, 4, 16)) ||
+        (rc = check_tensor(value_cache, 4, 16)) || (rc = check_tensor(block_tables, 2, 4)) ||
+        (rc = check_tensor(seq_lens, 1, 4)) || (rc = check_tensor(out, 3, 16)) ||
+        (qsl && (rc = check_tensor(qsl, 1, 4))))
+        return rc;
+    if (value_cache->dtype != key_cache->dtype || out->dtype != q->dtype ||
+        seq_lens->dtype != PA_I32 || (qsl && qsl->dtype != PA_I32))
+        return PA_ERR_DTYPE;
+    for (int i = 0; i < 4; ++i)
+        if (value_cache->shape[i] != key_cache->shape[i])
+            return PA_ERR_SHAPE;
+    for (int i = 0; i < 3; ++i)
+        if (out->shape[i] != q->shape[i])
+            return PA_ERR_SHAPE;
+    const int64_t S = qsl ? block_tables->shape[0] : q->shape[0];
+    if (seq_lens->shape[0] != S || (qsl && qsl->shape[0] != S + 1))
+        return PA_ERR_SHAPE;
+    if (!isfinite(scale))
+        return PA_ERR_UNSUPPORTED;
+    const bool fp8 = key_cache->dtype == PA_FP8_E4M3;
+    const float ks = (fp8 && opts) ? opts->k_scale : 1.0f;
+    const float vs = (fp8 && opts) ? opts->v_scale : 1.0f;
+    if (fp8 && !(isfinite(ks) && ks > 0.0f && isfinite(vs) && vs > 0.0f))
+        return PA_ERR_UNSUPPORTED;
+    DecodePlan p;
+    if ((rc = plan_decode(q, key_cache, block_tables, opts, qm, &p)))
+        return rc;
+    if (p.S == 0 || p.T == 0)
+        return PA_OK;
+    if (!opts || !opts->workspace || opts->workspace_bytes < p.ws_bytes)
+        return PA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(opts->workspace) % 16)
+        return PA_ERR_ALIGN;
+
+    DecodeArgs a;
+    a.q = q->data;
+    a.key_cache = key_cache->data;
+    a.value_cache = value_cache->data;
+    a.block_tables = static_cast<const int32_t *>(block_tables->data);
+    a.seq_lens = static_cast<const int32_t *>(seq_lens->data);
+    a.out = out->data;
+    a.ws_acc = static_cast<float *>(opts->workspace);
+    a.ws_ml = a.ws_acc + p.slots * p.rows * p.D;
+    a.ws_seg = reinterpret_cast<int32_t *>(a.ws_ml + p.slots * p.rows * 2);
+    a.err_flag = opts->err_flag;
+    a.num_seqs = (int32_t)p.S;
+    a.num_heads = (int32_t)p.H;
+    a.num_kv_heads = (int32_t)p.Hkv;
+    a.max_nb = (int32_t)p.max_nb;
+    a.num_blocks = (int32_t)p.NB;
+    a.chunk_units = (int32_t)p.chunk_units;
+    a.num_waves = (int32_t)p.waves;
+    a.rows_per_slot = (int32_t)p.rows;
+    a.query_start_loc = qsl ? static_cast<const int32_t *>(qsl->data) : nullptr;
+    a.max_query_len = (int32_t)(qm > 0 ? qm : 1);
+    a.num_tokens = (int32_t)p.T;
+    a.log2_group = __builtin_ctz((unsigned)p.G);
+    a.qk_scale_log2 = scale * kLog2e * ks;
+    a.v_scale = vs;
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    hipEvent_t ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);
+    hipEvent_t ev1 = static_cast<hipEvent_t>(opts->kernel_events[1]);
+    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess)
+        return PA_ERR_HIP;
+    hipError_t e;
+    if (qm > 0)
+        e = launch_decode_mfma_multi(a, p.kv_type, (int)p.D, (int)p.bs, (int)p.col_tiles, stream);
+    else if (p.variant == PA_VARIANT_MFMA)
+        e = launch_decode_mfma(a, p.kv_type, (int)p.D, (int)p.bs, (int)p.G, stream);
+    else
+        e = launch_decode_valu(a, p.q_type, p.kv_type, (int)p.D, (int)p.bs, (int)p.G, stream);
+    if (e != hipSuccess)
+        return PA_ERR_HIP;
+    if (ev1 && hipEventRecord(ev1, stream) != hipSuccess)
+        return PA_ERR_HIP;
+    e = launch_merge(a, p.q_type, (int)p.D, (int)p.bs, stream);
+    if (e != hipSuccess)
+        return PA_ERR_HIP;
+    return PA_OK;
 }
 
 }  // namespace
@@ -374,7 +483,23 @@ int pa_decode_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
     if (!bytes)
         return PA_ERR_NULL;
     DecodePlan p;
-    int rc = plan_decode(q, key_cache, block_tables, opts, &p);
+    int rc = plan_decode(q, key_cache, block_tables, opts, 0, &p);
+    if (rc)
+        return rc;
+    *bytes = p.ws_bytes;
+    return PA_OK;
+}
+
+int pa_decode_multi_workspace_size(const pa_tensor *q, int32_t max_query_len,
+                                   const pa_tensor *key_cache, const pa_tensor *block_tables,
+                                   const pa_opts *opts, size_t *bytes)
+{
+    if (!bytes)
+        return PA_ERR_NULL;
+    if (max_query_len < 1)
+        return PA_ERR_UNSUPPORTED;
+    DecodePlan p;
+    int rc = plan_decode(q, key_cache, block_tables, opts, max_query_len, &p);
     if (rc)
         return rc;
     *bytes = p.ws_bytes;
@@ -385,78 +510,21 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
               const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,
               pa_tensor *out, const pa_opts *opts, void *hip_stream)
 {
-    int rc;
-    if ((rc = check_tensor(q, 3, 16)) || (rc = check_tensor(key_cache, 4, 16)) ||
-        (rc = check_tensor(value_cache, 4, 16)) || (rc = check_tensor(block_tables, 2, 4)) ||
-        (rc = check_tensor(seq_lens, 1, 4)) || (rc = check_tensor(out, 3, 16)))
-        return rc;
-    if (value_cache->dtype != key_cache->dtype || out->dtype != q->dtype ||
-        seq_lens->dtype != PA_I32)
-        return PA_ERR_DTYPE;
-    for (int i = 0; i < 4; ++i)
-        if (value_cache->shape[i] != key_cache->shape[i])
-            return PA_ERR_SHAPE;
-    for (int i = 0; i < 3; ++i)
-        if (out->shape[i] != q->shape[i])
-            return PA_ERR_SHAPE;
-    if (seq_lens->shape[0] != q->shape[0])
-        return PA_ERR_SHAPE;
-    if (!isfinite(scale))
-        return PA_ERR_UNSUPPORTED;
-    const bool fp8 = key_cache->dtype == PA_FP8_E4M3;
-    const float ks = (fp8 && opts) ? opts->k_scale : 1.0f;
-    const float vs = (fp8 && opts) ? opts->v_scale : 1.0f;
-    if (fp8 && !(isfinite(ks) && ks > 0.0f && isfinite(vs) && vs > 0.0f))
-        return PA_ERR_UNSUPPORTED;
-    DecodePlan p;
-    if ((rc = plan_decode(q, key_cache, block_tables, opts, &p)))
-        return rc;
-    if (p.S == 0)
-        return PA_OK;
-    if (!opts || !opts->workspace || opts->workspace_bytes < p.ws_bytes)
-        return PA_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(opts->workspace) % 16)
-        return PA_ERR_ALIGN;
+    return run_decode(q, nullptr, 0, key_cache, value_cache, block_tables, seq_lens, scale, out,
+                      opts, hip_stream);
+}
 
-    DecodeArgs a;
-    a.q = q->data;
-    a.key_cache = key_cache->data;
-    a.value_cache = value_cache->data;
-    a.block_tables = static_cast<const int32_t *>(block_tables->data);
-    a.seq_lens = static_cast<const int32_t *>(seq_lens->data);
-    a.out = out->data;
-    a.ws_acc = static_cast<float *>(opts->workspace);
-    a.ws_ml = a.ws_acc + p.slots * p.G * p.D;
-    a.ws_seg = reinterpret_cast<int32_t *>(a.ws_ml + p.slots * p.G * 2);
-    a.err_flag = opts->err_flag;
-    a.num_seqs = (int32_t)p.S;
-    a.num_heads = (int32_t)p.H;
-    a.num_kv_heads = (int32_t)p.Hkv;
-    a.max_nb = (int32_t)p.max_nb;
-    a.num_blocks = (int32_t)p.NB;
-    a.chunk_units = (int32_t)p.chunk_units;
-    a.num_waves = (int32_t)p.waves;
-    a.qk_scale_log2 = scale * kLog2e * ks;
-    a.v_scale = vs;
-
-    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    hipEvent_t ev0 = opts ? static_cast<hipEvent_t>(opts->kernel_events[0]) : nullptr;
-    hipEvent_t ev1 = opts ? static_cast<hipEvent_t>(opts->kernel_events[1]) : nullptr;
-    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess)
-        return PA_ERR_HIP;
-    hipError_t e;
-    if (p.variant == PA_VARIANT_MFMA)
-        e = launch_decode_mfma(a, p.kv_type, (int)p.D, (int)p.bs, (int)p.G, stream);
-    else
-        e = launch_decode_valu(a, p.q_type, p.kv_type, (int)p.D, (int)p.bs, (int)p.G, stream);
-    if (e != hipSuccess)
-        return PA_ERR_HIP;
-    if (ev1 && hipEventRecord(ev1, stream) != hipSuccess)
-        return PA_ERR_HIP;
-    e = launch_merge(a, p.q_type, (int)p.D, (int)p.bs, stream);
-    if (e != hipSuccess)
-        return PA_ERR_HIP;
-    return PA_OK;
+int pa_decode_multi(const pa_tensor *q, const pa_tensor *query_start_loc, int32_t max_query_len,
+                    const pa_tensor *key_cache, const pa_tensor *value_cache,
+                    const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,
+                    pa_tensor *out, const pa_opts *opts, void *hip_stream)
+{
+    if (!query_start_loc)
+        return PA_ERR_NULL;
+    if (max_query_len < 1)
+        return PA_ERR_UNSUPPORTED;
+    return run_decode(q, query_start_loc, max_query_len, key_cache, value_cache, block_tables,
+                      seq_lens, scale, out, opts, hip_stream);
 }
 
 }  // extern "C"

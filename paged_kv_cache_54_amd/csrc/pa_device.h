@@ -444,4 +444,23 @@ __device__ __forceinline__ void record_segment(const DecodeArgs &a, int g, int s
         rec[1] = slot;
 }
 
+// Query tokens of sequence s: first token and count, clamped to what the
+// layout allows (0 <= qs <= qe <= T, count <= max_query_len and <= L); a
+// sequence whose layout breaks the contract raises PA_DEVERR_QUERY when
+// `flag` is set.  Used by the multi-token decode kernel and the merge, so both
+// clamp alike.
+__device__ __forceinline__ void query_span(const DecodeArgs &a, int s, int L, int *qs_out,
+                                           int *ql_out, uint32_t *flag)
+{
+    const int qs = a.query_start_loc[s], qe = a.query_start_loc[s + 1];
+    const bool bad_range = qs < 0 || qe < qs || qe > a.num_tokens;
+    int ql = bad_range ? 0 : qe - qs;
+    const bool too_many = ql > a.max_query_len || ql > L;
+    ql = min(ql, min(a.max_query_len, L));
+    if ((bad_range || too_many) && flag)
+        raise_flag(flag, PA_DEVERR_QUERY);
+    *qs_out = bad_range ? 0 : qs;
+    *ql_out = ql;
+}
+
 }  // namespace pa

@@ -32,6 +32,12 @@ struct DecodeArgs {
     int32_t num_seqs, num_heads, num_kv_heads, max_nb, num_blocks;
     int32_t chunk_units;         // units per chunk, 0 = balanced over the grid
     int32_t num_waves;           // grid size (one wavefront per workgroup)
+    int32_t rows_per_slot;       // partial rows per slot: G, or G * max_query_len
+    // several query tokens per sequence (NULL query_start_loc: one per sequence)
+    const int32_t *query_start_loc; // [S + 1]
+    int32_t max_query_len;
+    int32_t num_tokens;          // T, rows of q and out
+    int32_t log2_group;          // G = 2^log2_group
     float qk_scale_log2;         // scale * log2(e) * k_scale (k_scale = 1 unless fp8)
     float v_scale;               // 1 unless fp8
 };
@@ -84,6 +90,13 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, int kv_type, int head_dim, in
                               int group, hipStream_t stream);
 bool mfma_supported(int q_type, int kv_type, int head_dim, int block_size, int group);
 
+// Matrix-core decode of several query tokens per sequence; col_tiles = 16-column
+// tiles of (query token, head) pairs per KV head, 1, 2 or 4.
+hipError_t launch_decode_mfma_multi(const DecodeArgs &a, int kv_type, int head_dim,
+                                    int block_size, int col_tiles, hipStream_t stream);
+hipError_t decode_mfma_multi_occupancy(int kv_type, int head_dim, int block_size, int col_tiles,
+                                       int *waves_per_cu);
+
 // Wavefronts (one-wavefront workgroups) of the matching decode kernel that one
 // compute unit holds at once.
 hipError_t decode_valu_occupancy(int q_type, int kv_type, int head_dim, int block_size, int group,
@@ -92,7 +105,8 @@ hipError_t decode_mfma_occupancy(int kv_type, int head_dim, int block_size, int 
                                  int *waves_per_cu);
 
 // Log-sum-exp merge of the chunk partials of every segment that more than
-// one chunk touched; zero rows for empty sequences.  Grid (S * H) of
+// one chunk touched; zero rows for empty sequences.  Grid (S * H), or
+// (S * max_query_len * H) with several query tokens per sequence, of
 // 256-thread workgroups.
 hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int block_size,
                         hipStream_t stream);

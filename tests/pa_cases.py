@@ -33,6 +33,13 @@ def gpu_step(b, kc, vc, **kw):
                      v_scale=b.v_scale, **kw)
 
 
+def gpu_step_multi(b, kc, vc, **kw):
+    """pa_kv_append of every new row, then pa_decode_multi."""
+    pa.kv_append(b.k_new, b.v_new, b.slot_mapping, kc, vc, b.k_scale, b.v_scale)
+    return pa.decode_multi(b.q, b.query_start_loc, b.max_query_len, kc, vc, b.block_tables,
+                           b.seq_lens, b.scale, k_scale=b.k_scale, v_scale=b.v_scale, **kw)
+
+
 def oracle_step(b):
     """Oracle output [S, H, D] and host caches for a whole batch."""
     return oracle.reference_step(b)
@@ -57,6 +64,27 @@ def oracle_rows(b, rows):
                      b.v_scale)
     out = oracle.decode(b.q.cpu(), kc, vc, tables, lens, b.scale, b.k_scale, b.v_scale, rows=rows)
     return out, kc, vc, slots
+
+
+def oracle_rows_multi(b, rows):
+    """Oracle output for flat rows token*H + h of a multi-token batch: host
+    caches hold the pool blocks of those rows' sequences (the oracle's own
+    append), then every new row; then multi-token decode of those rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    qsl = b.query_start_loc.cpu().numpy()
+    seqs = np.unique(np.searchsorted(qsl, rows // b.num_heads, side="right") - 1)
+    NB, bs, Hkv, D = b.num_blocks, b.block_size, b.num_kv_heads, b.head_dim
+    tables = b.block_tables.cpu().numpy()
+    lens = b.seq_lens.cpu().numpy()
+    blocks = np.unique(np.concatenate([tables[s, :-(-int(lens[s]) // bs)] for s in seqs]))
+    slots_t = torch.from_numpy((blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1))
+    kp = b.key_pool.view(NB * bs, Hkv, D)[slots_t.to(b.key_pool.device)].cpu()
+    vp = b.value_pool.view(NB * bs, Hkv, D)[slots_t.to(b.key_pool.device)].cpu()
+    kc, vc = oracle.fill_cache(b, kp, vp, slots_t)
+    oracle.kv_append(b.k_new.cpu(), b.v_new.cpu(), b.slot_mapping.cpu(), kc, vc, b.k_scale,
+                     b.v_scale)
+    return oracle.decode_multi(b.q.cpu(), b.query_start_loc.cpu(), kc, vc, tables, lens,
+                               b.scale, b.k_scale, b.v_scale, rows=rows)
 
 
 def check_close(got, ref, cache_dtype, what=""):

@@ -35,7 +35,8 @@ def lib():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["pa_kv_append", "pa_decode", "pa_decode_workspace_size", "pa_opts_init",
-         "pa_status_string", "pa_version", "pa_zero_blocks", "pa_copy_blocks"])
+         "pa_status_string", "pa_version", "pa_zero_blocks", "pa_copy_blocks",
+         "pa_decode_multi", "pa_decode_multi_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -218,3 +219,49 @@ def test_block_op_validation_errors():
     assert L.pa_copy_blocks(ids + 4, 5, bases, bases, 4, 4096, 4096, 100, 100, None, None) \
         == PA_ERR_ALIGN                                                  # pairs need 8 bytes
     assert L.pa_zero_blocks(ids, 5, bases + 4, 4, 4096, 4096, 100, None, None) == PA_ERR_ALIGN
+
+
+def call_multi(a, qsl, qm, o=None, scale=0.125):
+    r = lambda x: None if x is None else ctypes.byref(x)
+    return lib().pa_decode_multi(r(a["q"]), r(qsl), qm, r(a["kc"]), r(a["vc"]), r(a["bt"]),
+                                 r(a["lens"]), scale, r(a["out"]), r(o), None)
+
+
+def multi_args(T=10, S=3, H=8, Hkv=2, D=128, bs=16, NB=10, max_nb=4, qd=BF16, kd=BF16):
+    a = decode_args(S=T, H=H, Hkv=Hkv, D=D, bs=bs, NB=NB, max_nb=max_nb, qd=qd, kd=kd)
+    a["bt"] = desc([S, max_nb], I32)
+    a["lens"] = desc([S], I32)
+    return a, desc([S + 1], I32)
+
+
+def test_decode_multi_validation_errors():
+    a, qsl = multi_args(T=0)
+    assert call_multi(a, qsl, 4, opts(partition_tokens=64)) == PA_OK      # no query tokens
+    a, qsl = multi_args()
+    assert call_multi(a, None, 4) == PA_ERR_NULL
+    assert call_multi(a, qsl, 0) == PA_ERR_UNSUPPORTED
+    assert call_multi(a, qsl, 17) == PA_ERR_UNSUPPORTED
+    assert call_multi(*multi_args(H=16, Hkv=2), 9) == PA_ERR_UNSUPPORTED  # G 8 x 9 > 64 columns
+    assert call_multi(*multi_args(qd=F32, kd=F32), 4) == PA_ERR_UNSUPPORTED   # matrix cores only
+    assert call_multi(a, qsl, 4, opts(variant=1)) == PA_ERR_UNSUPPORTED
+    assert call_multi(a, desc([3], I32), 4) == PA_ERR_SHAPE                 # needs S + 1
+    assert call_multi(a, desc([4], I64), 4) == PA_ERR_DTYPE
+    b, _ = multi_args()
+    b["lens"] = desc([2], I32)
+    assert call_multi(b, qsl, 4) == PA_ERR_SHAPE
+    assert call_multi(a, qsl, 4, opts(partition_tokens=16)) == PA_ERR_WORKSPACE
+
+
+def test_decode_multi_workspace_formula():
+    a, _ = multi_args(S=3, H=8, Hkv=2, D=64, max_nb=10)
+    n = ctypes.c_size_t(0)
+    for qm, P in ((4, 32), (8, 160), (16, 16 * 64)):
+        rc = lib().pa_decode_multi_workspace_size(ctypes.byref(a["q"]), qm, ctypes.byref(a["kc"]),
+                                                  ctypes.byref(a["bt"]),
+                                                  ctypes.byref(opts(partition_tokens=P)),
+                                                  ctypes.byref(n))
+        assert rc == PA_OK
+        G = 4
+        chunks = -(-3 * 2 * 10 // (P // 16))
+        slots = chunks + 3 * 2
+        assert n.value == 4 * slots * G * qm * (64 + 2) + 8 * 3 * 2

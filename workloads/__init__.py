@@ -65,10 +65,18 @@ CONFIGS = {
         num_seqs=8, num_heads=64, num_kv_heads=8, head_dim=128, block_size=32,
         q_dtype="bf16", cache_dtype="fp8_e4m3", lens=("fixed", 131072), pool=("exact",),
         max_len=131072, partition_tokens=512),
+    # Speculative-decoding verify step on the Llama-3-8B-shaped batch: each
+    # sequence checks 7 drafted tokens plus the last accepted one (8 new query
+    # tokens; the P-EAGLE page reports its best speed-up at 7 drafts).
+    "llama3_8b_bf16_spec8": dict(
+        num_seqs=64, num_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+        q_dtype="bf16", cache_dtype="bf16", lens=("uniform", 512, 4096), pool=("factor", 1.2),
+        max_len=4096, partition_tokens=None, query_lens=("fixed", 8)),
 }
 
-# Seeds: one per workload, in the order the workloads are listed.
-SEEDS = {name: i + 1 for i, name in enumerate(CONFIGS)}
+# Seeds, one per workload (block workloads below take 6 to 8).
+SEEDS = {"tiny_f32": 1, "llama3_8b_bf16": 2, "qwen3_0p6b_bf16": 3, "shared_prefix_bf16": 4,
+         "long_fp8": 5, "llama3_8b_bf16_spec8": 9}
 
 _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 # Largest finite magnitude of the OCP E4M3FN format (exponent 1111, mantissa 110).
@@ -101,6 +109,15 @@ class DecodeBatch:
     v_scale: float = 1.0
     partition_tokens: Optional[int] = None
     poisoned: bool = False
+    # Several new tokens per sequence (None: one): sequence s owns rows
+    # query_start_loc[s] .. query_start_loc[s+1]-1 of q, k_new, v_new and
+    # slot_mapping, its last q_len positions in order.
+    query_start_loc: Optional[torch.Tensor] = None   # int32 [S + 1]
+    max_query_len: int = 1
+
+    @property
+    def num_query_tokens(self) -> int:
+        return self.q.shape[0]
 
     @property
     def group_size(self) -> int:
@@ -168,6 +185,16 @@ def make_batch(name: str = "tiny_f32", seed: Optional[int] = None, device="cpu",
     if lens.min() < 1 or lens.max() > max_nb * bs:
         raise ValueError("drawn length outside [1, capacity]")
     nblk = (lens + bs - 1) // bs
+    # 1b. new query tokens per sequence (multi-token workloads only)
+    qspec = cfg.get("query_lens")
+    if qspec is None:
+        qlens = np.ones(S, dtype=np.int64)
+    else:
+        qlens = np.minimum(_draw_lens(rng, qspec, S).astype(np.int64), lens)
+        if qlens.min() < 0:
+            raise ValueError("negative query length")
+    qsl = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    T = int(qsl[-1])
 
     # 2. placement of logical blocks in the physical pool
     pool = cfg["pool"]
@@ -206,15 +233,16 @@ def make_batch(name: str = "tiny_f32", seed: Optional[int] = None, device="cpu",
 
     # 3. values: q, pool K, pool V, new K rows, new V rows -- all N(0, 1)
     val_dtype = torch.float32 if cfg["cache_dtype"] == "f32" else torch.bfloat16
-    q = _randn((S, H, D), gen, device).to(_TORCH_DTYPE[cfg["q_dtype"]])
+    q = _randn((T, H, D), gen, device).to(_TORCH_DTYPE[cfg["q_dtype"]])
     key_pool = _randn((NB, bs, Hkv, D), gen, device, out_dtype=val_dtype)
     value_pool = _randn((NB, bs, Hkv, D), gen, device, out_dtype=val_dtype)
-    k_new = _randn((S, Hkv, D), gen, device).to(val_dtype)
-    v_new = _randn((S, Hkv, D), gen, device).to(val_dtype)
+    k_new = _randn((T, Hkv, D), gen, device).to(val_dtype)
+    v_new = _randn((T, Hkv, D), gen, device).to(val_dtype)
 
-    # 4. the slot of each sequence's newest token (position L-1)
-    last = lens - 1
-    slots = tables[np.arange(S), last // bs].astype(np.int64) * bs + (last % bs)
+    # 4. the slots of each sequence's new tokens (positions L-q_len .. L-1)
+    seq_of = np.repeat(np.arange(S), qlens)
+    pos = lens[seq_of] - qlens[seq_of] + (np.arange(T) - qsl[:-1][seq_of])
+    slots = tables[seq_of, pos // bs].astype(np.int64) * bs + (pos % bs)
 
     # 5. per-tensor fp8 scales: largest magnitude maps to the format's largest value
     k_scale = v_scale = 1.0
@@ -236,7 +264,9 @@ def make_batch(name: str = "tiny_f32", seed: Optional[int] = None, device="cpu",
         seq_lens=seq_lens_t, block_tables=tables_t, q=q, key_pool=key_pool,
         value_pool=value_pool, k_new=k_new, v_new=v_new,
         slot_mapping=torch.from_numpy(slots).to(device), k_scale=k_scale, v_scale=v_scale,
-        partition_tokens=cfg.get("partition_tokens"), poisoned=poison)
+        partition_tokens=cfg.get("partition_tokens"), poisoned=poison,
+        query_start_loc=None if qspec is None else torch.from_numpy(qsl).to(device),
+        max_query_len=1 if qspec is None else max(1, int(qlens.max())))
 
 
 def _randn(shape, gen, device, out_dtype=torch.float32, chunk=1 << 26):
@@ -299,7 +329,7 @@ BLOCK_CONFIGS = {
     "block_copy_cow": dict(op="copy", layers=32, block_size=16, kv_heads=8, head_dim=128,
                            elem_bytes=2, num_blocks=4096, items=256),
 }
-BLOCK_SEEDS = {name: len(CONFIGS) + i + 1 for i, name in enumerate(BLOCK_CONFIGS)}
+BLOCK_SEEDS = {name: 6 + i for i, name in enumerate(BLOCK_CONFIGS)}
 
 
 @dataclasses.dataclass
