@@ -32,6 +32,8 @@ KERNEL_SOURCES = {
                    "paged_kv_cache_54_amd/csrc/mfma_common.h",
                    "paged_kv_cache_54_amd/csrc/pa_device.h"],
 }
+KERNEL_SOURCES["blocks"] = ["paged_kv_cache_54_amd/csrc/blocks.hip",
+                            "paged_kv_cache_54_amd/csrc/pa_device.h"]
 KERNEL_NAMES = {"valu": "decode_valu_kernel", "mfma": "decode_mfma_kernel",
                 "mfma_multi": "decode_mfma_multi_kernel"}
 
@@ -99,14 +101,14 @@ def source_sha(variant):
     return h.hexdigest()
 
 
-def traffic_for(variant, workload):
+def traffic_for(variant, workload, kernel=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the kernel source as it stands now; else None."""
     try:
         data = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    rec = data.get(f"{KERNEL_NAMES[variant]}:{workload}")
+    rec = data.get(f"{kernel or KERNEL_NAMES[variant]}:{workload}")
     if not rec or rec.get("source_sha256") != source_sha(variant):
         return None
     return rec.get("traffic_bytes_per_launch")
@@ -269,6 +271,7 @@ def bench_blocks(args):
     value = nbytes / (ms * 1e-3) / 1e9
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     kname = "block_op_kernel<true>" if case.op == "copy" else "block_op_kernel<false>"
+    traffic = traffic_for("blocks", args.workload, kernel=kname)
     res = {
         "metric": f"block {'clear' if case.op == 'zero' else 'copy'}: achieved HBM GB/s "
                   f"({'bytes written' if case.op == 'zero' else 'bytes read + written'})",
@@ -281,7 +284,7 @@ def bench_blocks(args):
         "algorithmic_bytes_per_step": nbytes,
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel_ms": round(kernel_ms, 5),
                      "kernel_ms_from": f"HIP events around each of the {args.steps} launches",
                      "algorithmic_bytes_per_launch": nbytes},

@@ -6,150 +6,188 @@
 // A chunk's partial for one head holds acc_p = sum_t 2^(z_t - m_p) v_t,
 // l_p = sum_t 2^(z_t - m_p) and m_p (scores z in log2 units).  With
 // M = max_p m_p and w_p = 2^(m_p - M): out = sum_p w_p acc_p / sum_p w_p l_p,
-// which equals the softmax-weighted sum over the whole sequence.  Partials
-// with no tokens (m_p = -inf) get weight 0 by selection.  The segment record
-// gives the first and last slot of the segment; equal slots mean a single
-// chunk covered the segment and already wrote the output.
+// which equals the softmax-weighted sum over the whole sequence.  The sum is
+// taken online (M raised part by part, earlier terms rescaled), so every
+// partial is read once, in one pass.  Partials with no tokens (m_p = -inf)
+// get weight 0 by selection.  The segment record gives the first and last
+// slot of the segment; equal slots mean a single chunk covered the segment and
+// already wrote the output.
+//
+// Layout: WPR wavefronts per output row.  A partial row (D floats) is read
+// by D/4 lanes, so a wavefront reads 64/(D/4) partials per pass, four passes
+// unrolled; the lane groups' running (M, sum, acc) are combined by shuffles,
+// the wavefronts of a row through LDS.  One wavefront per row when there are
+// many rows (most segments split into a few parts), four when there are few
+// (long sequences cut into hundreds of parts).
 #include "pa_device.h"
 
 namespace pa {
 namespace {
 
-__device__ __forceinline__ float wave_max(float x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        x += __shfl_xor(x, off);
-    return x;
-}
-
 constexpr int kMergeThreads = 256;
 
-template <int OT, int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int block_size)
-{
-    constexpr int NT = kMergeThreads;
-    constexpr int LPP = D / 4;                   // threads per partial row (4 floats each)
-    constexpr int NSUB = NT / LPP;               // partial rows read per pass
-    __shared__ float wts[NT];
-    __shared__ float red[NT / 64];
-    __shared__ float4 part[NSUB][LPP];
+// Running log-sum-exp state of one lane: max M, weighted sum den, weighted
+// accumulator o (4 floats of the row).
+struct Lse {
+    float M, den;
+    float4 o;
+};
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int sub = t / LPP, col = (t % LPP) * 4;
+__device__ __forceinline__ void lse_add(Lse &s, float m, float l, float4 x)
+{
+    const float mn = fmaxf(s.M, m);
+    const float a = (s.M == mn) ? 1.f : __builtin_amdgcn_exp2f(s.M - mn);   // 0 when M = -inf
+    const float w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    s.M = mn;
+    s.den = s.den * a + w * l;
+    s.o.x = fmaf(w, x.x, s.o.x * a);
+    s.o.y = fmaf(w, x.y, s.o.y * a);
+    s.o.z = fmaf(w, x.z, s.o.z * a);
+    s.o.w = fmaf(w, x.w, s.o.w * a);
+}
+
+// Fold another state (its sum already weighted by its own M) into s.
+__device__ __forceinline__ void lse_fold(Lse &s, const Lse &t)
+{
+    const float mn = fmaxf(s.M, t.M);
+    const float a = (s.M == mn) ? 1.f : __builtin_amdgcn_exp2f(s.M - mn);
+    const float b = (t.M == mn) ? 1.f : __builtin_amdgcn_exp2f(t.M - mn);
+    s.M = mn;
+    s.den = s.den * a + t.den * b;
+    s.o.x = s.o.x * a + t.o.x * b;
+    s.o.y = s.o.y * a + t.o.y * b;
+    s.o.z = s.o.z * a + t.o.z * b;
+    s.o.w = s.o.w * a + t.o.w * b;
+}
+
+template <int OT, int D, int WPR>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int block_size,
+                                                               int64_t num_rows)
+{
+    constexpr int LPP = D / 4;                   // lanes per partial row (4 floats each)
+    constexpr int PPW = 64 / LPP;                // partials per wavefront pass
+    constexpr int UNROLL = 4;
+    constexpr int RPW = 4 / WPR;                 // rows per workgroup
+    __shared__ Lse part[4][LPP];
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sub = lane / LPP, col = (lane % LPP) * 4;
+    const int wr = wave % WPR;                   // wavefront within its row
+    const int64_t r = (int64_t)blockIdx.x * RPW + wave / WPR;
     const int H = a.num_heads, G = a.num_heads / a.num_kv_heads;
     const int RPS = a.rows_per_slot;
+
     // Output row and the row of its partials within a slot: one query token
-    // per sequence -- workgroup s * H + h, partial row h % G; several --
-    // workgroup (s * max_query_len + i) * H + h for query token i, partial
-    // row i * G + h % G (absent when the sequence has at most i tokens).
-    int s, h, prow;
-    int64_t row;
-    int L;
-    if (a.query_start_loc) {
-        const int64_t r = blockIdx.x;
-        h = (int)(r % H);
-        const int i = (int)((r / H) % a.max_query_len);
-        s = (int)(r / ((int64_t)H * a.max_query_len));
-        L = min(a.seq_lens[s], a.max_nb * block_size);
-        int qs, ql;
-        query_span(a, s, max(L, 0), &qs, &ql, nullptr);
-        if (i >= ql)
-            return;
-        row = (int64_t)(qs + i) * H + h;
-        prow = i * G + h % G;
-    } else {
-        row = blockIdx.x;
-        s = (int)(row / H);
-        h = (int)(row % H);
-        L = min(a.seq_lens[s], a.max_nb * block_size);
-        prow = h % G;
+    // per sequence -- grid row s * H + h, partial row h % G; several -- grid
+    // row (s * max_query_len + i) * H + h for query token i, partial row
+    // i * G + h % G (absent when the sequence has at most i tokens).
+    bool live = r < num_rows;
+    int s = 0, h = 0, prow = 0, L = 0, first = 0, n = 0;
+    int64_t row = 0;
+    if (live) {
+        if (a.query_start_loc) {
+            h = (int)(r % H);
+            const int i = (int)((r / H) % a.max_query_len);
+            s = (int)(r / ((int64_t)H * a.max_query_len));
+            L = min(a.seq_lens[s], a.max_nb * block_size);
+            int qs, ql;
+            query_span(a, s, max(L, 0), &qs, &ql, nullptr);
+            live = i < ql;
+            row = (int64_t)(qs + i) * H + h;
+            prow = i * G + h % G;
+        } else {
+            row = r;
+            s = (int)(r / H);
+            h = (int)(r % H);
+            L = min(a.seq_lens[s], a.max_nb * block_size);
+            prow = h % G;
+        }
+    }
+    bool zero_row = live && L <= 0;
+    if (live && L > 0) {
+        const int g = s * a.num_kv_heads + h / G;
+        first = a.ws_seg[2 * g];
+        const int last = a.ws_seg[2 * g + 1];
+        live = first != last;                    // else one chunk wrote the output
+        n = last - first + 1;
     }
 
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float inv = 0.f;
-    if (L > 0) {
-        const int g = s * a.num_kv_heads + h / G;
-        const int first = a.ws_seg[2 * g], last = a.ws_seg[2 * g + 1];
-        if (first == last)
-            return;                              // one chunk wrote the output
-        const int n = last - first + 1;
-        // partial p of this row lives at slot first + p, row prow
+    Lse st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
+    if (live && !zero_row) {
+        // partial p of this row: slot first + p, row prow
         const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (int64_t)first * RPS + prow;
         const float *acc = a.ws_acc + ((int64_t)first * RPS + prow) * D + col;
-
-        float M = -INFINITY;
-        for (int i = t; i < n; i += NT)
-            M = fmaxf(M, ml[(int64_t)i * RPS].x);
-        M = wave_max(M);
-        if (lane == 0)
-            red[wave] = M;
-        __syncthreads();
-        M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        __syncthreads();
-
-        // Thread i of each NT-partial chunk computes partial i's weight once;
-        // all threads then read it from LDS while accumulating 16-byte pieces.
-        float den = 0.f;
-        for (int c = 0; c < n; c += NT) {
-            float wgt = 0.f;
-            if (c + t < n) {
-                const float2 v = ml[(int64_t)(c + t) * RPS];
-                wgt = (v.x == -INFINITY) ? 0.f : exp2f(v.x - M);
-                den += wgt * v.y;
+        const int stride = WPR * PPW;
+        for (int p0 = wr * PPW + sub; p0 < n; p0 += UNROLL * stride) {
+            float2 mlv[UNROLL];
+            float4 x[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int p = p0 + u * stride;
+                if (p < n) {
+                    mlv[u] = ml[(int64_t)p * RPS];
+                    x[u] = *reinterpret_cast<const float4 *>(acc + (int64_t)p * RPS * D);
+                }
             }
-            wts[t] = wgt;
-            __syncthreads();
-            const int cnt = min(NT, n - c);
-#pragma unroll 4
-            for (int i = sub; i < cnt; i += NSUB) {
-                const float wi = wts[i];
-                const float4 x = *reinterpret_cast<const float4 *>(acc + (int64_t)(c + i) * RPS * D);
-                o.x = fmaf(wi, x.x, o.x);
-                o.y = fmaf(wi, x.y, o.y);
-                o.z = fmaf(wi, x.z, o.z);
-                o.w = fmaf(wi, x.w, o.w);
-            }
-            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                if (p0 + u * stride < n)
+                    lse_add(st, mlv[u].x, mlv[u].y, x[u]);
         }
-        den = wave_sum(den);
-        if (lane == 0)
-            red[wave] = den;
-        part[sub][t % LPP] = o;
+    }
+    // lane groups of the wavefront hold the same columns for different parts
+#pragma unroll
+    for (int off = LPP; off < 64; off <<= 1) {
+        Lse t;
+        t.M = __shfl_xor(st.M, off);
+        t.den = __shfl_xor(st.den, off);
+        t.o.x = __shfl_xor(st.o.x, off);
+        t.o.y = __shfl_xor(st.o.y, off);
+        t.o.z = __shfl_xor(st.o.z, off);
+        t.o.w = __shfl_xor(st.o.w, off);
+        lse_fold(st, t);
+    }
+    if constexpr (WPR > 1) {
+        if (sub == 0)
+            part[wave][lane] = st;
         __syncthreads();
-        den = red[0] + red[1] + red[2] + red[3];
-        inv = den > 0.f ? 1.f / den : 0.f;
-        if (sub != 0)
+        if (wr != 0)
             return;
 #pragma unroll
-        for (int k = 1; k < NSUB; ++k) {
-            const float4 y = part[k][t];
-            o.x += y.x;
-            o.y += y.y;
-            o.z += y.z;
-            o.w += y.w;
-        }
-    } else if (sub != 0) {
-        return;
+        for (int k = 1; k < WPR; ++k)
+            if (sub == 0)
+                lse_fold(st, part[wave + k][lane]);
     }
+    if (sub != 0 || !(live || zero_row))
+        return;
+    const float inv = st.den > 0.f ? 1.f / st.den : 0.f;
     const int64_t obase = row * D + col;
-    const float r[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+    const float o[4] = {st.o.x * inv, st.o.y * inv, st.o.z * inv, st.o.w * inv};
     if constexpr (OT == KT_F32) {
         *reinterpret_cast<float4 *>(static_cast<float *>(a.out) + obase) =
-            make_float4(r[0], r[1], r[2], r[3]);
+            make_float4(o[0], o[1], o[2], o[3]);
     } else {
         *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + obase) =
-            make_uint2(f32_to_bf16(r[0]) | (f32_to_bf16(r[1]) << 16),
-                       f32_to_bf16(r[2]) | (f32_to_bf16(r[3]) << 16));
+            make_uint2(f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16),
+                       f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16));
     }
+}
+
+template <int OT, int D>
+hipError_t launch(const DecodeArgs &a, int block_size, int64_t rows, hipStream_t stream)
+{
+    // Few rows: their sequences are long and cut into many parts; give each
+    // row a whole workgroup.
+    const bool wide = rows < 2048;
+    const int64_t wgs = wide ? rows : (rows + 3) / 4;
+    if (wgs > INT32_MAX)
+        return hipErrorInvalidValue;
+    dim3 grid((unsigned)wgs), block(kMergeThreads);
+    if (wide)
+        hipLaunchKernelGGL((merge_kernel<OT, D, 4>), grid, block, 0, stream, a, block_size, rows);
+    else
+        hipLaunchKernelGGL((merge_kernel<OT, D, 1>), grid, block, 0, stream, a, block_size, rows);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -159,20 +197,15 @@ hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int blo
 {
     const int64_t rows = (int64_t)a.num_seqs * a.num_heads *
                          (a.query_start_loc ? a.max_query_len : 1);
-    if (rows > INT32_MAX)
-        return hipErrorInvalidValue;
-    dim3 grid((unsigned)rows), block(kMergeThreads);
     if (out_type == KT_F32 && head_dim == 64)
-        hipLaunchKernelGGL((merge_kernel<KT_F32, 64>), grid, block, 0, stream, a, block_size);
-    else if (out_type == KT_F32 && head_dim == 128)
-        hipLaunchKernelGGL((merge_kernel<KT_F32, 128>), grid, block, 0, stream, a, block_size);
-    else if (out_type == KT_BF16 && head_dim == 64)
-        hipLaunchKernelGGL((merge_kernel<KT_BF16, 64>), grid, block, 0, stream, a, block_size);
-    else if (out_type == KT_BF16 && head_dim == 128)
-        hipLaunchKernelGGL((merge_kernel<KT_BF16, 128>), grid, block, 0, stream, a, block_size);
-    else
-        return hipErrorInvalidValue;
-    return hipGetLastError();
+        return launch<KT_F32, 64>(a, block_size, rows, stream);
+    if (out_type == KT_F32 && head_dim == 128)
+        return launch<KT_F32, 128>(a, block_size, rows, stream);
+    if (out_type == KT_BF16 && head_dim == 64)
+        return launch<KT_BF16, 64>(a, block_size, rows, stream);
+    if (out_type == KT_BF16 && head_dim == 128)
+        return launch<KT_BF16, 128>(a, block_size, rows, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace pa
