@@ -294,6 +294,90 @@ def bench_blocks(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_prep(args):
+    """One pa_prepare_step launch per step over a step-metadata workload;
+    value = microseconds per call (the work is a few hundred KB: latency)."""
+    import torch
+
+    import paged_kv_cache_54_amd as pa
+    import workloads
+
+    c = workloads.make_prep_case(args.workload, device="cuda:0")
+    S, R = c["idx_mapping"].numel(), c["num_computed"].numel()
+    max_nb, max_len = c["block_table"].shape[1], c["token_ids"].shape[1]
+    T = int(c["num_scheduled"].sum())
+    mt = c["max_tokens"]
+    nbytes = (12 * S + 4 * S * max_nb) + 8 * T + (8 * S + 4 + 20 * mt + 4 * S * max_nb)
+    ev = HipEvents(2 * args.steps)
+    stream = torch.cuda.current_stream().cuda_stream
+    outs = pa.prepare_step(c["idx_mapping"], c["num_scheduled"], c["num_computed"],
+                           c["block_table"], c["token_ids"], c["block_size"], c["num_blocks"], mt)
+    st = pa.PaStepState(c["num_computed"].data_ptr(), c["block_table"].data_ptr(),
+                        c["token_ids"].data_ptr(), R, max_nb, max_len)
+    io = pa.PaStepInputs(*[outs[k].data_ptr() for k in ("query_start_loc", "seq_lens",
+                                                          "positions", "input_ids",
+                                                          "slot_mapping", "block_tables")], mt)
+    lib = pa._load()
+    o = pa._opts()
+    by = ctypes.byref
+
+    def step(k=None):
+        if k is not None:
+            ev.record(2 * k, stream)
+        rc = lib.pa_prepare_step(c["idx_mapping"].data_ptr(), c["num_scheduled"].data_ptr(), S,
+                                 by(st), c["block_size"], c["num_blocks"], by(io), by(o), stream)
+        if rc:
+            raise pa.PaError("pa_prepare_step", rc)
+        if k is not None:
+            ev.record(2 * k + 1, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = sum(ev.elapsed_ms(2 * k, 2 * k + 1) for k in range(args.steps)) / args.steps
+    ev.close()
+    ms = wall / args.steps * 1e3
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    res = {
+        "metric": "step metadata prep: microseconds per call", "value": round(ms * 1e3, 3),
+        "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": args.workload, "reqs": S, "state_rows": R, "new_tokens": T,
+                   "max_tokens": mt, "max_blocks": max_nb},
+        "algorithmic_bytes_per_step": nbytes,
+        "roofline": {"bound": "hbm", "kernel": "step_prep_kernel", "achieved": round(achieved, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 6), "traffic": None,
+                     "kernel_ms": round(kernel_ms, 5),
+                     "kernel_ms_from": f"HIP events around each of the {args.steps} launches",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "note": "a few hundred KB per call: bound by launch latency, not HBM"},
+    }
+    if args.no_cpu_baseline:
+        res["cpu_baseline"] = None
+    else:
+        import oracle.step_prep as osp
+        h = {k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in c.items()}
+        done, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_budget_s and done < 200:
+            t1 = time.perf_counter()
+            osp.prepare_step(h["idx_mapping"], h["num_scheduled"], h["num_computed"],
+                             h["block_table"], h["token_ids"], h["block_size"], mt,
+                             h["num_blocks"])
+            t_cpu += time.perf_counter() - t1
+            done += 1
+        res["cpu_baseline"] = {"value": round(t_cpu / done * 1e6, 1), "unit": "us", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{done} whole calls in {t_cpu:.1f} s; python loops"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -321,6 +405,9 @@ def main():
         return
     if args.workload in workloads.BLOCK_CONFIGS:
         bench_blocks(args)
+        return
+    if args.workload in workloads.PREP_CONFIGS:
+        bench_prep(args)
         return
     b = workloads.make_batch(args.workload, device=dev)
     P = args.partition_tokens if args.partition_tokens is not None else (b.partition_tokens or 0)

@@ -83,6 +83,8 @@ typedef enum pa_status {
 #define PA_DEVERR_SEQ_LEN 0x2u   /* seq_len > table capacity: clamped */
 #define PA_DEVERR_SLOT 0x4u      /* slot >= num_blocks * block_size: token not written */
 #define PA_DEVERR_REGION 0x8u    /* block-op region base NULL or not 16-byte aligned: skipped */
+#define PA_DEVERR_STEP 0x20u     /* pa_prepare_step: bad state row, count or position, or the
+                                    step's tokens exceed max_tokens (see there) */
 #define PA_DEVERR_QUERY 0x10u    /* query_start_loc outside [0, T] or decreasing, or a sequence
                                     with more query tokens than max_query_len or seq_len: its
                                     query count clamped, rows beyond left unwritten */
@@ -269,6 +271,56 @@ int pa_copy_blocks(const int32_t *block_pairs, int64_t num_pairs, const void *co
                    void *const *dst_bases, int32_t num_regions, int64_t block_stride,
                    int64_t block_bytes, int64_t src_num_blocks, int64_t dst_num_blocks,
                    const pa_opts *opts, void *hip_stream);
+
+/*
+ * pa_prepare_step -- one step's attention inputs, built on the GPU from a
+ * persistent per-request state table (Model Runner V2 page, "better
+ * persistent batch and GPU-native input preparation": every active request
+ * keeps a stable row of a fixed-size state table and each step gathers its
+ * inputs in the current request order on the device, so that no host-device
+ * synchronisation is needed and device-side results -- the accepted token
+ * counts of speculative decoding -- can feed the next step directly).
+ *
+ * For batch entry i with state row r = idx_mapping[i] and n_i =
+ * num_scheduled[i] new tokens (token k at position num_computed[r] + k):
+ *   query_start_loc[i+1] = query_start_loc[i] + n_i      (query_start_loc[0] = 0)
+ *   seq_lens[i]          = num_computed[r] + n_i
+ *   block_tables[i, :]   = state block_table[r, :]
+ *   positions[t], input_ids[t] = token_ids[r, position], slot_mapping[t] =
+ *       block_table[r, position / block_size] * block_size + position % block_size
+ * Rows t >= query_start_loc[S] up to max_tokens are padding: slot -1 (which
+ * pa_kv_append skips), position 0, input id 0.  The outputs feed pa_kv_append
+ * (slot_mapping), pa_decode / pa_decode_multi (block_tables, seq_lens,
+ * query_start_loc) and the model (positions, input_ids).
+ *
+ * Every pointer is device memory (or device-readable host memory); int32
+ * arrays 4-byte and int64 arrays 8-byte aligned.  1 <= num_reqs <= 2048.
+ * Contract on device data: rows in [0, num_rows), counts and num_computed
+ * >= 0, the step's total <= max_tokens, positions < max_len and their blocks
+ * in the table and the pool.  A violation raises PA_DEVERR_STEP (entry
+ * dropped, or its count cut at max_tokens, or input id 0, or slot -1) or
+ * PA_DEVERR_BLOCK_ID (slot -1).
+ */
+typedef struct pa_step_state {
+    const int32_t *num_computed;  /* [num_rows] tokens of each request already in the cache */
+    const int32_t *block_table;   /* [num_rows, max_blocks] physical block ids */
+    const int32_t *token_ids;     /* [num_rows, max_len] each request's token ids */
+    int32_t num_rows, max_blocks, max_len;
+} pa_step_state;
+
+typedef struct pa_step_inputs {
+    int32_t *query_start_loc;     /* [num_reqs + 1] */
+    int32_t *seq_lens;            /* [num_reqs] */
+    int64_t *positions;           /* [max_tokens] */
+    int32_t *input_ids;           /* [max_tokens] */
+    int64_t *slot_mapping;        /* [max_tokens] */
+    int32_t *block_tables;        /* [num_reqs, max_blocks] */
+    int32_t max_tokens;
+} pa_step_inputs;
+
+int pa_prepare_step(const int32_t *idx_mapping, const int32_t *num_scheduled, int32_t num_reqs,
+                    const pa_step_state *state, int32_t block_size, int32_t num_blocks,
+                    const pa_step_inputs *out, const pa_opts *opts, void *hip_stream);
 
 /* Static description of a status code. */
 const char *pa_status_string(int status);

@@ -15,6 +15,7 @@ fallback implementation.
     zero_blocks(block_ids, regions)
     copy_blocks(block_pairs, src_regions, dst_regions)
     region_table(caches, device)
+    prepare_step(idx_mapping, num_scheduled, num_computed, block_table, token_ids, ...)
 """
 from __future__ import annotations
 
@@ -26,9 +27,9 @@ import torch
 
 __all__ = ["kv_append", "decode", "decode_workspace_size", "decode_multi",
            "decode_multi_workspace_size", "zero_blocks", "copy_blocks",
-           "region_table", "Regions", "PaError", "status_string", "version", "library_path",
+           "region_table", "Regions", "prepare_step", "PaError", "status_string", "version", "library_path",
            "VARIANT_AUTO", "VARIANT_VALU", "VARIANT_MFMA", "DEVERR_BLOCK_ID", "DEVERR_SEQ_LEN",
-           "DEVERR_SLOT", "DEVERR_REGION", "DEVERR_QUERY"]
+           "DEVERR_SLOT", "DEVERR_REGION", "DEVERR_QUERY", "DEVERR_STEP"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -36,6 +37,7 @@ _LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_F32, PA_BF16, PA_FP8_E4M3, PA_I32, PA_I64 = 0, 1, 2, 3, 4
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
 DEVERR_BLOCK_ID, DEVERR_SEQ_LEN, DEVERR_SLOT, DEVERR_REGION, DEVERR_QUERY = 0x1, 0x2, 0x4, 0x8, 0x10
+DEVERR_STEP = 0x20
 
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
            torch.float8_e4m3fn: PA_FP8_E4M3, torch.int32: PA_I32, torch.int64: PA_I64}
@@ -51,6 +53,19 @@ class PaOpts(ctypes.Structure):
                 ("partition_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("err_flag", ctypes.c_void_p), ("kernel_events", ctypes.c_void_p * 2)]
+
+
+class PaStepState(ctypes.Structure):
+    _fields_ = [("num_computed", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("token_ids", ctypes.c_void_p), ("num_rows", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("max_len", ctypes.c_int32)]
+
+
+class PaStepInputs(ctypes.Structure):
+    _fields_ = [("query_start_loc", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("positions", ctypes.c_void_p), ("input_ids", ctypes.c_void_p),
+                ("slot_mapping", ctypes.c_void_p), ("block_tables", ctypes.c_void_p),
+                ("max_tokens", ctypes.c_int32)]
 
 
 class PaError(RuntimeError):
@@ -99,6 +114,9 @@ def _load():
         lib.pa_version.restype = ctypes.c_int
         lib.pa_version.argtypes = []
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        lib.pa_prepare_step.restype = ctypes.c_int
+        lib.pa_prepare_step.argtypes = [vp, vp, i32, P(PaStepState), i32, i32, P(PaStepInputs),
+                                        P(PaOpts), vp]
         lib.pa_zero_blocks.restype = ctypes.c_int
         lib.pa_zero_blocks.argtypes = [vp, i64, vp, i32, i64, i64, i64, P(PaOpts), vp]
         lib.pa_copy_blocks.restype = ctypes.c_int
@@ -319,3 +337,41 @@ def copy_blocks(block_pairs: torch.Tensor, src: Regions, dst: Regions, err_flag=
                               _dev_ptr(src.bases, "src bases"), _dev_ptr(dst.bases, "dst bases"),
                               dst.bases.numel(), dst.block_stride, dst.block_bytes,
                               src.num_blocks, dst.num_blocks, ctypes.byref(o), _stream(stream)))
+
+
+def prepare_step(idx_mapping, num_scheduled, num_computed, block_table, token_ids, block_size,
+                 num_blocks, max_tokens, err_flag=None, stream=None):
+    """One step's inputs from the per-request state table (all int32 device
+    tensors: idx_mapping [S], num_scheduled [S], num_computed [R],
+    block_table [R, max_blocks], token_ids [R, max_len]).  Returns a dict of
+    device tensors: query_start_loc [S+1], seq_lens [S], positions int64
+    [max_tokens], input_ids [max_tokens], slot_mapping int64 [max_tokens],
+    block_tables [S, max_blocks]."""
+    for name, t in (("idx_mapping", idx_mapping), ("num_scheduled", num_scheduled),
+                    ("num_computed", num_computed), ("block_table", block_table),
+                    ("token_ids", token_ids)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous int32 tensor")
+    S = idx_mapping.numel()
+    if num_scheduled.numel() != S or block_table.dim() != 2 or token_ids.dim() != 2 or \
+            block_table.shape[0] != num_computed.numel() or token_ids.shape[0] != num_computed.numel():
+        raise ValueError("inconsistent state shapes")
+    dev = idx_mapping.device
+    out = dict(query_start_loc=torch.empty(S + 1, dtype=torch.int32, device=dev),
+               seq_lens=torch.empty(S, dtype=torch.int32, device=dev),
+               positions=torch.empty(max_tokens, dtype=torch.int64, device=dev),
+               input_ids=torch.empty(max_tokens, dtype=torch.int32, device=dev),
+               slot_mapping=torch.empty(max_tokens, dtype=torch.int64, device=dev),
+               block_tables=torch.empty((S, block_table.shape[1]), dtype=torch.int32, device=dev))
+    st = PaStepState(num_computed.data_ptr(), block_table.data_ptr(), token_ids.data_ptr(),
+                     num_computed.numel(), block_table.shape[1], token_ids.shape[1])
+    io = PaStepInputs(out["query_start_loc"].data_ptr(), out["seq_lens"].data_ptr(),
+                      out["positions"].data_ptr(), out["input_ids"].data_ptr(),
+                      out["slot_mapping"].data_ptr(), out["block_tables"].data_ptr(),
+                      int(max_tokens))
+    o = _opts(err_flag=err_flag)
+    _check("pa_prepare_step",
+           _load().pa_prepare_step(idx_mapping.data_ptr(), num_scheduled.data_ptr(), S,
+                                   ctypes.byref(st), int(block_size), int(num_blocks),
+                                   ctypes.byref(io), ctypes.byref(o), _stream(stream)))
+    return out

@@ -477,6 +477,53 @@ int pa_copy_blocks(const int32_t *block_pairs, int64_t num_pairs, const void *co
                     block_bytes, src_num_blocks, dst_num_blocks, opts, hip_stream);
 }
 
+int pa_prepare_step(const int32_t *idx_mapping, const int32_t *num_scheduled, int32_t num_reqs,
+                    const pa_step_state *state, int32_t block_size, int32_t num_blocks,
+                    const pa_step_inputs *out, const pa_opts *opts, void *hip_stream)
+{
+    if (!idx_mapping || !num_scheduled || !state || !out || !state->num_computed ||
+        !state->block_table || !state->token_ids || !out->query_start_loc || !out->seq_lens ||
+        !out->block_tables ||
+        (out->max_tokens > 0 && (!out->positions || !out->input_ids || !out->slot_mapping)))
+        return PA_ERR_NULL;
+    if (num_reqs < 1 || state->num_rows < 1 || state->max_blocks < 1 || state->max_len < 1 ||
+        out->max_tokens < 0 || block_size < 1 || num_blocks < 1)
+        return PA_ERR_SHAPE;
+    if (num_reqs > kMaxPrepReqs)
+        return PA_ERR_UNSUPPORTED;
+    const void *p4[] = {idx_mapping, num_scheduled, state->num_computed, state->block_table,
+                        state->token_ids, out->query_start_loc, out->seq_lens, out->input_ids,
+                        out->block_tables};
+    for (const void *p : p4)
+        if (reinterpret_cast<uintptr_t>(p) % 4)
+            return PA_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(out->positions) % 8 ||
+        reinterpret_cast<uintptr_t>(out->slot_mapping) % 8)
+        return PA_ERR_ALIGN;
+    StepPrepArgs a;
+    a.idx_mapping = idx_mapping;
+    a.num_scheduled = num_scheduled;
+    a.num_computed = state->num_computed;
+    a.block_table = state->block_table;
+    a.token_ids = state->token_ids;
+    a.query_start_loc = out->query_start_loc;
+    a.seq_lens = out->seq_lens;
+    a.positions = out->positions;
+    a.input_ids = out->input_ids;
+    a.slot_mapping = out->slot_mapping;
+    a.block_tables = out->block_tables;
+    a.err_flag = opts ? opts->err_flag : nullptr;
+    a.num_reqs = num_reqs;
+    a.num_rows = state->num_rows;
+    a.max_blocks = state->max_blocks;
+    a.max_len = state->max_len;
+    a.max_tokens = out->max_tokens;
+    a.block_size = block_size;
+    a.num_blocks = num_blocks;
+    hipError_t e = launch_step_prep(a, static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 int pa_decode_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
                              const pa_tensor *block_tables, const pa_opts *opts, size_t *bytes)
 {

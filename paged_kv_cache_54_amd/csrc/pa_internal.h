@@ -76,6 +76,25 @@ struct BlockOpArgs {
     int32_t group_items;         // 1 .. kMaxGroupItems
 };
 
+// One step's attention inputs gathered from a per-request state table.
+constexpr int kMaxPrepReqs = 2048;
+
+struct StepPrepArgs {
+    const int32_t *idx_mapping;   // [S] state row of each batch entry
+    const int32_t *num_scheduled; // [S] new tokens of each entry
+    const int32_t *num_computed;  // [R] tokens already in the cache, per state row
+    const int32_t *block_table;   // [R, max_blocks]
+    const int32_t *token_ids;     // [R, max_len]
+    int32_t *query_start_loc;     // [S + 1]
+    int32_t *seq_lens;            // [S]
+    int64_t *positions;           // [max_tokens]
+    int32_t *input_ids;           // [max_tokens]
+    int64_t *slot_mapping;        // [max_tokens]
+    int32_t *block_tables;        // [S, max_blocks]
+    uint32_t *err_flag;
+    int32_t num_reqs, num_rows, max_blocks, max_len, max_tokens, block_size, num_blocks;
+};
+
 // Launchers (defined in the .hip translation units).  Each returns a
 // hipError_t from hipGetLastError() after the launch.
 hipError_t launch_kv_append(const AppendArgs &a, int in_type, int cache_type,
@@ -110,6 +129,9 @@ hipError_t decode_mfma_occupancy(int kv_type, int head_dim, int block_size, int 
 // 256-thread workgroups.
 hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int block_size,
                         hipStream_t stream);
+
+// Step metadata from the state table; num_reqs <= kMaxPrepReqs.
+hipError_t launch_step_prep(const StepPrepArgs &a, hipStream_t stream);
 
 // Block clear (copy = false) or copy; chunk bytes per workgroup pass.
 hipError_t launch_block_op(const BlockOpArgs &a, bool copy, hipStream_t stream);

@@ -36,7 +36,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["pa_kv_append", "pa_decode", "pa_decode_workspace_size", "pa_opts_init",
          "pa_status_string", "pa_version", "pa_zero_blocks", "pa_copy_blocks",
-         "pa_decode_multi", "pa_decode_multi_workspace_size"])
+         "pa_decode_multi", "pa_decode_multi_workspace_size", "pa_prepare_step"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -265,3 +265,22 @@ def test_decode_multi_workspace_formula():
         chunks = -(-3 * 2 * 10 // (P // 16))
         slots = chunks + 3 * 2
         assert n.value == 4 * slots * G * qm * (64 + 2) + 8 * 3 * 2
+
+
+def test_prepare_step_validation_errors():
+    L = lib()
+    st = pa.PaStepState(FAKE, FAKE, FAKE, 10, 8, 128)
+    io = pa.PaStepInputs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 64)
+    call = lambda ids=FAKE, n=FAKE, S=4, s=st, bs=16, nb=100, o=io: L.pa_prepare_step(
+        ids, n, S, None if s is None else ctypes.byref(s), bs, nb,
+        None if o is None else ctypes.byref(o), None, None)
+    assert call(ids=None) == PA_ERR_NULL
+    assert call(s=None) == PA_ERR_NULL
+    assert call(o=pa.PaStepInputs(FAKE, FAKE, None, FAKE, FAKE, FAKE, 64)) == PA_ERR_NULL
+    assert call(S=0) == PA_ERR_SHAPE
+    assert call(bs=0) == PA_ERR_SHAPE
+    assert call(s=pa.PaStepState(FAKE, FAKE, FAKE, 0, 8, 128)) == PA_ERR_SHAPE
+    assert call(o=pa.PaStepInputs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1)) == PA_ERR_SHAPE
+    assert call(S=4096) == PA_ERR_UNSUPPORTED
+    assert call(ids=FAKE + 2) == PA_ERR_ALIGN
+    assert call(o=pa.PaStepInputs(FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, 64)) == PA_ERR_ALIGN

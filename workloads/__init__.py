@@ -373,3 +373,43 @@ def make_block_case(name: str, seed: Optional[int] = None, device="cpu",
         regions.append(torch.randint(1, 256, (NB, block_bytes), dtype=torch.uint8,
                                      device=device, generator=dev_gen))
     return BlockCase(name, cfg["op"], regions, items, block_bytes, NB)
+
+
+# --------------------------------------------------------------------------
+# Step-metadata workloads: a persistent state table of `rows` requests
+# (block tables of max_blocks entries over a pool of num_blocks, token ids up
+# to max_blocks * block_size) and one step's batch: `reqs` requests in a
+# random order, each with U{lo..hi} new tokens, outputs sized `max_tokens`.
+# "prep_decode" is the Llama-3-8B-shaped decode batch (64 requests, one token
+# each); "prep_mixed" a chunked-prefill-sized step (256 requests, up to 32
+# new tokens each, 8192 token rows).
+# --------------------------------------------------------------------------
+PREP_CONFIGS = {
+    "prep_decode": dict(rows=256, reqs=64, new=(1, 1), max_tokens=64, block_size=16,
+                        max_blocks=256, num_blocks=16384),
+    "prep_mixed": dict(rows=1024, reqs=256, new=(0, 32), max_tokens=8192, block_size=16,
+                       max_blocks=256, num_blocks=65536),
+}
+PREP_SEEDS = {"prep_decode": 10, "prep_mixed": 11}
+
+
+def make_prep_case(name: str, seed: Optional[int] = None, device="cpu", **overrides) -> dict:
+    """State table and step batch (int32 tensors on ``device``) of workload
+    ``name``: idx_mapping, num_scheduled, num_computed, block_table, token_ids,
+    plus block_size, num_blocks, max_tokens.  Every request has room in its
+    table for its computed and new tokens."""
+    cfg = dict(PREP_CONFIGS[name])
+    cfg.update(overrides)
+    rng = np.random.default_rng(PREP_SEEDS.get(name, 0) if seed is None else seed)
+    R, S, bs, max_nb = cfg["rows"], cfg["reqs"], cfg["block_size"], cfg["max_blocks"]
+    max_len = max_nb * bs
+    lo, hi = cfg["new"]
+    n = rng.integers(lo, hi + 1, S)
+    computed = rng.integers(0, max_len - hi, R)
+    block_table = rng.integers(0, cfg["num_blocks"], size=(R, max_nb))
+    token_ids = rng.integers(0, 150000, size=(R, max_len))
+    idx = rng.permutation(R)[:S]
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x).astype(np.int32)).to(device)
+    return dict(idx_mapping=t(idx), num_scheduled=t(n), num_computed=t(computed),
+                block_table=t(block_table), token_ids=t(token_ids), block_size=bs,
+                num_blocks=cfg["num_blocks"], max_tokens=cfg["max_tokens"])
