@@ -34,8 +34,11 @@ KERNEL_SOURCES = {
 }
 KERNEL_SOURCES["blocks"] = ["paged_kv_cache_54_amd/csrc/blocks.hip",
                             "paged_kv_cache_54_amd/csrc/pa_device.h"]
+KERNEL_SOURCES["cascade"] = KERNEL_SOURCES["mfma"] + ["paged_kv_cache_54_amd/csrc/decode_mfma_multi.hip",
+                                                      "paged_kv_cache_54_amd/csrc/cascade.hip"]
 KERNEL_NAMES = {"valu": "decode_valu_kernel", "mfma": "decode_mfma_kernel",
-                "mfma_multi": "decode_mfma_multi_kernel"}
+                "mfma_multi": "decode_mfma_multi_kernel",
+                "cascade": "decode_mfma_multi_kernel + decode_mfma_kernel"}
 
 
 def parse():
@@ -46,6 +49,9 @@ def parse():
     ap.add_argument("--workload", default="llama3_8b_bf16")
     ap.add_argument("--variant", default="auto", choices=["auto", "valu", "mfma"])
     ap.add_argument("--partition-tokens", type=int, default=None)
+    ap.add_argument("--no-cascade", action="store_true",
+                    help="for a batch with a shared prefix, use plain pa_decode instead of "
+                         "pa_decode_cascade")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--event-every", type=int, default=8,
@@ -424,7 +430,12 @@ def main():
         kc, vc = b.key_pool.clone(), b.value_pool.clone()
     out = torch.empty_like(b.q)
     multi = b.query_start_loc is not None
-    if multi:
+    cascade = (b.shared_prefix_blocks > 0 and not args.no_cascade and b.q_dtype == "bf16"
+               and variant != pa.VARIANT_VALU)
+    if cascade:
+        ws_bytes = pa.decode_cascade_workspace_size(b.q, kc, b.block_tables,
+                                                    b.shared_prefix_blocks, P, variant)
+    elif multi:
         ws_bytes = pa.decode_multi_workspace_size(b.q, b.max_query_len, kc, b.block_tables, P,
                                                   variant)
     else:
@@ -455,7 +466,11 @@ def main():
         else:
             o.kernel_events[0], o.kernel_events[1] = ev.ev[2 * k], ev.ev[2 * k + 1]
         rc = lib.pa_kv_append(by(d_k), by(d_v), by(d_slot), by(d_kc), by(d_vc), by(o), stream)
-        if multi:
+        if cascade:
+            rc = rc or lib.pa_decode_cascade(by(d_q), by(d_kc), by(d_vc), by(d_bt), by(d_len),
+                                             b.shared_prefix_blocks, ctypes.c_float(b.scale),
+                                             by(d_out), by(o), stream)
+        elif multi:
             rc = rc or lib.pa_decode_multi(by(d_q), by(d_qsl), b.max_query_len, by(d_kc),
                                            by(d_vc), by(d_bt), by(d_len), ctypes.c_float(b.scale),
                                            by(d_out), by(o), stream)
@@ -481,6 +496,8 @@ def main():
     value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
     used = "mfma_multi" if multi else "mfma" if (variant == pa.VARIANT_MFMA or (
         variant == pa.VARIANT_AUTO and _mfma_ok(pa, b, kc))) else "valu"
+    if cascade:
+        used = "cascade"
     achieved = nbytes["decode"] / (kernel_ms * 1e-3) / 1e9
     traffic = traffic_for(used, args.workload)
     res = {
@@ -502,6 +519,7 @@ def main():
                    "mean_seq_len": round(nbytes["logical_tokens"] / b.num_seqs, 1),
                    "q_dtype": b.q_dtype, "cache_dtype": b.cache_dtype,
                    "partition_tokens": P or "auto", "variant": used,
+                   **({"shared_prefix_blocks": b.shared_prefix_blocks} if cascade else {}),
                    **({"query_tokens": b.q.shape[0], "max_query_len": b.max_query_len}
                       if multi else {})},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),

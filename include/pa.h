@@ -85,6 +85,9 @@ typedef enum pa_status {
 #define PA_DEVERR_REGION 0x8u    /* block-op region base NULL or not 16-byte aligned: skipped */
 #define PA_DEVERR_STEP 0x20u     /* pa_prepare_step: bad state row, count or position, or the
                                     step's tokens exceed max_tokens (see there) */
+#define PA_DEVERR_PREFIX 0x40u   /* pa_decode_cascade: a table not starting with the shared
+                                    prefix, or a sequence shorter than it (its output is
+                                    then not the attention over its own blocks) */
 #define PA_DEVERR_QUERY 0x10u    /* query_start_loc outside [0, T] or decreasing, or a sequence
                                     with more query tokens than max_query_len or seq_len: its
                                     query count clamped, rows beyond left unwritten */
@@ -215,6 +218,32 @@ int pa_decode_multi(const pa_tensor *q, const pa_tensor *query_start_loc, int32_
 int pa_decode_multi_workspace_size(const pa_tensor *q, int32_t max_query_len,
                                    const pa_tensor *key_cache, const pa_tensor *block_tables,
                                    const pa_opts *opts, size_t *bytes);
+
+/*
+ * pa_decode_cascade -- pa_decode for a batch whose sequences share their
+ * first prefix_blocks logical blocks (the same physical blocks: a common
+ * prompt, vLLM internals blog section 1 and figure 1).  Equal to pa_decode
+ * within its tolerance, but the shared blocks are read once per group of
+ * sequences instead of once per sequence: the attention is split at the
+ * prefix boundary into a pass of all queries over the shared blocks and a
+ * pass of each query over its own later blocks, joined by log-sum-exp.
+ *
+ *   prefix_blocks  0 <= N < max_blocks_per_seq (0: exactly pa_decode)
+ *   the rest as pa_decode; matrix-core kernels only (bf16 q, bf16 or e4m3
+ *   cache; PA_ERR_UNSUPPORTED otherwise).  Workspace:
+ *   pa_decode_cascade_workspace_size bytes.
+ * Contract on device data: block_tables[s][j] == block_tables[0][j] for
+ * j < N and seq_lens[s] >= N * block_size for every s; a violation raises
+ * PA_DEVERR_PREFIX.
+ */
+int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
+                      const pa_tensor *value_cache, const pa_tensor *block_tables,
+                      const pa_tensor *seq_lens, int32_t prefix_blocks, float scale,
+                      pa_tensor *out, const pa_opts *opts, void *hip_stream);
+
+int pa_decode_cascade_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
+                                     const pa_tensor *block_tables, int32_t prefix_blocks,
+                                     const pa_opts *opts, size_t *bytes);
 
 /*
  * Block maintenance.  A "region" is one cache of the pool layout, for example

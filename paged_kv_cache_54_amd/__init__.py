@@ -11,6 +11,7 @@ fallback implementation.
     decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, ...)
     decode_workspace_size(q, key_cache, block_tables, ...)
     decode_multi(q, query_start_loc, max_query_len, key_cache, value_cache, ...)
+    decode_cascade(q, key_cache, value_cache, block_tables, seq_lens, prefix_blocks, scale, ...)
     decode_multi_workspace_size(q, max_query_len, key_cache, block_tables, ...)
     zero_blocks(block_ids, regions)
     copy_blocks(block_pairs, src_regions, dst_regions)
@@ -25,11 +26,12 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["kv_append", "decode", "decode_workspace_size", "decode_multi",
+__all__ = ["kv_append", "decode", "decode_workspace_size", "decode_multi", "decode_cascade",
+           "decode_cascade_workspace_size",
            "decode_multi_workspace_size", "zero_blocks", "copy_blocks",
            "region_table", "Regions", "prepare_step", "PaError", "status_string", "version", "library_path",
            "VARIANT_AUTO", "VARIANT_VALU", "VARIANT_MFMA", "DEVERR_BLOCK_ID", "DEVERR_SEQ_LEN",
-           "DEVERR_SLOT", "DEVERR_REGION", "DEVERR_QUERY", "DEVERR_STEP"]
+           "DEVERR_SLOT", "DEVERR_REGION", "DEVERR_QUERY", "DEVERR_STEP", "DEVERR_PREFIX"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpa.so")
@@ -37,7 +39,7 @@ _LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_F32, PA_BF16, PA_FP8_E4M3, PA_I32, PA_I64 = 0, 1, 2, 3, 4
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
 DEVERR_BLOCK_ID, DEVERR_SEQ_LEN, DEVERR_SLOT, DEVERR_REGION, DEVERR_QUERY = 0x1, 0x2, 0x4, 0x8, 0x10
-DEVERR_STEP = 0x20
+DEVERR_STEP, DEVERR_PREFIX = 0x20, 0x40
 
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8_E4M3,
            torch.float8_e4m3fn: PA_FP8_E4M3, torch.int32: PA_I32, torch.int64: PA_I64}
@@ -96,6 +98,14 @@ def _load():
         lib.pa_decode.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor), P(PaTensor),
                                   P(PaTensor), ctypes.c_float, P(PaTensor), P(PaOpts),
                                   ctypes.c_void_p]
+        lib.pa_decode_cascade.restype = ctypes.c_int
+        lib.pa_decode_cascade.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor), P(PaTensor),
+                                          P(PaTensor), ctypes.c_int32, ctypes.c_float,
+                                          P(PaTensor), P(PaOpts), ctypes.c_void_p]
+        lib.pa_decode_cascade_workspace_size.restype = ctypes.c_int
+        lib.pa_decode_cascade_workspace_size.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor),
+                                                         ctypes.c_int32, P(PaOpts),
+                                                         P(ctypes.c_size_t)]
         lib.pa_decode_multi.restype = ctypes.c_int
         lib.pa_decode_multi.argtypes = [P(PaTensor), P(PaTensor), ctypes.c_int32, P(PaTensor),
                                         P(PaTensor), P(PaTensor), P(PaTensor), ctypes.c_float,
@@ -226,6 +236,42 @@ def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, k
     _check("pa_decode", lib.pa_decode(*[ctypes.byref(x) for x in args], float(scale),
                                       ctypes.byref(describe(out)), ctypes.byref(o),
                                       _stream(stream)))
+    return out
+
+
+def decode_cascade_workspace_size(q, key_cache, block_tables, prefix_blocks, partition_tokens=0,
+                                  variant=VARIANT_AUTO) -> int:
+    lib = _load()
+    o = _opts(partition_tokens=partition_tokens, variant=variant)
+    n = ctypes.c_size_t(0)
+    _check("pa_decode_cascade_workspace_size",
+           lib.pa_decode_cascade_workspace_size(ctypes.byref(describe(q)),
+                                                ctypes.byref(describe(key_cache)),
+                                                ctypes.byref(describe(block_tables)),
+                                                int(prefix_blocks), ctypes.byref(o),
+                                                ctypes.byref(n)))
+    return n.value
+
+
+def decode_cascade(q, key_cache, value_cache, block_tables, seq_lens, prefix_blocks, scale,
+                   out=None, k_scale=1.0, v_scale=1.0, partition_tokens=0, variant=VARIANT_AUTO,
+                   workspace=None, err_flag=None, events=None, stream=None):
+    """pa_decode for a batch whose sequences share their first prefix_blocks
+    blocks: the shared blocks are read once per group of sequences."""
+    lib = _load()
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        need = decode_cascade_workspace_size(q, key_cache, block_tables, prefix_blocks,
+                                             partition_tokens, variant)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events)
+    args = [describe(x) for x in (q, key_cache, value_cache, block_tables, seq_lens)]
+    _check("pa_decode_cascade",
+           lib.pa_decode_cascade(*[ctypes.byref(x) for x in args], int(prefix_blocks),
+                                 float(scale), ctypes.byref(describe(out)), ctypes.byref(o),
+                                 _stream(stream)))
     return out
 
 

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a)
         if (c16 >= G)
             return;                            // replicated columns
         const int64_t row = (int64_t)c.s * H + c.kvh * G + c16;
-        if (seg_starts && ends) {
+        if (seg_starts && ends && !(a.flags & kPartialOnly)) {
             const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
             uint16_t *o = static_cast<uint16_t *>(a.out) + row * D + 4 * g4;
 #pragma unroll

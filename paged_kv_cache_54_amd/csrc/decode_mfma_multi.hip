@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
             const int col = 16 * nt + c16;
             const int i = col >> lg, g = col & (G - 1);
             const bool valid = i < ql;
-            lim[nt] = valid ? c.L - ql + i + 1 : 0;
+            lim[nt] = !valid ? 0 : (a.flags & kNonCausal) ? c.L : c.L - ql + i + 1;
             orow[nt] = valid ? (int64_t)(qs + i) * H + c.kvh * G + g : -1;
             const uint16_t *qrow =
                 static_cast<const uint16_t *>(a.q) + (valid ? orow[nt] : 0) * D + 8 * g4;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
             lt += __shfl_xor(lt, 32);
             if (orow[nt] < 0)
                 continue;
-            if (seg_starts && ends) {
+            if (seg_starts && ends && !(a.flags & kPartialOnly)) {
                 const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
                 uint16_t *o = static_cast<uint16_t *>(a.out) + orow[nt] * D + 4 * g4;
 #pragma unroll

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -350,6 +351,7 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     a.log2_group = __builtin_ctz((unsigned)p.G);
     a.qk_scale_log2 = scale * kLog2e * ks;
     a.v_scale = vs;
+    a.flags = 0;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     hipEvent_t ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);
@@ -370,6 +372,75 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     e = launch_merge(a, p.q_type, (int)p.D, (int)p.bs, stream);
     if (e != hipSuccess)
         return PA_ERR_HIP;
+    return PA_OK;
+}
+
+// A descriptor with another shape (data pointer and dtype kept); dense strides.
+pa_tensor reshaped(const pa_tensor *t, std::initializer_list<int64_t> shape)
+{
+    pa_tensor r = *t;
+    r.ndim = (int32_t)shape.size();
+    int i = 0;
+    for (int64_t n : shape)
+        r.shape[i++] = n;
+    int64_t acc = 1;
+    for (int k = r.ndim - 1; k >= 0; --k) {
+        r.stride[k] = acc;
+        acc *= r.shape[k];
+    }
+    return r;
+}
+
+// The cascade's layout: setup arrays, then the prefix pass's and the suffix
+// pass's workspaces (each 256-byte aligned).
+struct CascadePlan {
+    DecodePlan pre, suf;
+    int64_t S, N, V, spg;
+    size_t setup_bytes, pre_off, suf_off, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int plan_cascade(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt, int64_t N,
+                 const pa_opts *opts, CascadePlan *c)
+{
+    if (!q || !kc || !bt)
+        return PA_ERR_NULL;
+    if (q->ndim != 3 || kc->ndim != 4 || bt->ndim != 2)
+        return PA_ERR_SHAPE;
+    const int64_t S = q->shape[0], max_nb = bt->shape[1];
+    if (N < 1 || N >= max_nb)
+        return PA_ERR_UNSUPPORTED;
+    if (q->shape[1] <= 0 || kc->shape[2] <= 0 || q->shape[1] % kc->shape[2])
+        return PA_ERR_SHAPE;
+    const int64_t G = q->shape[1] / kc->shape[2];
+    if (!supported_group(G))
+        return PA_ERR_UNSUPPORTED;
+    // sequences per virtual prefix sequence: at most 64 (sequence, head) columns
+    // and at most 16 query rows per virtual sequence
+    const int64_t spg = (64 / G) < 16 ? 64 / G : 16;
+    const int64_t V = (S + spg - 1) / spg;
+    pa_opts o;
+    pa_opts_init(&o);
+    if (opts)
+        o = *opts;
+    o.variant = PA_VARIANT_MFMA;
+    pa_opts po = o;
+    po.partition_tokens = 0;                   // the prefix pass: balanced split
+    const pa_tensor bt_pre = reshaped(bt, {V > 0 ? V : 1, N});
+    const pa_tensor bt_suf = reshaped(bt, {S, max_nb - N});
+    int rc;
+    if ((rc = plan_decode(q, kc, &bt_pre, &po, spg, &c->pre)) ||
+        (rc = plan_decode(q, kc, &bt_suf, &o, 0, &c->suf)))
+        return rc;
+    c->S = S;
+    c->N = N;
+    c->V = V;
+    c->spg = spg;
+    c->setup_bytes = align256(sizeof(int32_t) * (size_t)(V * N + V + V + 1 + S * (max_nb - N) + S));
+    c->pre_off = c->setup_bytes;
+    c->suf_off = c->pre_off + align256(c->pre.ws_bytes);
+    c->total = S > 0 ? c->suf_off + align256(c->suf.ws_bytes) : 0;
     return PA_OK;
 }
 
@@ -559,6 +630,156 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
 {
     return run_decode(q, nullptr, 0, key_cache, value_cache, block_tables, seq_lens, scale, out,
                       opts, hip_stream);
+}
+
+int pa_decode_cascade_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
+                                     const pa_tensor *block_tables, int32_t prefix_blocks,
+                                     const pa_opts *opts, size_t *bytes)
+{
+    if (!bytes)
+        return PA_ERR_NULL;
+    if (prefix_blocks == 0)
+        return pa_decode_workspace_size(q, key_cache, block_tables, opts, bytes);
+    CascadePlan c;
+    int rc = plan_cascade(q, key_cache, block_tables, prefix_blocks, opts, &c);
+    if (rc)
+        return rc;
+    *bytes = c.total;
+    return PA_OK;
+}
+
+int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
+                      const pa_tensor *value_cache, const pa_tensor *block_tables,
+                      const pa_tensor *seq_lens, int32_t prefix_blocks, float scale,
+                      pa_tensor *out, const pa_opts *opts, void *hip_stream)
+{
+    if (prefix_blocks == 0)
+        return pa_decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out, opts,
+                         hip_stream);
+    if (prefix_blocks < 0)
+        return PA_ERR_UNSUPPORTED;
+    int rc;
+    if ((rc = check_tensor(q, 3, 16)) || (rc = check_tensor(key_cache, 4, 16)) ||
+        (rc = check_tensor(value_cache, 4, 16)) || (rc = check_tensor(block_tables, 2, 4)) ||
+        (rc = check_tensor(seq_lens, 1, 4)) || (rc = check_tensor(out, 3, 16)))
+        return rc;
+    if (value_cache->dtype != key_cache->dtype || out->dtype != q->dtype ||
+        seq_lens->dtype != PA_I32)
+        return PA_ERR_DTYPE;
+    for (int i = 0; i < 4; ++i)
+        if (value_cache->shape[i] != key_cache->shape[i])
+            return PA_ERR_SHAPE;
+    for (int i = 0; i < 3; ++i)
+        if (out->shape[i] != q->shape[i])
+            return PA_ERR_SHAPE;
+    if (seq_lens->shape[0] != q->shape[0] || block_tables->shape[0] != q->shape[0])
+        return PA_ERR_SHAPE;
+    if (!isfinite(scale))
+        return PA_ERR_UNSUPPORTED;
+    if (q->dtype != PA_BF16 || (opts && opts->variant == PA_VARIANT_VALU))
+        return PA_ERR_UNSUPPORTED;
+    const bool fp8 = key_cache->dtype == PA_FP8_E4M3;
+    const float ks = (fp8 && opts) ? opts->k_scale : 1.0f;
+    const float vs = (fp8 && opts) ? opts->v_scale : 1.0f;
+    if (fp8 && !(isfinite(ks) && ks > 0.0f && isfinite(vs) && vs > 0.0f))
+        return PA_ERR_UNSUPPORTED;
+    CascadePlan c;
+    if ((rc = plan_cascade(q, key_cache, block_tables, prefix_blocks, opts, &c)))
+        return rc;
+    if (c.S == 0)
+        return PA_OK;
+    if (!opts || !opts->workspace || opts->workspace_bytes < c.total)
+        return PA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(opts->workspace) % 16)
+        return PA_ERR_ALIGN;
+    const int64_t S = c.S, N = c.N, V = c.V, max_nb = block_tables->shape[1];
+    const DecodePlan &pp = c.pre, &sp = c.suf;
+    uint8_t *ws = static_cast<uint8_t *>(opts->workspace);
+
+    CascadeSetupArgs su;
+    su.block_tables = static_cast<const int32_t *>(block_tables->data);
+    su.seq_lens = static_cast<const int32_t *>(seq_lens->data);
+    su.p_tables = reinterpret_cast<int32_t *>(ws);
+    su.p_lens = su.p_tables + V * N;
+    su.p_qsl = su.p_lens + V;
+    su.s_tables = su.p_qsl + V + 1;
+    su.s_lens = su.s_tables + S * (max_nb - N);
+    su.err_flag = opts->err_flag;
+    su.num_seqs = (int32_t)S;
+    su.max_nb = (int32_t)max_nb;
+    su.prefix_blocks = (int32_t)N;
+    su.block_size = (int32_t)key_cache->shape[1];
+    su.num_virtual = (int32_t)V;
+    su.seqs_per_virtual = (int32_t)c.spg;
+
+    auto base_args = [&](const DecodePlan &p, uint8_t *w) {
+        DecodeArgs a;
+        a.q = q->data;
+        a.key_cache = key_cache->data;
+        a.value_cache = value_cache->data;
+        a.out = out->data;
+        a.ws_acc = reinterpret_cast<float *>(w);
+        a.ws_ml = a.ws_acc + p.slots * p.rows * p.D;
+        a.ws_seg = reinterpret_cast<int32_t *>(a.ws_ml + p.slots * p.rows * 2);
+        a.err_flag = opts->err_flag;
+        a.num_seqs = (int32_t)p.S;
+        a.num_heads = (int32_t)p.H;
+        a.num_kv_heads = (int32_t)p.Hkv;
+        a.max_nb = (int32_t)p.max_nb;
+        a.num_blocks = (int32_t)p.NB;
+        a.chunk_units = (int32_t)p.chunk_units;
+        a.num_waves = (int32_t)p.waves;
+        a.rows_per_slot = (int32_t)p.rows;
+        a.query_start_loc = nullptr;
+        a.max_query_len = 1;
+        a.num_tokens = (int32_t)p.T;
+        a.log2_group = __builtin_ctz((unsigned)p.G);
+        a.qk_scale_log2 = scale * kLog2e * ks;
+        a.v_scale = vs;
+        a.flags = kPartialOnly;
+        return a;
+    };
+    DecodeArgs pa_ = base_args(pp, ws + c.pre_off);
+    pa_.block_tables = su.p_tables;
+    pa_.seq_lens = su.p_lens;
+    pa_.query_start_loc = su.p_qsl;
+    pa_.max_query_len = (int32_t)c.spg;
+    pa_.flags = kPartialOnly | kNonCausal;
+    DecodeArgs sa = base_args(sp, ws + c.suf_off);
+    sa.block_tables = su.s_tables;
+    sa.seq_lens = su.s_lens;
+
+    CascadeMergeArgs ma;
+    ma.out = out->data;
+    ma.s_acc = sa.ws_acc;
+    ma.s_ml = sa.ws_ml;
+    ma.s_seg = sa.ws_seg;
+    ma.s_lens = su.s_lens;
+    ma.p_acc = pa_.ws_acc;
+    ma.p_ml = pa_.ws_ml;
+    ma.p_seg = pa_.ws_seg;
+    ma.num_seqs = (int32_t)S;
+    ma.num_heads = (int32_t)sp.H;
+    ma.num_kv_heads = (int32_t)sp.Hkv;
+    ma.seqs_per_virtual = (int32_t)c.spg;
+
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    hipEvent_t ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);
+    hipEvent_t ev1 = static_cast<hipEvent_t>(opts->kernel_events[1]);
+    hipError_t e = launch_cascade_setup(su, stream);
+    if (e != hipSuccess)
+        return PA_ERR_HIP;
+    if (ev0 && hipEventRecord(ev0, stream) != hipSuccess)
+        return PA_ERR_HIP;
+    if ((e = launch_decode_mfma_multi(pa_, pp.kv_type, (int)pp.D, (int)pp.bs, (int)pp.col_tiles,
+                                      stream)) != hipSuccess ||
+        (e = launch_decode_mfma(sa, sp.kv_type, (int)sp.D, (int)sp.bs, (int)sp.G, stream)) !=
+            hipSuccess)
+        return PA_ERR_HIP;
+    if (ev1 && hipEventRecord(ev1, stream) != hipSuccess)
+        return PA_ERR_HIP;
+    e = launch_cascade_merge(ma, sp.q_type, (int)sp.D, stream);
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 int pa_decode_multi(const pa_tensor *q, const pa_tensor *query_start_loc, int32_t max_query_len,

@@ -40,7 +40,15 @@ struct DecodeArgs {
     int32_t log2_group;          // G = 2^log2_group
     float qk_scale_log2;         // scale * log2(e) * k_scale (k_scale = 1 unless fp8)
     float v_scale;               // 1 unless fp8
+    int32_t flags;               // kPartialOnly | kNonCausal
 };
+
+// DecodeArgs.flags (matrix-core kernels).  kPartialOnly: every segment ends
+// as a partial (acc, m, l), also one a single chunk covers, so that a second
+// pass can combine it with another source.  kNonCausal (several query
+// tokens): every query row sees the whole sequence.
+constexpr int32_t kPartialOnly = 1;
+constexpr int32_t kNonCausal = 2;
 
 struct AppendArgs {
     const void *k;               // [T, Hkv, D]
@@ -95,6 +103,35 @@ struct StepPrepArgs {
     int32_t num_reqs, num_rows, max_blocks, max_len, max_tokens, block_size, num_blocks;
 };
 
+// Cascade decode for a batch whose sequences share their first N blocks.
+// Setup: builds, in the workspace, the prefix pass's virtual batch (V virtual
+// sequences of N blocks, each carrying the queries of SPG real sequences as
+// its "query tokens") and the suffix pass's batch (each sequence's blocks
+// from N on), and checks the shared-prefix contract.
+struct CascadeSetupArgs {
+    const int32_t *block_tables;  // [S, max_nb]
+    const int32_t *seq_lens;      // [S]
+    int32_t *p_tables;            // [V, N]
+    int32_t *p_lens;              // [V]
+    int32_t *p_qsl;               // [V + 1]
+    int32_t *s_tables;            // [S, max_nb - N]
+    int32_t *s_lens;              // [S]
+    uint32_t *err_flag;
+    int32_t num_seqs, max_nb, prefix_blocks, block_size, num_virtual, seqs_per_virtual;
+};
+
+// Combination of each row's suffix partials (rows_per_slot G) and prefix
+// partials (rows_per_slot G * SPG, row (s mod SPG) * G + h mod G of virtual
+// sequence s / SPG).
+struct CascadeMergeArgs {
+    void *out;                    // [S, H, D]
+    const float *s_acc, *s_ml;    // suffix partials
+    const int32_t *s_seg, *s_lens;
+    const float *p_acc, *p_ml;    // prefix partials
+    const int32_t *p_seg;
+    int32_t num_seqs, num_heads, num_kv_heads, seqs_per_virtual;
+};
+
 // Launchers (defined in the .hip translation units).  Each returns a
 // hipError_t from hipGetLastError() after the launch.
 hipError_t launch_kv_append(const AppendArgs &a, int in_type, int cache_type,
@@ -129,6 +166,10 @@ hipError_t decode_mfma_occupancy(int kv_type, int head_dim, int block_size, int 
 // 256-thread workgroups.
 hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int block_size,
                         hipStream_t stream);
+
+hipError_t launch_cascade_setup(const CascadeSetupArgs &a, hipStream_t stream);
+hipError_t launch_cascade_merge(const CascadeMergeArgs &a, int out_type, int head_dim,
+                                hipStream_t stream);
 
 // Step metadata from the state table; num_reqs <= kMaxPrepReqs.
 hipError_t launch_step_prep(const StepPrepArgs &a, hipStream_t stream);

@@ -36,7 +36,8 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(
         ["pa_kv_append", "pa_decode", "pa_decode_workspace_size", "pa_opts_init",
          "pa_status_string", "pa_version", "pa_zero_blocks", "pa_copy_blocks",
-         "pa_decode_multi", "pa_decode_multi_workspace_size", "pa_prepare_step"])
+         "pa_decode_multi", "pa_decode_multi_workspace_size", "pa_prepare_step",
+         "pa_decode_cascade", "pa_decode_cascade_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -284,3 +285,19 @@ def test_prepare_step_validation_errors():
     assert call(S=4096) == PA_ERR_UNSUPPORTED
     assert call(ids=FAKE + 2) == PA_ERR_ALIGN
     assert call(o=pa.PaStepInputs(FAKE, FAKE, FAKE + 4, FAKE, FAKE, FAKE, 64)) == PA_ERR_ALIGN
+
+
+def test_decode_cascade_validation_errors():
+    r = lambda x: None if x is None else ctypes.byref(x)
+
+    def call(a, N, o=None):
+        return lib().pa_decode_cascade(r(a["q"]), r(a["kc"]), r(a["vc"]), r(a["bt"]),
+                                       r(a["lens"]), N, 0.125, r(a["out"]), r(o), None)
+    a = decode_args(S=4, H=8, Hkv=2, D=128, max_nb=8, qd=BF16, kd=BF16)
+    assert call(a, -1) == PA_ERR_UNSUPPORTED
+    assert call(a, 8) == PA_ERR_UNSUPPORTED                        # N must leave a suffix
+    assert call(decode_args(S=4, max_nb=8), 2) == PA_ERR_UNSUPPORTED  # f32: matrix cores only
+    assert call(a, 2, opts(variant=1)) == PA_ERR_UNSUPPORTED
+    b = decode_args(S=4, H=8, Hkv=2, D=128, max_nb=8, qd=BF16, kd=BF16)
+    b["bt"] = desc([3, 8], I32)
+    assert call(b, 2) == PA_ERR_SHAPE

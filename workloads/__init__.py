@@ -114,6 +114,8 @@ class DecodeBatch:
     # slot_mapping, its last q_len positions in order.
     query_start_loc: Optional[torch.Tensor] = None   # int32 [S + 1]
     max_query_len: int = 1
+    # leading logical blocks every sequence shares (the same physical blocks)
+    shared_prefix_blocks: int = 0
 
     @property
     def num_query_tokens(self) -> int:
@@ -266,7 +268,8 @@ def make_batch(name: str = "tiny_f32", seed: Optional[int] = None, device="cpu",
         slot_mapping=torch.from_numpy(slots).to(device), k_scale=k_scale, v_scale=v_scale,
         partition_tokens=cfg.get("partition_tokens"), poisoned=poison,
         query_start_loc=None if qspec is None else torch.from_numpy(qsl).to(device),
-        max_query_len=1 if qspec is None else max(1, int(qlens.max())))
+        max_query_len=1 if qspec is None else max(1, int(qlens.max())),
+        shared_prefix_blocks=cfg["lens"][1] // bs if cfg["lens"][0] == "prefix" else 0)
 
 
 def _randn(shape, gen, device, out_dtype=torch.float32, chunk=1 << 26):
