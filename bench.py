@@ -34,11 +34,10 @@ KERNEL_SOURCES = {
 }
 KERNEL_SOURCES["blocks"] = ["paged_kv_cache_54_amd/csrc/blocks.hip",
                             "paged_kv_cache_54_amd/csrc/pa_device.h"]
-KERNEL_SOURCES["cascade"] = KERNEL_SOURCES["mfma"] + ["paged_kv_cache_54_amd/csrc/decode_mfma_multi.hip",
-                                                      "paged_kv_cache_54_amd/csrc/cascade.hip"]
+KERNEL_SOURCES["cascade"] = KERNEL_SOURCES["mfma"] + ["paged_kv_cache_54_amd/csrc/cascade.hip"]
 KERNEL_NAMES = {"valu": "decode_valu_kernel", "mfma": "decode_mfma_kernel",
                 "mfma_multi": "decode_mfma_multi_kernel",
-                "cascade": "decode_mfma_multi_kernel + decode_mfma_kernel"}
+                "cascade": "cascade_prefix_kernel + decode_mfma_kernel"}
 
 
 def parse():

@@ -26,11 +26,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
           "-fno-gpu-rdc", "-munsafe-fp-atomics"]
 
 
-# Per-source extra flags.  The matrix-core decode kernel rescales its MFMA
-# accumulators with vector instructions, so it keeps them in VGPRs rather than
+# Per-source extra flags.  The matrix-core decode kernels rescale their MFMA
+# accumulators with vector instructions, so they keep them in VGPRs rather than
 # copying them between AGPRs and VGPRs on every rescale.
 EXTRA = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "decode_mfma_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "decode_mfma_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "cascade.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

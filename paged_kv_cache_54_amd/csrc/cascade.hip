@@ -5,68 +5,321 @@
 // attention is split at the prefix boundary (log-sum-exp makes the split
 // exact):
 //
-//   prefix pass  all sequences' queries against the shared blocks, read once
-//                per group of SPG sequences: the matrix-core multi-query
-//                kernel over a virtual batch whose "query tokens" are the
-//                group's sequences (no causal bound), partials only;
-//   suffix pass  each sequence against its own blocks from the prefix on: the
-//                single-query kernel over shifted tables, partials only;
+//   prefix pass  every query row of a KV head against the shared blocks:
+//                a dense attention of R = S * G rows over N * bs tokens,
+//                cut into (KV head, token split, row block) workgroups whose
+//                four wavefronts share each K/V tile through LDS;
+//   suffix pass  each sequence against its own blocks from the prefix on:
+//                the single-query kernel over shifted tables, partials only;
 //   merge        per (sequence, head): log-sum-exp over both passes' parts.
 //
-// This file holds the setup kernel, which writes the two passes' tables,
-// lengths and query layout into the workspace and checks the contract, and
-// the two-source merge.
-#include "pa_device.h"
+// This file holds the prefix kernel (which also writes the suffix pass's
+// shifted tables and lengths and checks the contract) and the merge.
+#include "mfma_common.h"
 
 namespace pa {
 namespace {
 
+constexpr int kPrefixWaves = 4;     // wavefronts per prefix workgroup
+constexpr int kPrefixColTiles = 2;  // 16-row column tiles per wavefront
+constexpr int kPrefixDepth = 4;     // tiles in flight per workgroup
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void cascade_setup_kernel(CascadeSetupArgs a)
+// Suffix pass inputs and the contract check: table rows from block N on,
+// lengths less the prefix; every table starts with row 0's prefix and every
+// sequence covers it.  Workgroup wg of nwg.
+__device__ void suffix_inputs(const CascadePrefixArgs &a, int wg, int nwg)
 {
-    const int N = a.prefix_blocks, S = a.num_seqs, V = a.num_virtual;
+    const int N = a.prefix_blocks, S = a.num_seqs;
     const int sfx = a.max_nb - N;
-    const int64_t n_p = (int64_t)V * N, n_s = (int64_t)S * sfx;
-    const int64_t n_chk = (int64_t)S * N;
-    const int64_t total = n_p + n_s + n_chk + S + V + 1;
+    const int64_t n_s = (int64_t)S * sfx, n_chk = (int64_t)S * N;
+    const int64_t total = n_s + n_chk + S;
     const int cap = a.max_nb * a.block_size;
-    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * kThreads) {
+    for (int64_t e = (int64_t)wg * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)nwg * blockDim.x) {
         int64_t x = e;
-        if (x < n_p) {                       // prefix tables: row 0's first N blocks
-            a.p_tables[x] = a.block_tables[x % N];
-            continue;
-        }
-        x -= n_p;
-        if (x < n_s) {                       // suffix tables: blocks N .. max_nb-1
+        if (x < n_s) {
             const int64_t s = x / sfx, j = x % sfx;
             a.s_tables[x] = a.block_tables[s * a.max_nb + N + j];
             continue;
         }
         x -= n_s;
-        if (x < n_chk) {                     // contract: every table starts with the prefix
+        if (x < n_chk) {
             const int64_t s = x / N, j = x % N;
             if (a.block_tables[s * a.max_nb + j] != a.block_tables[j])
                 raise_flag(a.err_flag, PA_DEVERR_PREFIX);
             continue;
         }
         x -= n_chk;
-        if (x < S) {                         // suffix lengths; contract: prefix fully covered
-            const int L = min(a.seq_lens[x], cap);
-            if (L < N * a.block_size)
-                raise_flag(a.err_flag, PA_DEVERR_PREFIX);
-            a.s_lens[x] = max(0, L - N * a.block_size);
-            continue;
+        const int L = min(a.seq_lens[x], cap);
+        if (L < N * a.block_size)
+            raise_flag(a.err_flag, PA_DEVERR_PREFIX);
+        a.s_lens[x] = max(0, L - N * a.block_size);
+    }
+}
+
+// One K or V row chunk of a tile into its LDS tile as bf16 (e4m3 converted
+// exactly).
+template <class Geo, int ROWB>
+__device__ __forceinline__ void stage_chunk(uint8_t *tile, int row, int chunk, uint4 v)
+{
+    if constexpr (Geo::KT == KT_BF16) {
+        *reinterpret_cast<uint4 *>(tile + row * ROWB + chunk * 16) = v;
+    } else {
+        *reinterpret_cast<uint4 *>(tile + row * ROWB + chunk * 32) =
+            e4m3x8_to_bf16x8(make_uint2(v.x, v.y));
+        *reinterpret_cast<uint4 *>(tile + row * ROWB + chunk * 32 + 16) =
+            e4m3x8_to_bf16x8(make_uint2(v.z, v.w));
+    }
+}
+
+// Prefix pass.  Workgroup = four wavefronts over RB = 4 * 16 * NTW query
+// rows; wavefront w owns rows w * 16 * NTW .. of the block as NTW MFMA
+// column tiles.  The 2 * NLOAD load instructions of a tile (K rows, then V
+// rows) are dealt round-robin to the wavefronts; each tile is staged into
+// one of two LDS buffers and, after a barrier, read by all four.  DEPTH
+// tiles are in flight in registers.  Every prefix token is valid (the
+// contract), so no masking.
+template <int KT, int D, int BS, int NTW>
+__global__ __launch_bounds__(64 * kPrefixWaves) void cascade_prefix_kernel(CascadePrefixArgs a)
+{
+    using Geo = MfmaGeo<KT, D, BS>;
+    constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
+    constexpr int HALVES = Geo::HALVES, NLOAD = Geo::NLOAD;
+    constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
+    constexpr int NQ = 2 * NLOAD;                                   // load instructions per tile
+    constexpr int NPW = (NQ + kPrefixWaves - 1) / kPrefixWaves;      // ... per wavefront
+    constexpr int DEPTH = kPrefixDepth;
+    constexpr int RB = kPrefixWaves * 16 * NTW;
+
+    __shared__ __attribute__((aligned(16))) uint8_t kt_all[2][TILE * KROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t vt_all[2][TILE * VROWB];
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar selects
+    const int lane = threadIdx.x & 63;
+    const int g4 = lane >> 4, c16 = lane & 15;
+
+    // The workgroups past the items' 8 * items_per_xcd write the suffix
+    // pass's inputs.
+    const int item_wgs = 8 * a.items_per_xcd;
+    if ((int)blockIdx.x >= item_wgs) {
+        suffix_inputs(a, (int)blockIdx.x - item_wgs, (int)gridDim.x - item_wgs);
+        return;
+    }
+    // Workgroups are dispatched round-robin over the 8 XCDs; consecutive
+    // items -- the row blocks of one (KV head, split), which read the same
+    // tiles -- are given to workgroups of one XCD, so the tiles come from its
+    // L2 after the first read.
+    const int item = (int)(blockIdx.x & 7) * a.items_per_xcd + (int)(blockIdx.x >> 3);
+    if (item >= a.num_items)
+        return;
+    const int Hkv = a.num_kv_heads, H = a.num_heads, lg = a.log2_group;
+    const int rb = item % a.row_blocks;
+    const int pair = item / a.row_blocks;
+    const int split = pair % a.num_splits, kvh = pair / a.num_splits;
+    const int j0 = split * a.split_blocks;
+    const int nblk = min(a.prefix_blocks - j0, a.split_blocks);
+    const int ntiles = nblk * HALVES;
+
+    // loads: this wavefront's instructions u -> q = wave + 4u
+    const int slot_bytes = Hkv * D * Geo::EB;
+    const int64_t block_bytes = (int64_t)BS * slot_bytes;
+    const int l_row = lane / Geo::RCH, l_chunk = lane % Geo::RCH;
+    const int voff = l_row * slot_bytes + l_chunk * 16 + kvh * D * Geo::EB;
+    // block ids of the split (at most 64 blocks), checked once; a bad id
+    // reads zeros
+    int my_ids = lane < nblk ? a.block_tables[j0 + lane] : 0;
+    const bool bad = lane < nblk && (my_ids < 0 || my_ids >= a.num_blocks);
+    if (bad)
+        my_ids = -1;
+    if (__ballot(bad) && wave == 0 && lane == 0)
+        raise_flag(a.err_flag, PA_DEVERR_BLOCK_ID);
+    struct Part {
+        uint4 v[NPW];
+    };
+    // Every load is issued unconditionally (tiles past the split through a
+    // zero-size resource), so the compiler counts the loads in flight exactly
+    // and each stage waits for its own tile only.
+    auto block_id = [&](int t) {
+        const int id = __builtin_amdgcn_readlane(my_ids, min(t / HALVES, 63));
+        return __builtin_amdgcn_readfirstlane(t >= ntiles ? -1 : id);
+    };
+    auto load = [&](int t, Part &p) {
+        const int id = block_id(t);
+        const int soff = (t % HALVES) * TILE * slot_bytes;
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            const int q = wave + kPrefixWaves * u;
+            const bool is_v = q >= NLOAD;
+            const int i = is_v ? q - NLOAD : q;
+            const __amdgpu_buffer_rsrc_t r = block_rsrc(is_v ? a.value_cache : a.key_cache,
+                                                        block_bytes, q < NQ ? id : -1);
+            p.v[u] = buf_load16(r, voff, soff + i * Geo::LROWS * slot_bytes);
         }
-        x -= S;
-        if (x < V) {                         // every virtual sequence is the whole prefix
-            a.p_lens[x] = N * a.block_size;
-            continue;
+    };
+    auto stage = [&](const Part &p, int buf) {
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+            const int q = wave + kPrefixWaves * u;
+            if (q < NLOAD)
+                stage_chunk<Geo, KROWB>(kt_all[buf], q * Geo::LROWS + l_row, l_chunk, p.v[u]);
+            else if (q < NQ)
+                stage_chunk<Geo, VROWB>(vt_all[buf], (q - NLOAD) * Geo::LROWS + l_row, l_chunk,
+                                        p.v[u]);
         }
-        x -= V;
-        for (int v = 0; v <= V; ++v)         // virtual sequence v carries sequences v*SPG ..
-            a.p_qsl[v] = min(v * a.seqs_per_virtual, S);
+    };
+
+    // query operands of this wavefront's rows (rows past R are zeros)
+    const int R = a.rows;
+    const int row0 = rb * RB + wave * 16 * NTW;
+    bf16x8 qop[NTW][NC];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int r = row0 + 16 * nt + c16;
+        const bool valid = r < R;
+        const int rr = valid ? r : 0;
+        const int s = rr >> lg, g = rr & ((1 << lg) - 1);
+        const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
+                               ((int64_t)s * H + kvh * (1 << lg) + g) * D + 8 * g4;
+#pragma unroll
+        for (int k = 0; k < NC; ++k) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(qrow + 32 * k);
+            qop[nt][k] = as_bf16x8(valid ? v : make_uint4(0, 0, 0, 0));
+        }
+    }
+
+    // Tile loads after the query loads (the first tile's wait covers the
+    // queries), in tile order: the loop waits for tile t with every later
+    // tile's loads still in flight.
+    Part pf[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        load(d, pf[d]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    f32x4 acc[NTW][ND];
+    float m[NTW], l[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            acc[nt][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[nt] = -INFINITY;
+        l[nt] = 0.f;
+    }
+
+    // One tile from LDS: every K and Vt operand read is issued first, so the
+    // reads' latencies overlap each other and the QK products and softmax.
+    auto process = [&](int buf) {
+        const uint8_t *kt = kt_all[buf];
+        const uint8_t *vt = vt_all[buf];
+        bf16x8 kop[MT][NC];
+        s16x4 vop[MT][ND];
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const uint8_t *krow = kt + (16 * h + c16) * KROWB + 16 * g4;
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+                kop[h][k] = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + 64 * k));
+        }
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const int row = 16 * h + 4 * g4 + (c16 >> 2);
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                vop[h][d] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)((__attribute__((address_space(3))) uint8_t *)vt + row * VROWB +
+                                  32 * d + 8 * (c16 & 3)));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 sc[MT][NTW];
+#pragma unroll
+        for (int h = 0; h < MT; ++h)
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt) {
+                sc[h][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k = 0; k < NC; ++k)
+                    sc[h][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[h][k], qop[nt][k],
+                                                                      sc[h][nt], 0, 0, 0);
+            }
+        bf16x4 pop[MT][NTW];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            float bm = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < MT; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sc[h][nt][i] *= a.qk_scale_log2;
+                    bm = fmaxf(bm, sc[h][nt][i]);
+                }
+            const float mn = fmaxf(m[nt], rows_max(bm));
+            if (__ballot(mn > m[nt])) {
+                const float alpha = (mn > m[nt]) ? __builtin_amdgcn_exp2f(m[nt] - mn) : 1.f;
+                l[nt] *= alpha;
+#pragma unroll
+                for (int d = 0; d < ND; ++d)
+                    acc[nt][d] *= alpha;
+            }
+            m[nt] = mn;
+#pragma unroll
+            for (int h = 0; h < MT; ++h) {
+                float p[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    p[i] = __builtin_amdgcn_exp2f(sc[h][nt][i] - mn);
+                    l[nt] += p[i];
+                }
+                pop[h][nt] = __builtin_bit_cast(
+                    bf16x4, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < MT; ++h)
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+#pragma unroll
+                for (int nt = 0; nt < NTW; ++nt)
+                    acc[nt][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        as_bf16x4(vop[h][d]), pop[h][nt], acc[nt][d], 0, 0, 0);
+    };
+
+    // Tile t: stage from registers into buffer t & 1, barrier, refill the
+    // registers with tile t + DEPTH, compute from LDS.  Buffer t & 1 was last
+    // read by tile t - 2, which every wavefront finished before the barrier
+    // of tile t - 1.
+    for (int t0 = 0; t0 < ntiles; t0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int t = t0 + d;
+            const bool live = t < ntiles;
+            if (live)
+                stage(pf[d], t & 1);
+            __syncthreads();
+            load(t + DEPTH, pf[d]);
+            if (live)
+                process(t & 1);
+        }
+    }
+
+    // partials of the valid rows
+    const int64_t pbase = ((int64_t)split * Hkv + kvh) * R;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const float lt = rows_sum(l[nt]);
+        const int r = row0 + 16 * nt + c16;
+        if (r >= R)
+            continue;
+        float *o = a.p_acc + (pbase + r) * D + 4 * g4;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            *reinterpret_cast<float4 *>(o + 16 * d) =
+                make_float4(acc[nt][d][0] * a.v_scale, acc[nt][d][1] * a.v_scale,
+                            acc[nt][d][2] * a.v_scale, acc[nt][d][3] * a.v_scale);
+        if (g4 == 0)
+            *reinterpret_cast<float2 *>(a.p_ml + (pbase + r) * 2) = make_float2(m[nt], lt);
     }
 }
 
@@ -101,11 +354,11 @@ __device__ __forceinline__ void lse_fold(Lse &s, const Lse &t)
     s.o.w = s.o.w * a + t.o.w * b;
 }
 
-// Fold parts [first, last] of one partial source (rows_per_slot rps, row
+// Fold parts [first, last] of one partial source (part stride rps rows, row
 // prow) into st; the lanes' groups take parts p0, p0 + step, ...
 template <int D>
 __device__ __forceinline__ void add_parts(Lse &st, const float *acc_ws, const float *ml_ws,
-                                          int first, int last, int rps, int prow, int col,
+                                          int first, int last, int64_t rps, int64_t prow, int col,
                                           int p0, int step)
 {
     const float2 *ml = reinterpret_cast<const float2 *>(ml_ws) + (int64_t)first * rps + prow;
@@ -145,11 +398,10 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(CascadeMergeArg
         add_parts<D>(st, a.s_acc, a.s_ml, a.s_seg[2 * g], a.s_seg[2 * g + 1], G, h % G, col,
                      sub, PPW);
     }
-    {                                            // the shared prefix
-        const int spg = a.seqs_per_virtual, v = s / spg;
-        const int g = v * Hkv + kvh;
-        add_parts<D>(st, a.p_acc, a.p_ml, a.p_seg[2 * g], a.p_seg[2 * g + 1], G * spg,
-                     (s % spg) * G + h % G, col, sub, PPW);
+    {                                            // the shared prefix: one part per split
+        const int64_t R = (int64_t)a.num_seqs * G;
+        add_parts<D>(st, a.p_acc, a.p_ml, 0, a.num_splits - 1, Hkv * R,
+                     kvh * R + (int64_t)s * G + h % G, col, sub, PPW);
     }
 #pragma unroll
     for (int off = LPP; off < 64; off <<= 1) {
@@ -177,15 +429,36 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(CascadeMergeArg
     }
 }
 
+typedef void (*PrefixKernel)(CascadePrefixArgs);
+
+template <int KT>
+PrefixKernel pick_prefix(int d, int bs)
+{
+    if (d == 64 && bs == 16) return cascade_prefix_kernel<KT, 64, 16, kPrefixColTiles>;
+    if (d == 64 && bs == 32) return cascade_prefix_kernel<KT, 64, 32, kPrefixColTiles>;
+    if (d == 128 && bs == 16) return cascade_prefix_kernel<KT, 128, 16, kPrefixColTiles>;
+    if (d == 128 && bs == 32) return cascade_prefix_kernel<KT, 128, 32, kPrefixColTiles>;
+    return nullptr;
+}
+
 }  // namespace
 
-hipError_t launch_cascade_setup(const CascadeSetupArgs &a, hipStream_t stream)
+int cascade_prefix_rows() { return kPrefixWaves * 16 * kPrefixColTiles; }
+
+hipError_t launch_cascade_prefix(const CascadePrefixArgs &a, int kv_type, int head_dim,
+                                 int block_size, hipStream_t stream)
 {
-    const int64_t total = (int64_t)a.num_virtual * a.prefix_blocks +
-                          (int64_t)a.num_seqs * a.max_nb + a.num_seqs + a.num_virtual + 1;
-    int64_t wgs = (total + 4 * kThreads - 1) / (4 * kThreads);
-    wgs = wgs < 1 ? 1 : (wgs > 1024 ? 1024 : wgs);
-    hipLaunchKernelGGL(cascade_setup_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+    const PrefixKernel k = kv_type == KT_BF16   ? pick_prefix<KT_BF16>(head_dim, block_size)
+                           : kv_type == KT_E4M3 ? pick_prefix<KT_E4M3>(head_dim, block_size)
+                                                : nullptr;
+    if (!k)
+        return hipErrorInvalidValue;
+    // item workgroups, then those for the suffix inputs (about 1k elements each)
+    const int64_t side = (int64_t)a.num_seqs * (a.max_nb + 1);
+    int64_t side_wgs = (side + 4 * 64 * kPrefixWaves - 1) / (4 * 64 * kPrefixWaves);
+    side_wgs = side_wgs < 1 ? 1 : (side_wgs > 256 ? 256 : side_wgs);
+    hipLaunchKernelGGL(k, dim3((unsigned)(8 * (int64_t)a.items_per_xcd + side_wgs)),
+                       dim3(64 * kPrefixWaves), 0, stream, a);
     return hipGetLastError();
 }
 

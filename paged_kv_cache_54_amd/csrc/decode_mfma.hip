@@ -100,8 +100,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_mfma_kernel(Decode
     };
 
     auto finish_segment = [&](const Cursor &c, bool ends) {
-        float lt = l + __shfl_xor(l, 16);      // sum the four 16-lane groups
-        lt += __shfl_xor(lt, 32);
+        const float lt = rows_sum(l);          // sum the four 16-lane groups
         const int g = c.s * Hkv + c.kvh;
         const int slot = w + g;
         record_segment(a, g, slot, seg_starts, ends);
@@ -164,9 +163,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_mfma_kernel(Decode
                 sc[h][i] = v;
                 bm = fmaxf(bm, v);
             }
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m, bm);
+        const float mn = fmaxf(m, rows_max(bm));
         if (__ballot(mn > m)) {
             const float alpha = (mn > m) ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
             l *= alpha;

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
             const int col = 16 * nt + c16;
             const int i = col >> lg, g = col & (G - 1);
             const bool valid = i < ql;
-            lim[nt] = !valid ? 0 : (a.flags & kNonCausal) ? c.L : c.L - ql + i + 1;
+            lim[nt] = valid ? c.L - ql + i + 1 : 0;
             orow[nt] = valid ? (int64_t)(qs + i) * H + c.kvh * G + g : -1;
             const uint16_t *qrow =
                 static_cast<const uint16_t *>(a.q) + (valid ? orow[nt] : 0) * D + 8 * g4;
@@ -92,8 +92,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
         record_segment(a, g, slot, seg_starts, ends);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            float lt = l[nt] + __shfl_xor(l[nt], 16);    // sum the four 16-lane groups
-            lt += __shfl_xor(lt, 32);
+            const float lt = rows_sum(l[nt]);            // sum the four 16-lane groups
             if (orow[nt] < 0)
                 continue;
             if (seg_starts && ends && !(a.flags & kPartialOnly)) {
@@ -156,9 +155,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
                     sc[h][nt][i] = v;
                     bm = fmaxf(bm, v);
                 }
-            bm = fmaxf(bm, __shfl_xor(bm, 16));
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
-            const float mn = fmaxf(m[nt], bm);
+            const float mn = fmaxf(m[nt], rows_max(bm));
             if (__ballot(mn > m[nt])) {
                 const float alpha = (mn > m[nt]) ? __builtin_amdgcn_exp2f(m[nt] - mn) : 1.f;
                 l[nt] *= alpha;

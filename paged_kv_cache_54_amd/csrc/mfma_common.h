@@ -51,6 +51,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// Max and sum over the four 16-lane rows (lanes c, c + 16, c + 32, c + 48):
+// gfx950's row-swap permutes exchange rows 0<->1, 2<->3 (16-lane swap) and
+// the two halves (32-lane swap) on the vector ALU, with no LDS round trip.
+// Called with the same register twice, each swap returns the lane's own row
+// in one result and its partner row in the other, so every lane ends with
+// the same value.
+__device__ __forceinline__ float rows_max(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Tile geometry of one KV head's rows for a cache of element type KT.
 template <int KT_, int D_, int BS_>
 struct MfmaGeo {

@@ -391,12 +391,12 @@ pa_tensor reshaped(const pa_tensor *t, std::initializer_list<int64_t> shape)
     return r;
 }
 
-// The cascade's layout: setup arrays, then the prefix pass's and the suffix
-// pass's workspaces (each 256-byte aligned).
+// The cascade's plan: the prefix pass's work items and partials, the suffix
+// pass's tables, lengths and decode plan; workspace regions 256-byte aligned.
 struct CascadePlan {
-    DecodePlan pre, suf;
-    int64_t S, N, V, spg;
-    size_t setup_bytes, pre_off, suf_off, total;
+    DecodePlan suf;
+    int64_t S, N, G, R, row_blocks, P, split_blocks, items, per_xcd;
+    size_t tables_off, lens_off, acc_off, ml_off, suf_off, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -416,30 +416,46 @@ int plan_cascade(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt, i
     const int64_t G = q->shape[1] / kc->shape[2];
     if (!supported_group(G))
         return PA_ERR_UNSUPPORTED;
-    // sequences per virtual prefix sequence: at most 64 (sequence, head) columns
-    // and at most 16 query rows per virtual sequence
-    const int64_t spg = (64 / G) < 16 ? 64 / G : 16;
-    const int64_t V = (S + spg - 1) / spg;
     pa_opts o;
     pa_opts_init(&o);
     if (opts)
         o = *opts;
     o.variant = PA_VARIANT_MFMA;
-    pa_opts po = o;
-    po.partition_tokens = 0;                   // the prefix pass: balanced split
-    const pa_tensor bt_pre = reshaped(bt, {V > 0 ? V : 1, N});
     const pa_tensor bt_suf = reshaped(bt, {S, max_nb - N});
     int rc;
-    if ((rc = plan_decode(q, kc, &bt_pre, &po, spg, &c->pre)) ||
-        (rc = plan_decode(q, kc, &bt_suf, &o, 0, &c->suf)))
+    if ((rc = plan_decode(q, kc, &bt_suf, &o, 0, &c->suf)))
         return rc;
+    const int64_t Hkv = c->suf.Hkv, D = c->suf.D;
     c->S = S;
     c->N = N;
-    c->V = V;
-    c->spg = spg;
-    c->setup_bytes = align256(sizeof(int32_t) * (size_t)(V * N + V + V + 1 + S * (max_nb - N) + S));
-    c->pre_off = c->setup_bytes;
-    c->suf_off = c->pre_off + align256(c->pre.ws_bytes);
+    c->G = G;
+    c->R = S * G;
+    const int64_t rb = cascade_prefix_rows();
+    c->row_blocks = (c->R + rb - 1) / rb;
+    // Token splits of the prefix: about one workgroup per compute unit, at
+    // most 64 blocks per split (a wavefront holds a split's block ids in one
+    // register), no empty split.
+    int cus = 1;
+    if (S > 0 && (rc = device_cu_count(&cus)))
+        return rc;
+    const int64_t pairs = Hkv * (c->row_blocks > 0 ? c->row_blocks : 1);
+    int64_t P = (cus + pairs - 1) / pairs;
+    if (P < (N + 63) / 64)
+        P = (N + 63) / 64;
+    if (P > N)
+        P = N;
+    c->split_blocks = (N + P - 1) / P;
+    c->P = (N + c->split_blocks - 1) / c->split_blocks;
+    c->items = pairs * c->P;
+    c->per_xcd = (c->items + 7) / 8;
+    if (c->R > INT32_MAX / 2 || c->items > INT32_MAX / 2 || S * (max_nb - N) > INT32_MAX)
+        return PA_ERR_UNSUPPORTED;
+    const size_t prow = (size_t)(c->P * Hkv * c->R);
+    c->tables_off = 0;
+    c->lens_off = align256(sizeof(int32_t) * (size_t)(S * (max_nb - N)));
+    c->acc_off = c->lens_off + align256(sizeof(int32_t) * (size_t)S);
+    c->ml_off = c->acc_off + align256(sizeof(float) * prow * (size_t)D);
+    c->suf_off = c->ml_off + align256(sizeof(float) * prow * 2);
     c->total = S > 0 ? c->suf_off + align256(c->suf.ws_bytes) : 0;
     return PA_OK;
 }
@@ -692,87 +708,86 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
         return PA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(opts->workspace) % 16)
         return PA_ERR_ALIGN;
-    const int64_t S = c.S, N = c.N, V = c.V, max_nb = block_tables->shape[1];
-    const DecodePlan &pp = c.pre, &sp = c.suf;
+    const DecodePlan &sp = c.suf;
     uint8_t *ws = static_cast<uint8_t *>(opts->workspace);
 
-    CascadeSetupArgs su;
-    su.block_tables = static_cast<const int32_t *>(block_tables->data);
-    su.seq_lens = static_cast<const int32_t *>(seq_lens->data);
-    su.p_tables = reinterpret_cast<int32_t *>(ws);
-    su.p_lens = su.p_tables + V * N;
-    su.p_qsl = su.p_lens + V;
-    su.s_tables = su.p_qsl + V + 1;
-    su.s_lens = su.s_tables + S * (max_nb - N);
-    su.err_flag = opts->err_flag;
-    su.num_seqs = (int32_t)S;
-    su.max_nb = (int32_t)max_nb;
-    su.prefix_blocks = (int32_t)N;
-    su.block_size = (int32_t)key_cache->shape[1];
-    su.num_virtual = (int32_t)V;
-    su.seqs_per_virtual = (int32_t)c.spg;
+    CascadePrefixArgs pr;
+    pr.q = q->data;
+    pr.key_cache = key_cache->data;
+    pr.value_cache = value_cache->data;
+    pr.block_tables = static_cast<const int32_t *>(block_tables->data);
+    pr.seq_lens = static_cast<const int32_t *>(seq_lens->data);
+    pr.p_acc = reinterpret_cast<float *>(ws + c.acc_off);
+    pr.p_ml = reinterpret_cast<float *>(ws + c.ml_off);
+    pr.s_tables = reinterpret_cast<int32_t *>(ws + c.tables_off);
+    pr.s_lens = reinterpret_cast<int32_t *>(ws + c.lens_off);
+    pr.err_flag = opts->err_flag;
+    pr.num_seqs = (int32_t)c.S;
+    pr.num_heads = (int32_t)sp.H;
+    pr.num_kv_heads = (int32_t)sp.Hkv;
+    pr.max_nb = (int32_t)block_tables->shape[1];
+    pr.num_blocks = (int32_t)sp.NB;
+    pr.block_size = (int32_t)sp.bs;
+    pr.prefix_blocks = (int32_t)c.N;
+    pr.num_splits = (int32_t)c.P;
+    pr.split_blocks = (int32_t)c.split_blocks;
+    pr.rows = (int32_t)c.R;
+    pr.row_blocks = (int32_t)c.row_blocks;
+    pr.num_items = (int32_t)c.items;
+    pr.items_per_xcd = (int32_t)c.per_xcd;
+    pr.log2_group = __builtin_ctz((unsigned)c.G);
+    pr.qk_scale_log2 = scale * kLog2e * ks;
+    pr.v_scale = vs;
 
-    auto base_args = [&](const DecodePlan &p, uint8_t *w) {
-        DecodeArgs a;
-        a.q = q->data;
-        a.key_cache = key_cache->data;
-        a.value_cache = value_cache->data;
-        a.out = out->data;
-        a.ws_acc = reinterpret_cast<float *>(w);
-        a.ws_ml = a.ws_acc + p.slots * p.rows * p.D;
-        a.ws_seg = reinterpret_cast<int32_t *>(a.ws_ml + p.slots * p.rows * 2);
-        a.err_flag = opts->err_flag;
-        a.num_seqs = (int32_t)p.S;
-        a.num_heads = (int32_t)p.H;
-        a.num_kv_heads = (int32_t)p.Hkv;
-        a.max_nb = (int32_t)p.max_nb;
-        a.num_blocks = (int32_t)p.NB;
-        a.chunk_units = (int32_t)p.chunk_units;
-        a.num_waves = (int32_t)p.waves;
-        a.rows_per_slot = (int32_t)p.rows;
-        a.query_start_loc = nullptr;
-        a.max_query_len = 1;
-        a.num_tokens = (int32_t)p.T;
-        a.log2_group = __builtin_ctz((unsigned)p.G);
-        a.qk_scale_log2 = scale * kLog2e * ks;
-        a.v_scale = vs;
-        a.flags = kPartialOnly;
-        return a;
-    };
-    DecodeArgs pa_ = base_args(pp, ws + c.pre_off);
-    pa_.block_tables = su.p_tables;
-    pa_.seq_lens = su.p_lens;
-    pa_.query_start_loc = su.p_qsl;
-    pa_.max_query_len = (int32_t)c.spg;
-    pa_.flags = kPartialOnly | kNonCausal;
-    DecodeArgs sa = base_args(sp, ws + c.suf_off);
-    sa.block_tables = su.s_tables;
-    sa.seq_lens = su.s_lens;
+    // suffix pass: the single-query kernel over the shifted tables, partials only
+    DecodeArgs sa;
+    sa.q = q->data;
+    sa.key_cache = key_cache->data;
+    sa.value_cache = value_cache->data;
+    sa.block_tables = pr.s_tables;
+    sa.seq_lens = pr.s_lens;
+    sa.out = out->data;
+    sa.ws_acc = reinterpret_cast<float *>(ws + c.suf_off);
+    sa.ws_ml = sa.ws_acc + sp.slots * sp.rows * sp.D;
+    sa.ws_seg = reinterpret_cast<int32_t *>(sa.ws_ml + sp.slots * sp.rows * 2);
+    sa.err_flag = opts->err_flag;
+    sa.num_seqs = (int32_t)sp.S;
+    sa.num_heads = (int32_t)sp.H;
+    sa.num_kv_heads = (int32_t)sp.Hkv;
+    sa.max_nb = (int32_t)sp.max_nb;
+    sa.num_blocks = (int32_t)sp.NB;
+    sa.chunk_units = (int32_t)sp.chunk_units;
+    sa.num_waves = (int32_t)sp.waves;
+    sa.rows_per_slot = (int32_t)sp.rows;
+    sa.query_start_loc = nullptr;
+    sa.max_query_len = 1;
+    sa.num_tokens = (int32_t)sp.T;
+    sa.log2_group = __builtin_ctz((unsigned)sp.G);
+    sa.qk_scale_log2 = scale * kLog2e * ks;
+    sa.v_scale = vs;
+    sa.flags = kPartialOnly;
 
     CascadeMergeArgs ma;
     ma.out = out->data;
     ma.s_acc = sa.ws_acc;
     ma.s_ml = sa.ws_ml;
     ma.s_seg = sa.ws_seg;
-    ma.s_lens = su.s_lens;
-    ma.p_acc = pa_.ws_acc;
-    ma.p_ml = pa_.ws_ml;
-    ma.p_seg = pa_.ws_seg;
-    ma.num_seqs = (int32_t)S;
+    ma.s_lens = pr.s_lens;
+    ma.p_acc = pr.p_acc;
+    ma.p_ml = pr.p_ml;
+    ma.num_seqs = (int32_t)c.S;
     ma.num_heads = (int32_t)sp.H;
     ma.num_kv_heads = (int32_t)sp.Hkv;
-    ma.seqs_per_virtual = (int32_t)c.spg;
+    ma.num_splits = (int32_t)c.P;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     hipEvent_t ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);
     hipEvent_t ev1 = static_cast<hipEvent_t>(opts->kernel_events[1]);
-    hipError_t e = launch_cascade_setup(su, stream);
-    if (e != hipSuccess)
-        return PA_ERR_HIP;
     if (ev0 && hipEventRecord(ev0, stream) != hipSuccess)
         return PA_ERR_HIP;
-    if ((e = launch_decode_mfma_multi(pa_, pp.kv_type, (int)pp.D, (int)pp.bs, (int)pp.col_tiles,
-                                      stream)) != hipSuccess ||
+    hipError_t e;
+    if ((e = launch_cascade_prefix(pr, sp.kv_type, (int)sp.D, (int)sp.bs, stream)) !=
+            hipSuccess ||
         (e = launch_decode_mfma(sa, sp.kv_type, (int)sp.D, (int)sp.bs, (int)sp.G, stream)) !=
             hipSuccess)
         return PA_ERR_HIP;

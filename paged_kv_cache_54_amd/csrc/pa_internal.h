@@ -40,15 +40,13 @@ struct DecodeArgs {
     int32_t log2_group;          // G = 2^log2_group
     float qk_scale_log2;         // scale * log2(e) * k_scale (k_scale = 1 unless fp8)
     float v_scale;               // 1 unless fp8
-    int32_t flags;               // kPartialOnly | kNonCausal
+    int32_t flags;               // kPartialOnly
 };
 
 // DecodeArgs.flags (matrix-core kernels).  kPartialOnly: every segment ends
 // as a partial (acc, m, l), also one a single chunk covers, so that a second
-// pass can combine it with another source.  kNonCausal (several query
-// tokens): every query row sees the whole sequence.
+// pass can combine it with another source.
 constexpr int32_t kPartialOnly = 1;
-constexpr int32_t kNonCausal = 2;
 
 struct AppendArgs {
     const void *k;               // [T, Hkv, D]
@@ -104,32 +102,39 @@ struct StepPrepArgs {
 };
 
 // Cascade decode for a batch whose sequences share their first N blocks.
-// Setup: builds, in the workspace, the prefix pass's virtual batch (V virtual
-// sequences of N blocks, each carrying the queries of SPG real sequences as
-// its "query tokens") and the suffix pass's batch (each sequence's blocks
-// from N on), and checks the shared-prefix contract.
-struct CascadeSetupArgs {
+//
+// Prefix pass: the query rows of KV head kvh are the (sequence, head of the
+// group) pairs, row r = s * G + g, R = S * G of them.  Work item
+// (kvh, split p, row block) attends the row block's rows to blocks
+// [p * bps, min(N, (p + 1) * bps)) of the shared prefix (row 0 of the block
+// table) and writes, per row, the partial (m, l, acc) to
+// p_acc/p_ml[(p * Hkv + kvh) * R + r].  The same launch writes the suffix
+// pass's batch (each sequence's table from block N on, its length less the
+// prefix) and checks the shared-prefix contract.
+struct CascadePrefixArgs {
+    const void *q;                // [S, H, D] bf16
+    const void *key_cache, *value_cache;
     const int32_t *block_tables;  // [S, max_nb]
     const int32_t *seq_lens;      // [S]
-    int32_t *p_tables;            // [V, N]
-    int32_t *p_lens;              // [V]
-    int32_t *p_qsl;               // [V + 1]
+    float *p_acc, *p_ml;          // [P, Hkv, R, D], [P, Hkv, R, 2]
     int32_t *s_tables;            // [S, max_nb - N]
     int32_t *s_lens;              // [S]
     uint32_t *err_flag;
-    int32_t num_seqs, max_nb, prefix_blocks, block_size, num_virtual, seqs_per_virtual;
+    int32_t num_seqs, num_heads, num_kv_heads, max_nb, num_blocks, block_size;
+    int32_t prefix_blocks, num_splits, split_blocks;   // N, P, bps
+    int32_t rows, row_blocks;                          // R, row blocks per KV head
+    int32_t num_items, items_per_xcd, log2_group;
+    float qk_scale_log2, v_scale;
 };
 
-// Combination of each row's suffix partials (rows_per_slot G) and prefix
-// partials (rows_per_slot G * SPG, row (s mod SPG) * G + h mod G of virtual
-// sequence s / SPG).
+// Combination of each row's suffix partials (rows_per_slot G) and its P
+// prefix partials (layout above).
 struct CascadeMergeArgs {
     void *out;                    // [S, H, D]
     const float *s_acc, *s_ml;    // suffix partials
     const int32_t *s_seg, *s_lens;
     const float *p_acc, *p_ml;    // prefix partials
-    const int32_t *p_seg;
-    int32_t num_seqs, num_heads, num_kv_heads, seqs_per_virtual;
+    int32_t num_seqs, num_heads, num_kv_heads, num_splits;
 };
 
 // Launchers (defined in the .hip translation units).  Each returns a
@@ -167,7 +172,10 @@ hipError_t decode_mfma_occupancy(int kv_type, int head_dim, int block_size, int 
 hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int block_size,
                         hipStream_t stream);
 
-hipError_t launch_cascade_setup(const CascadeSetupArgs &a, hipStream_t stream);
+hipError_t launch_cascade_prefix(const CascadePrefixArgs &a, int kv_type, int head_dim,
+                                 int block_size, hipStream_t stream);
+// Rows of one prefix-pass workgroup.
+int cascade_prefix_rows();
 hipError_t launch_cascade_merge(const CascadeMergeArgs &a, int out_type, int head_dim,
                                 hipStream_t stream);
 

@@ -1,9 +1,10 @@
 """GPU parity of pa_decode_cascade (shared prefix read once per group of
 sequences, then each sequence's own blocks, joined by log-sum-exp) against
 the oracle, and against pa_decode on the same caches: bf16 and e4m3 caches,
-group sizes 1 to 8 (1 to 4 column tiles in the prefix pass), head_dim 64 and
-128, block sizes 16 and 32, sequences ending exactly at the prefix, batches
-that do not fill the last sequence group, work splits, NaN in unread slots,
+group sizes 1 to 8, head_dim 64 and 128, block sizes 16 and 32, sequences
+ending exactly at the prefix, batches whose query rows do not fill the last
+row block of the prefix pass, prefixes split over several token ranges, work
+splits, NaN in unread slots,
 the full-size shared-prefix batch on sampled rows, and a broken contract
 flagged."""
 import numpy as np
@@ -71,6 +72,29 @@ def test_cascade_full_size_sampled_rows():
     ref, _, _, _ = oracle_rows(b, rows)
     got = out.view(-1, b.head_dim)[torch.from_numpy(rows).to(DEV)]
     check_close(got, ref, "bf16", "full-size cascade rows")
+
+
+def test_cascade_long_prefix_many_rows():
+    """512 sequences x 64 heads (G 8): more (KV head, row block) pairs than
+    compute units, and a 68-block prefix: the prefix pass cuts it into
+    token ranges of at most 64 blocks.  Sampled rows against the oracle,
+    every row against plain decode."""
+    b = workloads.make_batch("shared_prefix_bf16", device=DEV, num_seqs=512, num_heads=64,
+                             num_kv_heads=8, lens=("prefix", 68 * 16, 1, 40),
+                             max_len=68 * 16 + 48, seed=83)
+    kc, vc = gpu_caches(b)
+    pa.kv_append(b.k_new, b.v_new, b.slot_mapping, kc, vc)
+    print("CASE cascade long prefix, 512 x 64 rows", flush=True)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = pa.decode_cascade(b.q, kc, vc, b.block_tables, b.seq_lens, 68, b.scale, err_flag=flag)
+    plain = pa.decode(b.q, kc, vc, b.block_tables, b.seq_lens, b.scale)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    rows = sample_rows(b, n=10)
+    ref, _, _, _ = oracle_rows(b, rows)
+    got = out.view(-1, b.head_dim)[torch.from_numpy(rows).to(DEV)]
+    check_close(got, ref, "bf16", "long-prefix cascade rows")
+    check_close(out, plain.double().cpu().numpy(), "bf16", "long-prefix cascade vs decode")
 
 
 def test_broken_prefix_contract_is_flagged():
