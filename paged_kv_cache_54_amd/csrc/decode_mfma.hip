@@ -50,13 +50,9 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_mfma_kernel(Decode
     constexpr int HALVES = Geo::HALVES;
     constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
     static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group must divide 16");
-#ifdef PA_EXP_PINGPONG_ALL
-    constexpr bool PINGPONG = true;
-#elif defined(PA_EXP_SINGLE_ALL)
-    constexpr bool PINGPONG = false;
-#else
+    // bf16: two register tiles in flight.  e4m3 (32-token tiles) keeps one,
+    // which holds its register use at two wavefronts per SIMD.
     constexpr bool PINGPONG = KT == KT_BF16;
-#endif
 
     __shared__ __attribute__((aligned(16))) uint8_t kt_all[kWavesPerGroup][TILE * KROWB];
     __shared__ __attribute__((aligned(16))) uint8_t vt_all[kWavesPerGroup][TILE * VROWB];
