@@ -255,21 +255,22 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void cascade_prefix_kernel(Casca
                     sc[h][nt][i] *= a.qk_scale_log2;
                     bm = fmaxf(bm, sc[h][nt][i]);
                 }
-            const float mn = fmaxf(m[nt], rows_max(bm));
-            if (__ballot(mn > m[nt])) {
+            const float tm = rows_max(bm);
+            if (__ballot(tm > m[nt] + kRebase)) {
+                const float mn = fmaxf(m[nt], tm);
                 const float alpha = (mn > m[nt]) ? __builtin_amdgcn_exp2f(m[nt] - mn) : 1.f;
                 l[nt] *= alpha;
 #pragma unroll
                 for (int d = 0; d < ND; ++d)
                     acc[nt][d] *= alpha;
+                m[nt] = mn;
             }
-            m[nt] = mn;
 #pragma unroll
             for (int h = 0; h < MT; ++h) {
                 float p[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = __builtin_amdgcn_exp2f(sc[h][nt][i] - mn);
+                    p[i] = __builtin_amdgcn_exp2f(sc[h][nt][i] - m[nt]);
                     l[nt] += p[i];
                 }
                 pop[h][nt] = __builtin_bit_cast(

@@ -148,35 +148,42 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_mfma_kernel(Decode
             }
         }
 
-        // scale, mask by selection, tile max per column
+        // scale; mask by selection (only a tile reaching past the sequence
+        // end); tile max per column
+        const bool full = tok_base + TILE <= t1;
         float bm = -INFINITY;
 #pragma unroll
         for (int h = 0; h < MT; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok = tok_base + 16 * h + 4 * g4 + i < t1;
-                const float v = ok ? sc[h][i] * a.qk_scale_log2 : -INFINITY;
+                float v = sc[h][i] * a.qk_scale_log2;
+                if (!full)
+                    v = tok_base + 16 * h + 4 * g4 + i < t1 ? v : -INFINITY;
                 sc[h][i] = v;
                 bm = fmaxf(bm, v);
             }
-        const float mn = fmaxf(m, rows_max(bm));
-        if (__ballot(mn > m)) {
+        const float tm = rows_max(bm);
+        if (__ballot(tm > m + kRebase)) {
+            const float mn = fmaxf(m, tm);
             const float alpha = (mn > m) ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
             l *= alpha;
 #pragma unroll
             for (int d = 0; d < ND; ++d)
                 acc[d] *= alpha;
+            m = mn;
         }
-        m = mn;
 
-        // P = 2^(S - m), summed per lane; bf16 copy is the PV B operand
+        // P = 2^(S - m), summed per lane; bf16 copy is the PV B operand.  In a
+        // full tile every score is finite and m is (the first tile of a
+        // segment always sets it).
         bf16x4 pop[MT];
 #pragma unroll
         for (int h = 0; h < MT; ++h) {
             float p[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[i] = (sc[h][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sc[h][i] - m);
+                p[i] = (!full && sc[h][i] == -INFINITY) ? 0.f
+                                                        : __builtin_amdgcn_exp2f(sc[h][i] - m);
                 l += p[i];
             }
             pop[h] = __builtin_bit_cast(

@@ -57,6 +57,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
     float m[NT], l[NT];
     int lim[NT];                               // tokens [0, lim) visible; 0 = unused column
     int64_t orow[NT];                          // (token * H + head), -1 = unused column
+    int full_end = 0;                          // tiles ending by here need no mask
     bool seg_starts = false;
 
     auto begin_segment = [&](const Cursor &c) {
@@ -64,6 +65,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
         query_span(a, c.s, c.L, &qs, &ql, c.kvh == 0 && lane == 0 ? a.err_flag : nullptr);
         qs = __builtin_amdgcn_readfirstlane(qs);
         ql = __builtin_amdgcn_readfirstlane(ql);
+        full_end = c.L - ql + 1;               // the first query token's bound, the smallest
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int col = 16 * nt + c16;
@@ -124,6 +126,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
     // QK^T for every column tile, online softmax per column, PV.
     auto process = [&](const Cursor &c, int half) {
         const int tok_base = c.j * BS + half * TILE;
+        const bool full = tok_base + TILE <= full_end;   // every column sees the whole tile
         f32x4 sc[MT][NT];
 #pragma unroll
         for (int h = 0; h < MT; ++h) {
@@ -150,27 +153,30 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
             for (int h = 0; h < MT; ++h)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool ok = tok_base + 16 * h + 4 * g4 + i < lim[nt];
-                    const float v = ok ? sc[h][nt][i] * a.qk_scale_log2 : -INFINITY;
+                    float v = sc[h][nt][i] * a.qk_scale_log2;
+                    if (!full)
+                        v = tok_base + 16 * h + 4 * g4 + i < lim[nt] ? v : -INFINITY;
                     sc[h][nt][i] = v;
                     bm = fmaxf(bm, v);
                 }
-            const float mn = fmaxf(m[nt], rows_max(bm));
-            if (__ballot(mn > m[nt])) {
+            const float tm = rows_max(bm);
+            if (__ballot(tm > m[nt] + kRebase)) {
+                const float mn = fmaxf(m[nt], tm);
                 const float alpha = (mn > m[nt]) ? __builtin_amdgcn_exp2f(m[nt] - mn) : 1.f;
                 l[nt] *= alpha;
 #pragma unroll
                 for (int d = 0; d < ND; ++d)
                     acc[nt][d] *= alpha;
+                m[nt] = mn;
             }
-            m[nt] = mn;
 #pragma unroll
             for (int h = 0; h < MT; ++h) {
                 float p[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[i] = (sc[h][nt][i] == -INFINITY) ? 0.f
-                                                       : __builtin_amdgcn_exp2f(sc[h][nt][i] - mn);
+                    p[i] = (!full && sc[h][nt][i] == -INFINITY)
+                               ? 0.f
+                               : __builtin_amdgcn_exp2f(sc[h][nt][i] - m[nt]);
                     l[nt] += p[i];
                 }
                 pop[h][nt] = __builtin_bit_cast(

@@ -77,6 +77,14 @@ __device__ __forceinline__ float rows_sum(float x)
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Online softmax with a lazily moved base: a column's running base m (log2
+// units) moves to a new maximum only when some column's tile maximum exceeds
+// it by more than kRebase, so most tiles skip rescaling the accumulators.
+// The unnormalised weights 2^(s - m) then stay below 2^kRebase; the base
+// cancels in the final acc / l, and a partial's (m, l, acc) stays
+// consistent for the log-sum-exp merge.
+constexpr float kRebase = 8.0f;
+
 // Tile geometry of one KV head's rows for a cache of element type KT.
 template <int KT_, int D_, int BS_>
 struct MfmaGeo {
