@@ -313,12 +313,12 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void cascade_prefix_kernel(Casca
         const int r = row0 + 16 * nt + c16;
         if (r >= R)
             continue;
-        float *o = a.p_acc + (pbase + r) * D + 4 * g4;
+        uint16_t *o = a.p_acc + (pbase + r) * D + 4 * g4;
 #pragma unroll
         for (int d = 0; d < ND; ++d)
-            *reinterpret_cast<float4 *>(o + 16 * d) =
-                make_float4(acc[nt][d][0] * a.v_scale, acc[nt][d][1] * a.v_scale,
-                            acc[nt][d][2] * a.v_scale, acc[nt][d][3] * a.v_scale);
+            *reinterpret_cast<uint2 *>(o + 16 * d) =
+                make_uint2(pack_bf16x2(acc[nt][d][0] * a.v_scale, acc[nt][d][1] * a.v_scale),
+                           pack_bf16x2(acc[nt][d][2] * a.v_scale, acc[nt][d][3] * a.v_scale));
         if (g4 == 0)
             *reinterpret_cast<float2 *>(a.p_ml + (pbase + r) * 2) = make_float2(m[nt], lt);
     }
@@ -358,21 +358,26 @@ __device__ __forceinline__ void lse_fold(Lse &s, const Lse &t)
 // Fold parts [first, last] of one partial source (part stride rps rows, row
 // prow) into st; the lanes' groups take parts p0, p0 + step, ...
 template <int D>
-__device__ __forceinline__ void add_parts(Lse &st, const float *acc_ws, const float *ml_ws,
+__device__ __forceinline__ void add_parts(Lse &st, const uint16_t *acc_ws, const float *ml_ws,
                                           int first, int last, int64_t rps, int64_t prow, int col,
                                           int p0, int step)
 {
     const float2 *ml = reinterpret_cast<const float2 *>(ml_ws) + (int64_t)first * rps + prow;
-    const float *acc = acc_ws + ((int64_t)first * rps + prow) * D + col;
+    const uint16_t *acc = acc_ws + ((int64_t)first * rps + prow) * D + col;
     const int n = last - first + 1;
+    auto bf16x4_at = [&](int p) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(acc + (int64_t)p * rps * D);
+        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    };
     for (int p = p0; p < n; p += 2 * step) {
         float2 m0 = make_float2(-INFINITY, 0.f), m1 = m0;
         float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
         m0 = ml[(int64_t)p * rps];
-        x0 = *reinterpret_cast<const float4 *>(acc + (int64_t)p * rps * D);
+        x0 = bf16x4_at(p);
         if (p + step < n) {
             m1 = ml[(int64_t)(p + step) * rps];
-            x1 = *reinterpret_cast<const float4 *>(acc + (int64_t)(p + step) * rps * D);
+            x1 = bf16x4_at(p + step);
         }
         lse_add(st, m0.x, m0.y, x0);
         lse_add(st, m1.x, m1.y, x1);

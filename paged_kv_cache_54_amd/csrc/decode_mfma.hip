@@ -113,12 +113,12 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void decode_mfma_kernel(Decode
                                pack_bf16x2(acc[d][2] * inv, acc[d][3] * inv));
         } else {
             const int64_t pi = (int64_t)slot * G + c16;
-            float *o = a.ws_acc + pi * D + 4 * g4;
+            uint16_t *o = static_cast<uint16_t *>(a.ws_acc) + pi * D + 4 * g4;
 #pragma unroll
             for (int d = 0; d < ND; ++d)
-                *reinterpret_cast<float4 *>(o + 16 * d) =
-                    make_float4(acc[d][0] * a.v_scale, acc[d][1] * a.v_scale,
-                                acc[d][2] * a.v_scale, acc[d][3] * a.v_scale);
+                *reinterpret_cast<uint2 *>(o + 16 * d) =
+                    make_uint2(pack_bf16x2(acc[d][0] * a.v_scale, acc[d][1] * a.v_scale),
+                               pack_bf16x2(acc[d][2] * a.v_scale, acc[d][3] * a.v_scale));
             if (g4 == 0)
                 *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m, lt);
         }

@@ -19,6 +19,8 @@
 // the wavefronts of a row through LDS.  One wavefront per row when there are
 // many rows (most segments split into a few parts), four when there are few
 // (long sequences cut into hundreds of parts).
+#include <type_traits>
+
 #include "pa_device.h"
 
 namespace pa {
@@ -116,7 +118,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
     if (live && !zero_row) {
         // partial p of this row: slot first + p, row prow
         const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (int64_t)first * RPS + prow;
-        const float *acc = a.ws_acc + ((int64_t)first * RPS + prow) * D + col;
+        using AT = typename std::conditional<OT == KT_F32, float, uint16_t>::type;
+        const AT *acc = static_cast<const AT *>(a.ws_acc) + ((int64_t)first * RPS + prow) * D + col;
         const int stride = WPR * PPW;
         for (int p0 = wr * PPW + sub; p0 < n; p0 += UNROLL * stride) {
             float2 mlv[UNROLL];
@@ -126,7 +129,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
                 const int p = p0 + u * stride;
                 if (p < n) {
                     mlv[u] = ml[(int64_t)p * RPS];
-                    x[u] = *reinterpret_cast<const float4 *>(acc + (int64_t)p * RPS * D);
+                    if constexpr (OT == KT_F32) {
+                        x[u] = *reinterpret_cast<const float4 *>(acc + (int64_t)p * RPS * D);
+                    } else {
+                        const uint2 v = *reinterpret_cast<const uint2 *>(acc + (int64_t)p * RPS * D);
+                        x[u] = make_float4(__uint_as_float(v.x << 16),
+                                           __uint_as_float(v.x & 0xffff0000u),
+                                           __uint_as_float(v.y << 16),
+                                           __uint_as_float(v.y & 0xffff0000u));
+                    }
                 }
             }
 #pragma unroll

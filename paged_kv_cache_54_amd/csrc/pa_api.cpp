@@ -105,9 +105,16 @@ struct DecodePlan {
 };
 
 // Workspace layout: acc [slots, rows, D] f32 | ml [slots, rows, 2] f32 | seg [S*Hkv, 2] i32
+// Partial accumulators are stored in the output's type (bf16 halves the
+// bytes a split segment writes and the merge reads), (m, l) in f32.
+size_t acc_bytes(const DecodePlan &p)
+{
+    return (p.q_type == KT_F32 ? 4 : 2) * (size_t)(p.slots * p.rows) * (size_t)p.D;
+}
+
 size_t workspace_bytes(const DecodePlan &p)
 {
-    return sizeof(float) * (size_t)(p.slots * p.rows) * (size_t)(p.D + 2) +
+    return acc_bytes(p) + sizeof(float) * (size_t)(p.slots * p.rows) * 2 +
            sizeof(int32_t) * 2 * (size_t)(p.S * p.Hkv);
 }
 
@@ -333,8 +340,8 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     a.block_tables = static_cast<const int32_t *>(block_tables->data);
     a.seq_lens = static_cast<const int32_t *>(seq_lens->data);
     a.out = out->data;
-    a.ws_acc = static_cast<float *>(opts->workspace);
-    a.ws_ml = a.ws_acc + p.slots * p.rows * p.D;
+    a.ws_acc = opts->workspace;
+    a.ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(opts->workspace) + acc_bytes(p));
     a.ws_seg = reinterpret_cast<int32_t *>(a.ws_ml + p.slots * p.rows * 2);
     a.err_flag = opts->err_flag;
     a.num_seqs = (int32_t)p.S;
@@ -454,7 +461,7 @@ int plan_cascade(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt, i
     c->tables_off = 0;
     c->lens_off = align256(sizeof(int32_t) * (size_t)(S * (max_nb - N)));
     c->acc_off = c->lens_off + align256(sizeof(int32_t) * (size_t)S);
-    c->ml_off = c->acc_off + align256(sizeof(float) * prow * (size_t)D);
+    c->ml_off = c->acc_off + align256(sizeof(uint16_t) * prow * (size_t)D);
     c->suf_off = c->ml_off + align256(sizeof(float) * prow * 2);
     c->total = S > 0 ? c->suf_off + align256(c->suf.ws_bytes) : 0;
     return PA_OK;
@@ -717,7 +724,7 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     pr.value_cache = value_cache->data;
     pr.block_tables = static_cast<const int32_t *>(block_tables->data);
     pr.seq_lens = static_cast<const int32_t *>(seq_lens->data);
-    pr.p_acc = reinterpret_cast<float *>(ws + c.acc_off);
+    pr.p_acc = reinterpret_cast<uint16_t *>(ws + c.acc_off);
     pr.p_ml = reinterpret_cast<float *>(ws + c.ml_off);
     pr.s_tables = reinterpret_cast<int32_t *>(ws + c.tables_off);
     pr.s_lens = reinterpret_cast<int32_t *>(ws + c.lens_off);
@@ -747,8 +754,8 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     sa.block_tables = pr.s_tables;
     sa.seq_lens = pr.s_lens;
     sa.out = out->data;
-    sa.ws_acc = reinterpret_cast<float *>(ws + c.suf_off);
-    sa.ws_ml = sa.ws_acc + sp.slots * sp.rows * sp.D;
+    sa.ws_acc = ws + c.suf_off;
+    sa.ws_ml = reinterpret_cast<float *>(ws + c.suf_off + acc_bytes(sp));
     sa.ws_seg = reinterpret_cast<int32_t *>(sa.ws_ml + sp.slots * sp.rows * 2);
     sa.err_flag = opts->err_flag;
     sa.num_seqs = (int32_t)sp.S;
@@ -769,7 +776,7 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
 
     CascadeMergeArgs ma;
     ma.out = out->data;
-    ma.s_acc = sa.ws_acc;
+    ma.s_acc = static_cast<const uint16_t *>(sa.ws_acc);
     ma.s_ml = sa.ws_ml;
     ma.s_seg = sa.ws_seg;
     ma.s_lens = pr.s_lens;

@@ -25,8 +25,9 @@ struct DecodeArgs {
     const int32_t *block_tables; // [S, max_nb]
     const int32_t *seq_lens;     // [S]
     void *out;                   // [S, H, D]
-    float *ws_acc;               // [slots, G, D]  unnormalised partial outputs
-    float *ws_ml;                // [slots, G, 2]  (running max in log2 units, sum)
+    void *ws_acc;                // [slots, rows, D] unnormalised partial outputs, in the
+                                 // output's type (bf16 or f32)
+    float *ws_ml;                // [slots, rows, 2] (softmax base in log2 units, sum)
     int32_t *ws_seg;             // [S * Hkv, 2]   first and last slot of each segment
     uint32_t *err_flag;          // optional
     int32_t num_seqs, num_heads, num_kv_heads, max_nb, num_blocks;
@@ -116,7 +117,8 @@ struct CascadePrefixArgs {
     const void *key_cache, *value_cache;
     const int32_t *block_tables;  // [S, max_nb]
     const int32_t *seq_lens;      // [S]
-    float *p_acc, *p_ml;          // [P, Hkv, R, D], [P, Hkv, R, 2]
+    uint16_t *p_acc;              // [P, Hkv, R, D] bf16
+    float *p_ml;                  // [P, Hkv, R, 2]
     int32_t *s_tables;            // [S, max_nb - N]
     int32_t *s_lens;              // [S]
     uint32_t *err_flag;
@@ -131,9 +133,11 @@ struct CascadePrefixArgs {
 // prefix partials (layout above).
 struct CascadeMergeArgs {
     void *out;                    // [S, H, D]
-    const float *s_acc, *s_ml;    // suffix partials
+    const uint16_t *s_acc;        // suffix partials (bf16 acc, f32 m and l)
+    const float *s_ml;
     const int32_t *s_seg, *s_lens;
-    const float *p_acc, *p_ml;    // prefix partials
+    const uint16_t *p_acc;        // prefix partials
+    const float *p_ml;
     int32_t num_seqs, num_heads, num_kv_heads, num_splits;
 };
 

@@ -144,13 +144,14 @@ def test_decode_validation_errors():
     assert call_decode(decode_args(), o) == PA_ERR_WORKSPACE
 
 
-def ws_bytes(S, H, Hkv, D, max_nb, chunk_units):
+def ws_bytes(S, H, Hkv, D, max_nb, chunk_units, acc_elt=4, rows=None):
     """Workspace of a fixed-chunk plan: partial slots = chunks + segments, each
-    holding G rows of D accumulators plus (max, sum); two ints per segment."""
-    G = H // Hkv
+    holding `rows` (G) rows of D accumulators in the output's type (acc_elt
+    bytes) plus an f32 (max, sum); two ints per segment."""
+    rows = H // Hkv if rows is None else rows
     chunks = -(-S * Hkv * max_nb // chunk_units)
     slots = chunks + S * Hkv
-    return 4 * slots * G * (D + 2) + 8 * S * Hkv
+    return acc_elt * slots * rows * D + 8 * slots * rows + 8 * S * Hkv
 
 
 def test_workspace_size_formula():
@@ -163,6 +164,15 @@ def test_workspace_size_formula():
                                             ctypes.byref(n))
         assert rc == PA_OK
         assert n.value == ws_bytes(3, 8, 2, 64, 10, P // 16)
+    # a bf16 output keeps its partial accumulators in bf16
+    b = decode_args(S=3, H=8, Hkv=2, D=64, bs=16, max_nb=10, qd=BF16, kd=BF16)
+    for P in (32, 160):
+        rc = lib().pa_decode_workspace_size(ctypes.byref(b["q"]), ctypes.byref(b["kc"]),
+                                            ctypes.byref(b["bt"]),
+                                            ctypes.byref(opts(partition_tokens=P)),
+                                            ctypes.byref(n))
+        assert rc == PA_OK
+        assert n.value == ws_bytes(3, 8, 2, 64, 10, P // 16, acc_elt=2)
     assert lib().pa_decode_workspace_size(None, ctypes.byref(a["kc"]), ctypes.byref(a["bt"]),
                                           None, ctypes.byref(n)) == PA_ERR_NULL
 
@@ -262,10 +272,7 @@ def test_decode_multi_workspace_formula():
                                                   ctypes.byref(opts(partition_tokens=P)),
                                                   ctypes.byref(n))
         assert rc == PA_OK
-        G = 4
-        chunks = -(-3 * 2 * 10 // (P // 16))
-        slots = chunks + 3 * 2
-        assert n.value == 4 * slots * G * qm * (64 + 2) + 8 * 3 * 2
+        assert n.value == ws_bytes(3, 8, 2, 64, 10, P // 16, acc_elt=2, rows=4 * qm)
 
 
 def test_prepare_step_validation_errors():
