@@ -275,7 +275,10 @@ def bench_blocks(args):
     ms = wall / args.steps * 1e3
     value = nbytes / (ms * 1e-3) / 1e9
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
-    kname = "block_op_kernel<true>" if case.op == "copy" else "block_op_kernel<false>"
+    # the library's choice: one workgroup per 4 KiB piece for operations of
+    # 128 MiB and more (tables here are in device memory), else grouped
+    kind = "block_piece_kernel" if n * R * case.block_bytes >= (128 << 20) else "block_op_kernel"
+    kname = f"{kind}<{'true' if case.op == 'copy' else 'false'}>"
     traffic = traffic_for("blocks", args.workload, kernel=kname)
     res = {
         "metric": f"block {'clear' if case.op == 'zero' else 'copy'}: achieved HBM GB/s "

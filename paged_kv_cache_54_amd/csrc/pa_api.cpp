@@ -236,6 +236,20 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
     return PA_OK;
 }
 
+// Whether HIP knows p as device memory (a host query of the runtime's
+// allocation table: no device access, no synchronisation).  Pinned host
+// memory, or a pointer the runtime does not know, is not; a failed query
+// leaves no error behind for the launch check.
+bool in_device_memory(const void *p)
+{
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return at.type == hipMemoryTypeDevice;
+}
+
 // Shared validation and launch of pa_zero_blocks (src_bases == NULL) and
 // pa_copy_blocks.
 int block_op(const int32_t *ids, int64_t n, const void *const *src_bases,
@@ -288,7 +302,17 @@ int block_op(const int32_t *ids, int64_t n, const void *const *src_bases,
     const int64_t groups = (n + a.group_items - 1) / a.group_items;
     if (groups > INT32_MAX / ((int64_t)num_regions * a.chunks))
         return PA_ERR_UNSUPPORTED;
-    hipError_t e = launch_block_op(a, copy, static_cast<hipStream_t>(hip_stream));
+    a.pieces = (int32_t)((block_bytes + block_op_piece_bytes() - 1) / block_op_piece_bytes());
+    // Large operations with tables in device memory: one workgroup per (item,
+    // region, piece).  Below 128 MiB the grouped kernel's fewer, longer
+    // workgroups measured faster (a 57 MiB clear: 12.1 against 13.5 us).
+    const int64_t pieces = n * num_regions * (int64_t)a.pieces;
+    const bool large = n * num_regions * block_bytes >= (int64_t(128) << 20);
+    const bool device_tables = large && in_device_memory(ids) && in_device_memory(dst_bases) &&
+                               (!copy || in_device_memory(src_bases));
+    hipError_t e = device_tables && pieces <= INT32_MAX
+                       ? launch_block_piece_op(a, copy, static_cast<hipStream_t>(hip_stream))
+                       : launch_block_op(a, copy, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -81,6 +81,7 @@ struct BlockOpArgs {
     int64_t chunks;              // ceil(block_bytes / chunk bytes)
     int32_t num_regions;
     int32_t group_items;         // 1 .. kMaxGroupItems
+    int32_t pieces;              // per-piece kernel: ceil(block_bytes / piece bytes)
 };
 
 // One step's attention inputs gathered from a per-request state table.
@@ -189,5 +190,9 @@ hipError_t launch_step_prep(const StepPrepArgs &a, hipStream_t stream);
 // Block clear (copy = false) or copy; chunk bytes per workgroup pass.
 hipError_t launch_block_op(const BlockOpArgs &a, bool copy, hipStream_t stream);
 int64_t block_op_chunk_bytes();
+// One workgroup per (item, region, piece): for id and base tables in device
+// memory.
+hipError_t launch_block_piece_op(const BlockOpArgs &a, bool copy, hipStream_t stream);
+int64_t block_op_piece_bytes();
 
 }  // namespace pa
