@@ -3,7 +3,9 @@
 the device error word must carry exactly the bits the oracle reports.
 
 Cases: ids and region tables in device memory and in pinned host memory
-(read by the kernel directly), duplicates and out-of-range ids, a cleared
+(read by the kernel directly), operations above and below the size from
+which device-resident tables get one workgroup per 4 KiB piece (both
+kernels, with the same error handling), duplicates and out-of-range ids, a cleared
 part shorter than the block stride, blocks larger than one workgroup pass and
 not a multiple of it, enough ids that workgroups take several each, region
 bases that are NULL or misaligned, copy-on-write inside one pool, and swap out
@@ -61,15 +63,19 @@ def test_zero_blocks(name, nb, n, pin):
     assert int(flag.item()) == want_flag == pa.DEVERR_BLOCK_ID
 
 
-@pytest.mark.parametrize("block_bytes,stride", [(20000, 20016), (16, 48), (16384 * 3, 16384 * 3)])
-def test_zero_partial_and_odd_blocks(block_bytes, stride):
+@pytest.mark.parametrize("block_bytes,stride,nb", [(20000, 20016, 40), (16, 48, 40),
+                                                   (16384 * 3, 16384 * 3, 40),
+                                                   (20000, 20016, 1800)])
+def test_zero_partial_and_odd_blocks(block_bytes, stride, nb):
     """Clear only the first block_bytes of each stride (a block larger or
-    smaller than one workgroup pass, not a multiple of it)."""
-    nb, R = 40, 4
+    smaller than one workgroup pass or piece, not a multiple of either); the
+    1800-block case is large enough for one workgroup per piece."""
+    R = 4
     g = torch.Generator(device=DEV).manual_seed(5)
     regions = [torch.randint(1, 256, (nb, stride), dtype=torch.uint8, device=DEV, generator=g)
                for _ in range(R)]
-    ids = torch.tensor([3, 0, 39, 17, 17, 22], dtype=torch.int32)
+    ids = (torch.tensor([3, 0, 39, 17, 17, 22], dtype=torch.int32) if nb == 40 else
+           torch.randperm(nb).to(torch.int32))
     want, _ = ob.zero_blocks(host(regions), ids.numpy(), stride, block_bytes, nb)
     regs = pa.region_table(regions)
     regs.block_bytes = block_bytes
@@ -79,10 +85,10 @@ def test_zero_partial_and_odd_blocks(block_bytes, stride):
     assert_regions_equal(regions, want, f"partial {block_bytes}/{stride}")
 
 
-def test_zero_bad_region_bases_are_skipped():
-    nb = 8
+@pytest.mark.parametrize("nb,bb", [(8, 4096), (700, 65536)], ids=["small", "large"])
+def test_zero_bad_region_bases_are_skipped(nb, bb):
     g = torch.Generator(device=DEV).manual_seed(6)
-    regions = [torch.randint(1, 256, (nb, 4096), dtype=torch.uint8, device=DEV, generator=g)
+    regions = [torch.randint(1, 256, (nb, bb), dtype=torch.uint8, device=DEV, generator=g)
                for _ in range(3)]
     regs = pa.region_table(regions)
     before = [r.clone() for r in regions]
@@ -90,12 +96,13 @@ def test_zero_bad_region_bases_are_skipped():
     bases[1] = 0                        # NULL
     bases[2] = bases[2] + 8             # misaligned
     bad = pa.Regions(bases, regs.block_stride, regs.block_bytes, nb, regions)
-    ids = torch.tensor([1, 6], dtype=torch.int32, device=DEV)
+    ids = (torch.tensor([1, 6], dtype=torch.int32) if nb == 8 else
+           torch.randperm(nb).to(torch.int32)).to(DEV)
     flag = flag_word()
-    announce("zero bad bases")
+    announce("zero bad bases", nb, bb)
     pa.zero_blocks(ids, bad, err_flag=flag)
     torch.cuda.synchronize()
-    want, _ = ob.zero_blocks(host(before[:1]), ids.cpu().numpy(), 4096, 4096, nb)
+    want, _ = ob.zero_blocks(host(before[:1]), ids.cpu().numpy(), bb, bb, nb)
     assert_regions_equal(regions[:1], want, "good region")
     assert torch.equal(regions[1], before[1]) and torch.equal(regions[2], before[2])
     assert int(flag.item()) == pa.DEVERR_REGION
@@ -114,6 +121,26 @@ def test_copy_on_write_within_pool():
     pa.copy_blocks(pairs.to(DEV), regs, regs, err_flag=flag)
     torch.cuda.synchronize()
     assert_regions_equal(case.regions, want, "cow")
+    assert int(flag.item()) == want_flag == pa.DEVERR_BLOCK_ID
+
+
+def test_large_copy_with_device_tables():
+    """128 MiB and more with tables in device memory: one workgroup per 4 KiB
+    piece; an out-of-range source and destination are skipped and flagged."""
+    case = workloads.make_block_case("block_copy_cow", device=DEV, num_blocks=1200, items=520,
+                                     layers=4)
+    assert case.items.shape[0] * len(case.regions) * case.block_bytes >= 128 << 20
+    pairs = case.items.clone()
+    pairs[3, 0] = -1
+    pairs[11, 1] = 1200
+    want, want_flag = ob.copy_blocks(host(case.regions), host(case.regions), pairs.numpy(),
+                                     case.block_bytes, case.block_bytes, 1200, 1200)
+    regs = pa.region_table(case.regions)
+    flag = flag_word()
+    announce("large copy", pairs.shape[0], "pairs", len(case.regions), "regions")
+    pa.copy_blocks(pairs.to(DEV), regs, regs, err_flag=flag)
+    torch.cuda.synchronize()
+    assert_regions_equal(case.regions, want, "large copy")
     assert int(flag.item()) == want_flag == pa.DEVERR_BLOCK_ID
 
 
