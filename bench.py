@@ -26,8 +26,9 @@ METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + decode seqs/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "valu": ["paged_kv_cache_54_amd/csrc/decode_valu.hip", "paged_kv_cache_54_amd/csrc/pa_device.h"],
-    "mfma": ["paged_kv_cache_54_amd/csrc/decode_mfma.hip", "paged_kv_cache_54_amd/csrc/mfma_common.h",
-             "paged_kv_cache_54_amd/csrc/pa_device.h"],
+    "mfma": ["paged_kv_cache_54_amd/csrc/decode_mfma.hip",
+             "paged_kv_cache_54_amd/csrc/decode_mfma_wave.h",
+             "paged_kv_cache_54_amd/csrc/mfma_common.h", "paged_kv_cache_54_amd/csrc/pa_device.h"],
     "mfma_multi": ["paged_kv_cache_54_amd/csrc/decode_mfma_multi.hip",
                    "paged_kv_cache_54_amd/csrc/mfma_common.h",
                    "paged_kv_cache_54_amd/csrc/pa_device.h"],
@@ -37,7 +38,7 @@ KERNEL_SOURCES["blocks"] = ["paged_kv_cache_54_amd/csrc/blocks.hip",
 KERNEL_SOURCES["cascade"] = KERNEL_SOURCES["mfma"] + ["paged_kv_cache_54_amd/csrc/cascade.hip"]
 KERNEL_NAMES = {"valu": "decode_valu_kernel", "mfma": "decode_mfma_kernel",
                 "mfma_multi": "decode_mfma_multi_kernel",
-                "cascade": "cascade_prefix_kernel + decode_mfma_kernel"}
+                "cascade": "cascade_kernel"}
 
 
 def parse():

@@ -10,40 +10,40 @@
 //                cut into (KV head, token split, row block) workgroups whose
 //                four wavefronts share each K/V tile through LDS;
 //   suffix pass  each sequence against its own blocks from the prefix on:
-//                the single-query kernel over shifted tables, partials only;
+//                the single-query decode wavefronts over the batch viewed
+//                from block N on (table column and length offsets), partials
+//                only;
 //   merge        per (sequence, head): log-sum-exp over both passes' parts.
 //
-// This file holds the prefix kernel (which also writes the suffix pass's
-// shifted tables and lengths and checks the contract) and the merge.
-#include "mfma_common.h"
+// The two passes share one launch: the prefix workgroups come first in the
+// grid (one per compute unit or so, bound by issue and latency), then a few
+// that check the contract, then the suffix pass's (bound by memory), so the
+// prefix pass runs in the shadow of the suffix pass instead of before it.
+// (Running them as two kernels on two streams cost more in the cross-stream
+// waits than the overlap saved.)  The merge is a second kernel.
+#include "decode_mfma_wave.h"
 
 namespace pa {
 namespace {
 
 constexpr int kPrefixWaves = 4;     // wavefronts per prefix workgroup
-constexpr int kPrefixColTiles = 2;  // 16-row column tiles per wavefront
+constexpr int kPrefixColTiles = 1;  // 16-row column tiles per wavefront
 constexpr int kPrefixDepth = 4;     // tiles in flight per workgroup
 constexpr int kThreads = 256;
+constexpr int kSuffixWaves = kThreads / 64;   // suffix-pass wavefronts per workgroup
+static_assert(kPrefixWaves * 64 == kThreads, "a prefix item takes a whole workgroup");
 
-// Suffix pass inputs and the contract check: table rows from block N on,
-// lengths less the prefix; every table starts with row 0's prefix and every
-// sequence covers it.  Workgroup wg of nwg.
-__device__ void suffix_inputs(const CascadePrefixArgs &a, int wg, int nwg)
+// The contract: every table starts with row 0's prefix and every sequence
+// covers it.  Workgroup wg of nwg.
+__device__ void check_contract(const CascadePrefixArgs &a, int wg, int nwg)
 {
     const int N = a.prefix_blocks, S = a.num_seqs;
-    const int sfx = a.max_nb - N;
-    const int64_t n_s = (int64_t)S * sfx, n_chk = (int64_t)S * N;
-    const int64_t total = n_s + n_chk + S;
+    const int64_t n_chk = (int64_t)S * N;
+    const int64_t total = n_chk + S;
     const int cap = a.max_nb * a.block_size;
     for (int64_t e = (int64_t)wg * blockDim.x + threadIdx.x; e < total;
          e += (int64_t)nwg * blockDim.x) {
         int64_t x = e;
-        if (x < n_s) {
-            const int64_t s = x / sfx, j = x % sfx;
-            a.s_tables[x] = a.block_tables[s * a.max_nb + N + j];
-            continue;
-        }
-        x -= n_s;
         if (x < n_chk) {
             const int64_t s = x / N, j = x % N;
             if (a.block_tables[s * a.max_nb + j] != a.block_tables[j])
@@ -51,10 +51,8 @@ __device__ void suffix_inputs(const CascadePrefixArgs &a, int wg, int nwg)
             continue;
         }
         x -= n_chk;
-        const int L = min(a.seq_lens[x], cap);
-        if (L < N * a.block_size)
+        if (min(a.seq_lens[x], cap) < N * a.block_size)
             raise_flag(a.err_flag, PA_DEVERR_PREFIX);
-        a.s_lens[x] = max(0, L - N * a.block_size);
     }
 }
 
@@ -73,15 +71,16 @@ __device__ __forceinline__ void stage_chunk(uint8_t *tile, int row, int chunk, u
     }
 }
 
-// Prefix pass.  Workgroup = four wavefronts over RB = 4 * 16 * NTW query
-// rows; wavefront w owns rows w * 16 * NTW .. of the block as NTW MFMA
-// column tiles.  The 2 * NLOAD load instructions of a tile (K rows, then V
-// rows) are dealt round-robin to the wavefronts; each tile is staged into
-// one of two LDS buffers and, after a barrier, read by all four.  DEPTH
-// tiles are in flight in registers.  Every prefix token is valid (the
-// contract), so no masking.
+// Prefix pass, one work item.  Workgroup = four wavefronts over RB = 4 * 16 *
+// NTW query rows; wavefront w owns rows w * 16 * NTW .. of the block as NTW
+// MFMA column tiles.  The 2 * NLOAD load instructions of a tile (K rows, then
+// V rows) are dealt round-robin to the wavefronts; each tile is staged into
+// one of two LDS buffers (kt0/vt0 + buffer * tile bytes) and, after a
+// barrier, read by all four.  DEPTH tiles are in flight in registers.  Every
+// prefix token is valid (the contract), so no masking.
 template <int KT, int D, int BS, int NTW>
-__global__ __launch_bounds__(64 * kPrefixWaves) void cascade_prefix_kernel(CascadePrefixArgs a)
+__device__ __forceinline__ void prefix_item(const CascadePrefixArgs &a, int item, uint8_t *kt0,
+                                            uint8_t *vt0)
 {
     using Geo = MfmaGeo<KT, D, BS>;
     constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
@@ -92,27 +91,13 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void cascade_prefix_kernel(Casca
     constexpr int DEPTH = kPrefixDepth;
     constexpr int RB = kPrefixWaves * 16 * NTW;
 
-    __shared__ __attribute__((aligned(16))) uint8_t kt_all[2][TILE * KROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t vt_all[2][TILE * VROWB];
+    auto kt_buf = [&](int buf) { return kt0 + buf * (TILE * KROWB); };
+    auto vt_buf = [&](int buf) { return vt0 + buf * (TILE * VROWB); };
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar selects
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4, c16 = lane & 15;
 
-    // The workgroups past the items' 8 * items_per_xcd write the suffix
-    // pass's inputs.
-    const int item_wgs = 8 * a.items_per_xcd;
-    if ((int)blockIdx.x >= item_wgs) {
-        suffix_inputs(a, (int)blockIdx.x - item_wgs, (int)gridDim.x - item_wgs);
-        return;
-    }
-    // Workgroups are dispatched round-robin over the 8 XCDs; consecutive
-    // items -- the row blocks of one (KV head, split), which read the same
-    // tiles -- are given to workgroups of one XCD, so the tiles come from its
-    // L2 after the first read.
-    const int item = (int)(blockIdx.x & 7) * a.items_per_xcd + (int)(blockIdx.x >> 3);
-    if (item >= a.num_items)
-        return;
     const int Hkv = a.num_kv_heads, H = a.num_heads, lg = a.log2_group;
     const int rb = item % a.row_blocks;
     const int pair = item / a.row_blocks;
@@ -162,9 +147,9 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void cascade_prefix_kernel(Casca
         for (int u = 0; u < NPW; ++u) {
             const int q = wave + kPrefixWaves * u;
             if (q < NLOAD)
-                stage_chunk<Geo, KROWB>(kt_all[buf], q * Geo::LROWS + l_row, l_chunk, p.v[u]);
+                stage_chunk<Geo, KROWB>(kt_buf(buf), q * Geo::LROWS + l_row, l_chunk, p.v[u]);
             else if (q < NQ)
-                stage_chunk<Geo, VROWB>(vt_all[buf], (q - NLOAD) * Geo::LROWS + l_row, l_chunk,
+                stage_chunk<Geo, VROWB>(vt_buf(buf), (q - NLOAD) * Geo::LROWS + l_row, l_chunk,
                                         p.v[u]);
         }
     };
@@ -212,8 +197,8 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void cascade_prefix_kernel(Casca
     // One tile from LDS: every K and Vt operand read is issued first, so the
     // reads' latencies overlap each other and the QK products and softmax.
     auto process = [&](int buf) {
-        const uint8_t *kt = kt_all[buf];
-        const uint8_t *vt = vt_all[buf];
+        const uint8_t *kt = kt_buf(buf);
+        const uint8_t *vt = vt_buf(buf);
         bf16x8 kop[MT][NC];
         s16x4 vop[MT][ND];
 #pragma unroll
@@ -324,6 +309,58 @@ __global__ __launch_bounds__(64 * kPrefixWaves) void cascade_prefix_kernel(Casca
     }
 }
 
+// Both passes in one launch.  Workgroups [0, 8 * items_per_xcd) take the
+// prefix items: workgroups are dispatched round-robin over the 8 XCDs, and
+// consecutive items -- the row blocks of one (KV head, split), which read the
+// same tiles -- go to workgroups of one XCD, so the tiles come from its L2
+// after the first read.  The next check_wgs check the contract; the rest run
+// four suffix-pass wavefronts each.  LDS holds a prefix item's two K and two
+// V tile buffers, or one K and one V tile per suffix wavefront.
+//
+// Register use sets how many suffix workgroups share a compute unit with a
+// prefix workgroup.  The bf16, 128-dimension, 16-token-block kernel needs
+// about 180 registers per lane, which allows two wavefronts per SIMD (one
+// suffix workgroup per compute unit); held to 168 it fits three without
+// spilling, and the suffix pass gets twice the wavefronts.  (Other shapes
+// either fit three or more already or spill at 168.)
+template <int KT, int D, int BS>
+constexpr int cascade_waves_per_simd()
+{
+    return (KT == KT_BF16 && D == 128 && BS == 16) ? 3 : 1;
+}
+
+template <int KT, int D, int BS, int NTW, int G>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(cascade_waves_per_simd<KT, D, BS>()))) void cascade_kernel(
+    CascadePrefixArgs p, DecodeArgs s)
+{
+    using Geo = MfmaGeo<KT, D, BS>;
+    constexpr int KTILE = Geo::TILE * Geo::KROWB, VTILE = Geo::TILE * Geo::VROWB;
+    static_assert(kSuffixWaves >= 2, "a prefix item takes two buffers of each");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kSuffixWaves * (KTILE + VTILE)];
+    uint8_t *const vt0 = lds + kSuffixWaves * KTILE;
+
+    int wg = blockIdx.x;
+    const int item_wgs = 8 * p.items_per_xcd;
+    if (wg < item_wgs) {
+        const int item = (wg & 7) * p.items_per_xcd + (wg >> 3);
+        if (item < p.num_items)
+            prefix_item<KT, D, BS, NTW>(p, item, lds, vt0);
+        return;
+    }
+    wg -= item_wgs;
+    if (wg < p.check_wgs) {
+        check_contract(p, wg, p.check_wgs);
+        return;
+    }
+    wg -= p.check_wgs;
+    const int wave = threadIdx.x >> 6;
+    // wavefronts past s.num_waves get no chunk
+    const TableView view{p.max_nb, p.prefix_blocks * p.block_size};
+    decode_mfma_wave<KT, D, BS, G>(s, view, wg * kSuffixWaves + wave, lds + wave * KTILE,
+                                   vt0 + wave * VTILE);
+}
+
 struct Lse {
     float M, den;
     float4 o;
@@ -399,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(CascadeMergeArg
     const int s = (int)(r / H), h = (int)(r % H), kvh = h / G;
 
     Lse st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
-    if (a.s_lens[s] > 0) {                       // the sequence's own blocks
+    if (min(a.seq_lens[s], a.capacity) > a.prefix_tokens) {   // the sequence's own blocks
         const int g = s * Hkv + kvh;
         add_parts<D>(st, a.s_acc, a.s_ml, a.s_seg[2 * g], a.s_seg[2 * g + 1], G, h % G, col,
                      sub, PPW);
@@ -435,15 +472,27 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(CascadeMergeArg
     }
 }
 
-typedef void (*PrefixKernel)(CascadePrefixArgs);
+typedef void (*CascadeKernel)(CascadePrefixArgs, DecodeArgs);
+
+template <int KT, int D, int BS>
+CascadeKernel pick_g(int group)
+{
+    switch (group) {
+    case 1: return cascade_kernel<KT, D, BS, kPrefixColTiles, 1>;
+    case 2: return cascade_kernel<KT, D, BS, kPrefixColTiles, 2>;
+    case 4: return cascade_kernel<KT, D, BS, kPrefixColTiles, 4>;
+    case 8: return cascade_kernel<KT, D, BS, kPrefixColTiles, 8>;
+    default: return nullptr;
+    }
+}
 
 template <int KT>
-PrefixKernel pick_prefix(int d, int bs)
+CascadeKernel pick_shape(int d, int bs, int group)
 {
-    if (d == 64 && bs == 16) return cascade_prefix_kernel<KT, 64, 16, kPrefixColTiles>;
-    if (d == 64 && bs == 32) return cascade_prefix_kernel<KT, 64, 32, kPrefixColTiles>;
-    if (d == 128 && bs == 16) return cascade_prefix_kernel<KT, 128, 16, kPrefixColTiles>;
-    if (d == 128 && bs == 32) return cascade_prefix_kernel<KT, 128, 32, kPrefixColTiles>;
+    if (d == 64 && bs == 16) return pick_g<KT, 64, 16>(group);
+    if (d == 64 && bs == 32) return pick_g<KT, 64, 32>(group);
+    if (d == 128 && bs == 16) return pick_g<KT, 128, 16>(group);
+    if (d == 128 && bs == 32) return pick_g<KT, 128, 32>(group);
     return nullptr;
 }
 
@@ -451,20 +500,40 @@ PrefixKernel pick_prefix(int d, int bs)
 
 int cascade_prefix_rows() { return kPrefixWaves * 16 * kPrefixColTiles; }
 
-hipError_t launch_cascade_prefix(const CascadePrefixArgs &a, int kv_type, int head_dim,
-                                 int block_size, hipStream_t stream)
+hipError_t cascade_suffix_occupancy(int kv_type, int head_dim, int block_size, int group,
+                                    int *waves_per_cu)
 {
-    const PrefixKernel k = kv_type == KT_BF16   ? pick_prefix<KT_BF16>(head_dim, block_size)
-                           : kv_type == KT_E4M3 ? pick_prefix<KT_E4M3>(head_dim, block_size)
-                                                : nullptr;
+    const CascadeKernel k = kv_type == KT_BF16   ? pick_shape<KT_BF16>(head_dim, block_size, group)
+                            : kv_type == KT_E4M3 ? pick_shape<KT_E4M3>(head_dim, block_size, group)
+                                                 : nullptr;
     if (!k)
         return hipErrorInvalidValue;
-    // item workgroups, then those for the suffix inputs (about 1k elements each)
-    const int64_t side = (int64_t)a.num_seqs * (a.max_nb + 1);
-    int64_t side_wgs = (side + 4 * 64 * kPrefixWaves - 1) / (4 * 64 * kPrefixWaves);
-    side_wgs = side_wgs < 1 ? 1 : (side_wgs > 256 ? 256 : side_wgs);
-    hipLaunchKernelGGL(k, dim3((unsigned)(8 * (int64_t)a.items_per_xcd + side_wgs)),
-                       dim3(64 * kPrefixWaves), 0, stream, a);
+    int wgs = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &wgs, reinterpret_cast<const void *>(k), kThreads, 0);
+    *waves_per_cu = (wgs > 1 ? wgs - 1 : 1) * kSuffixWaves;
+    return e;
+}
+
+hipError_t launch_cascade(const CascadePrefixArgs &p, const DecodeArgs &s, int kv_type,
+                          int head_dim, int block_size, int group, hipStream_t stream)
+{
+    const CascadeKernel k = kv_type == KT_BF16   ? pick_shape<KT_BF16>(head_dim, block_size, group)
+                            : kv_type == KT_E4M3 ? pick_shape<KT_E4M3>(head_dim, block_size, group)
+                                                 : nullptr;
+    if (!k)
+        return hipErrorInvalidValue;
+    // item workgroups, those for the contract check (about 1k elements
+    // each), then the suffix pass's
+    CascadePrefixArgs args = p;
+    const int64_t check = (int64_t)p.num_seqs * (p.prefix_blocks + 1);
+    int64_t check_wgs = (check + 4 * kThreads - 1) / (4 * kThreads);
+    args.check_wgs = (int32_t)(check_wgs < 1 ? 1 : (check_wgs > 256 ? 256 : check_wgs));
+    const int64_t wgs = 8 * (int64_t)p.items_per_xcd + args.check_wgs +
+                        ((int64_t)s.num_waves + kSuffixWaves - 1) / kSuffixWaves;
+    if (wgs > INT32_MAX)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k, dim3((unsigned)wgs), dim3(kThreads), 0, stream, args, s);
     return hipGetLastError();
 }
 

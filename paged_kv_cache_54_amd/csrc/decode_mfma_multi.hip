@@ -42,7 +42,8 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
     const int cap = a.max_nb * BS;
     const int w = blockIdx.x;
 
-    const Chunk chunk = my_chunk<BS>(a, w, a.num_waves);
+    const Lens lens{a.seq_lens, 0};
+    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
     if (chunk.n == 0)
         return;
 
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
     // Walk the chunk tile by tile with one register tile in flight: tile k is
     // staged into LDS, then the loads of tile k+1 are issued into the same
     // registers and stay in flight while tile k is computed from LDS.
-    BlockIds ids(a.block_tables, a.max_nb, a.num_blocks, a.err_flag);
+    BlockIds ids(a.block_tables, a.max_nb, a.max_nb, a.num_blocks, a.err_flag);
     Cursor cc = chunk.start;
     Cursor lc = cc;
     const int n = chunk.n;
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
         }
         if (++l_half == HALVES) {
             l_half = 0;
-            advance<BS>(lc, a.seq_lens, Hkv, cap);
+            advance<BS>(lc, lens, Hkv, cap);
             l_id = ids.get(lc.s, lc.j);
         }
     };
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
             if (ends || unit == n - 1)
                 finish_segment(cc, ends);
             if (unit + 1 < n)
-                advance<BS>(cc, a.seq_lens, Hkv, cap);
+                advance<BS>(cc, lens, Hkv, cap);
         }
         id = id_next;
         half = half_next;

@@ -1,0 +1,303 @@
+// decode_mfma_wave.h -- one wavefront of paged decode attention on the gfx950
+// matrix cores, for a bf16 query with a bf16 or OCP e4m3 KV cache.
+//
+// What is computed is the same as the vector-ALU kernel (vLLM concept page,
+// "Technical principles": PagedAttention gathers the blocks named by the page
+// table inside one fused kernel and runs scaled-dot-product attention over
+// them; grouped-query heads share a KV head).  The work split (equal chunks
+// of the batch's (sequence, KV head, block) list, one per wavefront),
+// selection masking and the partial/merge contract are also the same; what
+// differs is how one block of one KV head is processed by a wavefront:
+//
+//   loads K and V arrive in 16-token tiles (a 32-token block is two tiles)
+//         through 16-byte row-contiguous buffer loads (a
+//         wavefront instruction reads whole 256-byte rows; reading K directly
+//         in MFMA operand order -- 16 rows x 64 bytes per instruction --
+//         measured 15-20 % slower) and are stored to LDS as bf16 rows.
+//   QK^T  v_mfma_f32_16x16x32_bf16, A = K tile (M = 16 tokens, K = 32 dims)
+//         read from LDS, B = Q^T (N = 16 columns; column n is query head
+//         n mod G of the group).  Lane l gets S[token 4*(l/16)+i][column l%16]
+//         in its 4 accumulators.
+//   softmax  per column: max over the lane's 4 tokens and across the four
+//         16-lane groups; running max m, lane-partial sum l, one (lazy)
+//         rescale of the accumulators when some column's max grows.
+//   PV    v_mfma_f32_16x16x16bf16_1k computing O^T = V^T P^T: B = P^T is
+//         exactly the QK accumulator layout (converted to bf16), A = V^T is
+//         read from LDS with ds_read_b64_tr_b16, which transposes 16-bit
+//         elements within each 16-lane group.
+//
+// An e4m3 cache is converted to bf16 (exact) in registers before K and V are
+// stored to LDS; k_scale is folded into the score scale
+// and v_scale applied to the result.  Tokens at or beyond seq_len in the last
+// block are excluded by selection: their scores become -inf and their V rows
+// are stored to LDS as zeros, so stale NaN/Inf bits never enter an MFMA.
+//
+// decode_mfma_wave is the whole of a wavefront's work: its chunk of the work
+// list, walked tile by tile through its own LDS tiles kt and vt (TILE * KROWB
+// and TILE * VROWB bytes).  It is the body of the single-query decode kernel
+// and of the cascade's suffix pass, which runs it over a batch viewed from a
+// later block on: row s of the tables at a.block_tables + s * v.stride, each
+// length less v.len_offset ({a.max_nb, 0} for a plain batch).
+#pragma once
+
+#include "mfma_common.h"
+
+namespace pa {
+
+struct TableView {
+    int stride, len_offset;
+};
+
+template <int KT, int D, int BS, int G>
+__device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView v, int w,
+                                                 uint8_t *const kt, uint8_t *const vt)
+{
+    using Geo = MfmaGeo<KT, D, BS>;
+    constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
+    constexpr int HALVES = Geo::HALVES;
+    constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
+    static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group must divide 16");
+    // bf16: two register tiles in flight.  e4m3 (32-token tiles) keeps one,
+    // which holds its register use at two wavefronts per SIMD.
+    constexpr bool PINGPONG = KT == KT_BF16;
+
+    const int lane = threadIdx.x & 63;
+    const int g4 = lane >> 4;                  // 16-lane group
+    const int c16 = lane & 15;                 // token row (K operand) / column (output)
+    const int H = a.num_heads, Hkv = a.num_kv_heads;
+    const int cap = a.max_nb * BS;
+
+    const Lens lens{a.seq_lens, v.len_offset};
+    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
+    if (chunk.n == 0)
+        return;
+
+    const MfmaLoader<Geo> loader(a, lane);
+    using Tile = MfmaTile<Geo>;
+    auto load_tile = [&](int id, int kvh, int half, Tile &t) { loader.load(id, kvh, half, t); };
+
+    // per-segment state
+    bf16x8 qop[NC];
+    f32x4 acc[ND];
+    float m = -INFINITY, l = 0.f;
+    bool seg_starts = false;
+
+    auto begin_segment = [&](const Cursor &c) {
+        // Q^T operand: column c16 is query head kvh*G + c16 % G; 8 dims per lane per MFMA
+        const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
+                               ((int64_t)c.s * H + c.kvh * G + (c16 % G)) * D + 8 * g4;
+#pragma unroll
+        for (int k = 0; k < NC; ++k)
+            qop[k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * k));
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m = -INFINITY;
+        l = 0.f;
+        seg_starts = c.j == 0;
+    };
+
+    auto finish_segment = [&](const Cursor &c, bool ends) {
+        const float lt = rows_sum(l);          // sum the four 16-lane groups
+        const int g = c.s * Hkv + c.kvh;
+        const int slot = w + g;
+        record_segment(a, g, slot, seg_starts, ends);
+        if (c16 >= G)
+            return;                            // replicated columns
+        const int64_t row = (int64_t)c.s * H + c.kvh * G + c16;
+        if (seg_starts && ends && !(a.flags & kPartialOnly)) {
+            const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
+            uint16_t *o = static_cast<uint16_t *>(a.out) + row * D + 4 * g4;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                *reinterpret_cast<uint2 *>(o + 16 * d) =
+                    make_uint2(pack_bf16x2(acc[d][0] * inv, acc[d][1] * inv),
+                               pack_bf16x2(acc[d][2] * inv, acc[d][3] * inv));
+        } else {
+            const int64_t pi = (int64_t)slot * G + c16;
+            uint16_t *o = static_cast<uint16_t *>(a.ws_acc) + pi * D + 4 * g4;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                *reinterpret_cast<uint2 *>(o + 16 * d) =
+                    make_uint2(pack_bf16x2(acc[d][0] * a.v_scale, acc[d][1] * a.v_scale),
+                               pack_bf16x2(acc[d][2] * a.v_scale, acc[d][3] * a.v_scale));
+            if (g4 == 0)
+                *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m, lt);
+        }
+    };
+
+    // Stage a tile of the current segment into LDS as bf16 (V rows past the
+    // sequence end as zeros).
+    auto stage = [&](const Cursor &c, int half, const Tile &t) {
+        stage_tile<Geo>(loader, kt, vt, t, c.j * BS + half * TILE, c.L);
+    };
+
+    // QK^T, online softmax and PV of the staged tile.
+    auto process = [&](const Cursor &c, int half) {
+        const int tok_base = c.j * BS + half * TILE;
+        const int t1 = c.L;
+
+        // S = K Q^T per 16-token sub-tile; K operand: token c16, dims 32k + 8*g4
+        f32x4 sc[MT];
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint8_t *krow = kt + (16 * h + c16) * KROWB + 16 * g4;
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+                const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + 64 * k));
+                sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[k], sc[h], 0, 0, 0);
+            }
+        }
+
+        // scale; mask by selection (only a tile reaching past the sequence
+        // end); tile max per column
+        const bool full = tok_base + TILE <= t1;
+        float bm = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < MT; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v = sc[h][i] * a.qk_scale_log2;
+                if (!full)
+                    v = tok_base + 16 * h + 4 * g4 + i < t1 ? v : -INFINITY;
+                sc[h][i] = v;
+                bm = fmaxf(bm, v);
+            }
+        const float tm = rows_max(bm);
+        if (__ballot(tm > m + kRebase)) {
+            const float mn = fmaxf(m, tm);
+            const float alpha = (mn > m) ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+            l *= alpha;
+#pragma unroll
+            for (int d = 0; d < ND; ++d)
+                acc[d] *= alpha;
+            m = mn;
+        }
+
+        // P = 2^(S - m), summed per lane; bf16 copy is the PV B operand.  In a
+        // full tile every score is finite and m is (the first tile of a
+        // segment always sets it).
+        bf16x4 pop[MT];
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            float p[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[i] = (!full && sc[h][i] == -INFINITY) ? 0.f
+                                                        : __builtin_amdgcn_exp2f(sc[h][i] - m);
+                l += p[i];
+            }
+            pop[h] = __builtin_bit_cast(
+                bf16x4, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+        }
+
+        // O^T += V^T P^T, V^T read transposed from LDS
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const int row = 16 * h + 4 * g4 + (c16 >> 2);
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+                const int addr = row * VROWB + 32 * d + 8 * (c16 & 3);
+                const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)((__attribute__((address_space(3))) uint8_t *)vt + addr));
+                acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(raw), pop[h],
+                                                                 acc[d], 0, 0, 0);
+            }
+        }
+    };
+
+    // Walk the chunk tile by tile: the load cursor runs one tile ahead of the
+    // compute cursor, across block and segment boundaries.
+    BlockIds ids(a.block_tables, v.stride, a.max_nb, a.num_blocks, a.err_flag);
+    Cursor cc = chunk.start;
+    Cursor lc = cc;
+    const int n = chunk.n;                     // units (blocks)
+    const int steps = n * HALVES;              // tiles
+
+    // next_load moves the load cursor to tile `k`; past the chunk's last tile
+    // it yields no block (id -1), whose loads read nothing.
+    int l_half = 0;
+    int l_id = ids.get(lc.s, lc.j);
+    auto next_load = [&](int k) {
+        if (k >= steps) {
+            l_id = -1;
+            return;
+        }
+        if (++l_half == HALVES) {
+            l_half = 0;
+            advance<BS>(lc, lens, Hkv, cap);
+            l_id = ids.get(lc.s, lc.j);
+        }
+    };
+
+    // A tile's segment is started (its query rows loaded) before the loads of
+    // the following tile are issued: loads retire in order, so query loads
+    // issued after them would make the tile wait for the following one.
+    auto pre_step = [&](int k, int half) {
+        const int unit = k / HALVES;
+        if (half == 0 && (unit == 0 || cc.j == 0))
+            begin_segment(cc);
+    };
+    auto step = [&](int k, int id, int half, const Tile &t, auto issue_next) {
+        const int unit = k / HALVES;
+        if (id >= 0)
+            stage(cc, half, t);
+        issue_next();
+        if (id >= 0)
+            process(cc, half);
+        if (half == HALVES - 1) {
+            const bool ends = cc.j == cc.nb - 1;
+            if (ends || unit == n - 1)
+                finish_segment(cc, ends);
+            if (unit + 1 < n)
+                advance<BS>(cc, lens, Hkv, cap);
+        }
+    };
+
+    // Loads are issued unconditionally (a missing block reads nothing), so the
+    // wait before staging a tile counts exactly the loads issued after it.
+    if constexpr (PINGPONG) {
+        // Two register tiles: tile k+1 is loaded into the other tile before
+        // tile k is waited on, so two tiles are in flight at the wait.
+        Tile ta, tb;
+        int ida = l_id, ha = l_half;
+        load_tile(ida, lc.kvh, ha, ta);
+        for (int k = 0; k < steps; k += 2) {
+            pre_step(k, ha);
+            next_load(k + 1);
+            const int idb = l_id, hb = l_half;
+            load_tile(idb, lc.kvh, hb, tb);
+            step(k, ida, ha, ta, [] {});
+            if (k + 1 >= steps)
+                break;
+            pre_step(k + 1, hb);
+            next_load(k + 2);
+            ida = l_id;
+            ha = l_half;
+            load_tile(ida, lc.kvh, ha, ta);
+            step(k + 1, idb, hb, tb, [] {});
+        }
+    } else {
+        // One register tile: tile k is staged into LDS, then the loads of tile
+        // k+1 are issued into the same registers and stay in flight while
+        // tile k is computed from LDS.
+        Tile t;
+        int id = l_id, half = l_half;
+        load_tile(id, lc.kvh, half, t);
+        for (int k = 0; k < steps; ++k) {
+            int id_next = -1, half_next = 0;
+            pre_step(k, half);
+            step(k, id, half, t, [&] {
+                next_load(k + 1);
+                id_next = l_id;
+                half_next = l_half;
+                load_tile(id_next, lc.kvh, half_next, t);
+            });
+            id = id_next;
+            half = half_next;
+        }
+    }
+}
+
+}  // namespace pa

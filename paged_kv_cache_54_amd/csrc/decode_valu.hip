@@ -41,7 +41,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a)
     const int cap = a.max_nb * BS;
     const int w = blockIdx.x;
 
-    const Chunk chunk = my_chunk<BS>(a, w, a.num_waves);
+    const Lens lens{a.seq_lens, 0};
+    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
     if (chunk.n == 0)
         return;
 
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a)
     };
 
     // Walk the chunk; the next block's loads are issued before this one is used.
-    BlockIds ids(a.block_tables, a.max_nb, a.num_blocks, a.err_flag);
+    BlockIds ids(a.block_tables, a.max_nb, a.max_nb, a.num_blocks, a.err_flag);
     Cursor cc = chunk.start;
     Cursor lc = cc;
     const int n = chunk.n;
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a)
     for (int k = 0; k < n; ++k) {
         int id_next = -1;
         if (k + 1 < n) {
-            advance<BS>(lc, a.seq_lens, Hkv, cap);
+            advance<BS>(lc, lens, Hkv, cap);
             id_next = ids.get(lc.s, lc.j);
             if (id_next >= 0)
                 load_tile(id_next, lc.kvh, nxt);
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a)
         if (ends || k == n - 1)
             finish_segment(cc, ends);
         if (k + 1 < n)
-            advance<BS>(cc, a.seq_lens, Hkv, cap);
+            advance<BS>(cc, lens, Hkv, cap);
         id = id_next;
         cur = nxt;
     }

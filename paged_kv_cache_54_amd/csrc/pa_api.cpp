@@ -119,16 +119,18 @@ size_t workspace_bytes(const DecodePlan &p)
 }
 
 // Wavefronts of the chosen kernel one compute unit holds at once, cached per
-// (device, kernel instance).
-int resident_waves_per_cu(const DecodePlan &p, int *waves)
+// (device, kernel instance).  cascade: the suffix-pass wavefronts of the
+// cascade kernel, which shares each compute unit with a prefix workgroup.
+int resident_waves_per_cu(const DecodePlan &p, int *waves, bool cascade = false)
 {
     static std::mutex mu;
     static std::vector<std::pair<long long, int>> cache;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return PA_ERR_HIP;
-    const long long key = (((((((long long)dev * 4 + p.variant) * 4 + p.q_type) * 4 + p.kv_type) *
-                             256 + p.D) * 64 + p.bs) * 32 + p.G) * 8 + p.col_tiles;
+    const long long key = ((((((((long long)dev * 4 + p.variant) * 4 + p.q_type) * 4 + p.kv_type) *
+                             256 + p.D) * 64 + p.bs) * 32 + p.G) * 8 + p.col_tiles) * 2 +
+                         cascade;
     std::lock_guard<std::mutex> lock(mu);
     for (auto &kv : cache)
         if (kv.first == key) {
@@ -137,7 +139,8 @@ int resident_waves_per_cu(const DecodePlan &p, int *waves)
         }
     int n = 0;
     hipError_t e =
-        p.QM > 0 ? decode_mfma_multi_occupancy(p.kv_type, (int)p.D, (int)p.bs,
+        cascade    ? cascade_suffix_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G, &n)
+        : p.QM > 0 ? decode_mfma_multi_occupancy(p.kv_type, (int)p.D, (int)p.bs,
                                                (int)p.col_tiles, &n)
         : p.variant == PA_VARIANT_MFMA
             ? decode_mfma_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G, &n)
@@ -427,7 +430,7 @@ pa_tensor reshaped(const pa_tensor *t, std::initializer_list<int64_t> shape)
 struct CascadePlan {
     DecodePlan suf;
     int64_t S, N, G, R, row_blocks, P, split_blocks, items, per_xcd;
-    size_t tables_off, lens_off, acc_off, ml_off, suf_off, total;
+    size_t acc_off, ml_off, suf_off, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -456,6 +459,16 @@ int plan_cascade(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt, i
     int rc;
     if ((rc = plan_decode(q, kc, &bt_suf, &o, 0, &c->suf)))
         return rc;
+    if (c->suf.chunk_units == 0 && S > 0) {
+        // balanced chunks: the suffix wavefronts the cascade kernel holds
+        // beside the prefix workgroups
+        int cus = 0, per_cu = 0;
+        if ((rc = device_cu_count(&cus)) || (rc = resident_waves_per_cu(c->suf, &per_cu, true)))
+            return rc;
+        c->suf.waves = (int64_t)cus * per_cu;
+        c->suf.slots = c->suf.waves + c->suf.S * c->suf.Hkv;
+        c->suf.ws_bytes = workspace_bytes(c->suf);
+    }
     const int64_t Hkv = c->suf.Hkv, D = c->suf.D;
     c->S = S;
     c->N = N;
@@ -479,12 +492,10 @@ int plan_cascade(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt, i
     c->P = (N + c->split_blocks - 1) / c->split_blocks;
     c->items = pairs * c->P;
     c->per_xcd = (c->items + 7) / 8;
-    if (c->R > INT32_MAX / 2 || c->items > INT32_MAX / 2 || S * (max_nb - N) > INT32_MAX)
+    if (c->R > INT32_MAX / 2 || c->items > INT32_MAX / 2)
         return PA_ERR_UNSUPPORTED;
     const size_t prow = (size_t)(c->P * Hkv * c->R);
-    c->tables_off = 0;
-    c->lens_off = align256(sizeof(int32_t) * (size_t)(S * (max_nb - N)));
-    c->acc_off = c->lens_off + align256(sizeof(int32_t) * (size_t)S);
+    c->acc_off = 0;
     c->ml_off = c->acc_off + align256(sizeof(uint16_t) * prow * (size_t)D);
     c->suf_off = c->ml_off + align256(sizeof(float) * prow * 2);
     c->total = S > 0 ? c->suf_off + align256(c->suf.ws_bytes) : 0;
@@ -750,8 +761,6 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     pr.seq_lens = static_cast<const int32_t *>(seq_lens->data);
     pr.p_acc = reinterpret_cast<uint16_t *>(ws + c.acc_off);
     pr.p_ml = reinterpret_cast<float *>(ws + c.ml_off);
-    pr.s_tables = reinterpret_cast<int32_t *>(ws + c.tables_off);
-    pr.s_lens = reinterpret_cast<int32_t *>(ws + c.lens_off);
     pr.err_flag = opts->err_flag;
     pr.num_seqs = (int32_t)c.S;
     pr.num_heads = (int32_t)sp.H;
@@ -767,16 +776,18 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     pr.num_items = (int32_t)c.items;
     pr.items_per_xcd = (int32_t)c.per_xcd;
     pr.log2_group = __builtin_ctz((unsigned)c.G);
+    pr.check_wgs = 0;   // the launcher sizes the check
     pr.qk_scale_log2 = scale * kLog2e * ks;
     pr.v_scale = vs;
 
-    // suffix pass: the single-query kernel over the shifted tables, partials only
+    // suffix pass: single-query decode wavefronts over the batch viewed from
+    // block N on, partials only
     DecodeArgs sa;
     sa.q = q->data;
     sa.key_cache = key_cache->data;
     sa.value_cache = value_cache->data;
-    sa.block_tables = pr.s_tables;
-    sa.seq_lens = pr.s_lens;
+    sa.block_tables = pr.block_tables + c.N;
+    sa.seq_lens = pr.seq_lens;
     sa.out = out->data;
     sa.ws_acc = ws + c.suf_off;
     sa.ws_ml = reinterpret_cast<float *>(ws + c.suf_off + acc_bytes(sp));
@@ -803,7 +814,9 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     ma.s_acc = static_cast<const uint16_t *>(sa.ws_acc);
     ma.s_ml = sa.ws_ml;
     ma.s_seg = sa.ws_seg;
-    ma.s_lens = pr.s_lens;
+    ma.seq_lens = pr.seq_lens;
+    ma.prefix_tokens = (int32_t)(c.N * sp.bs);
+    ma.capacity = pr.max_nb * pr.block_size;
     ma.p_acc = pr.p_acc;
     ma.p_ml = pr.p_ml;
     ma.num_seqs = (int32_t)c.S;
@@ -817,10 +830,8 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     if (ev0 && hipEventRecord(ev0, stream) != hipSuccess)
         return PA_ERR_HIP;
     hipError_t e;
-    if ((e = launch_cascade_prefix(pr, sp.kv_type, (int)sp.D, (int)sp.bs, stream)) !=
-            hipSuccess ||
-        (e = launch_decode_mfma(sa, sp.kv_type, (int)sp.D, (int)sp.bs, (int)sp.G, stream)) !=
-            hipSuccess)
+    if ((e = launch_cascade(pr, sa, sp.kv_type, (int)sp.D, (int)sp.bs, (int)sp.G, stream)) !=
+        hipSuccess)
         return PA_ERR_HIP;
     if (ev1 && hipEventRecord(ev1, stream) != hipSuccess)
         return PA_ERR_HIP;

@@ -255,6 +255,14 @@ __device__ __forceinline__ int wave_incl_scan_i(int x)
     return x;
 }
 
+// Sequence lengths as the work split sees them: seq_lens[s] - off (off > 0
+// for a batch viewed from a later block on, 0 otherwise).
+struct Lens {
+    const int32_t *p;
+    int off;
+    __device__ __forceinline__ int operator[](int s) const { return p[s] - off; }
+};
+
 template <int BS>
 __device__ __forceinline__ int seq_blocks(int L, int cap)
 {
@@ -265,7 +273,7 @@ __device__ __forceinline__ int seq_blocks(int L, int cap)
 // Units of the whole batch; raises PA_DEVERR_SEQ_LEN through `flag` (if
 // non-null) when some seq_len exceeds the capacity.
 template <int BS>
-__device__ int64_t total_units(const int32_t *lens, int S, int Hkv, int cap, uint32_t *flag)
+__device__ int64_t total_units(Lens lens, int S, int Hkv, int cap, uint32_t *flag)
 {
     int64_t total = 0;
     bool over = false;
@@ -288,7 +296,7 @@ struct Cursor {
 
 // Cursor of unit u (< total units).
 template <int BS>
-__device__ Cursor locate(const int32_t *lens, int S, int Hkv, int cap, int64_t u)
+__device__ Cursor locate(Lens lens, int S, int Hkv, int cap, int64_t u)
 {
     int64_t base = 0;
     for (int c = 0; c < S; c += 64) {
@@ -315,7 +323,7 @@ __device__ Cursor locate(const int32_t *lens, int S, int Hkv, int cap, int64_t u
 
 // Next unit; only called when one exists, so a non-empty sequence lies ahead.
 template <int BS>
-__device__ __forceinline__ void advance(Cursor &c, const int32_t *lens, int Hkv, int cap)
+__device__ __forceinline__ void advance(Cursor &c, Lens lens, int Hkv, int cap)
 {
     if (++c.j < c.nb)
         return;
@@ -333,15 +341,16 @@ __device__ __forceinline__ void advance(Cursor &c, const int32_t *lens, int Hkv,
 // Physical block id of a cursor position, wave-uniform; ids of one sequence
 // are read 64 at a time by the lanes and handed out with readlane.  An id
 // outside [0, num_blocks) comes back as -1 and raises PA_DEVERR_BLOCK_ID.
+// Row s of the tables starts at tables + s * stride; max_nb entries are read.
 struct BlockIds {
     const int32_t *tables;
-    int max_nb, num_blocks;
+    int stride, max_nb, num_blocks;
     uint32_t *err;
     int s = -1, base = 0, ids = 0;
 
-    __device__ __forceinline__ BlockIds(const int32_t *tables_, int max_nb_, int nblocks,
-                                        uint32_t *err_)
-        : tables(tables_), max_nb(max_nb_), num_blocks(nblocks), err(err_)
+    __device__ __forceinline__ BlockIds(const int32_t *tables_, int stride_, int max_nb_,
+                                        int nblocks, uint32_t *err_)
+        : tables(tables_), stride(stride_), max_nb(max_nb_), num_blocks(nblocks), err(err_)
     {
     }
 
@@ -351,7 +360,7 @@ struct BlockIds {
             s = s_;
             base = j;
             const int jj = j + lane_id();
-            ids = jj < max_nb ? tables[(int64_t)s_ * max_nb + jj] : 0;
+            ids = jj < max_nb ? tables[(int64_t)s_ * stride + jj] : 0;
         }
         const int id = __builtin_amdgcn_readlane(ids, j - base);
         const bool bad = id < 0 || id >= num_blocks;
@@ -372,18 +381,18 @@ struct Chunk {
 };
 
 template <int BS>
-__device__ Chunk my_chunk(const DecodeArgs &a, int w, int W)
+__device__ Chunk my_chunk(const DecodeArgs &a, Lens lens, int w, int W)
 {
     const int S = a.num_seqs, Hkv = a.num_kv_heads;
     const int cap = a.max_nb * BS;
     uint32_t *flag = w == 0 ? a.err_flag : nullptr;
     if (S > 256) {
-        const int64_t U = total_units<BS>(a.seq_lens, S, Hkv, cap, flag);
+        const int64_t U = total_units<BS>(lens, S, Hkv, cap, flag);
         const int64_t cl = a.chunk_units > 0 ? a.chunk_units : (U + W - 1) / W;
         const int64_t u0 = (int64_t)w * cl;
         if (u0 >= U)
             return Chunk{0, 0, Cursor{}};
-        return Chunk{u0, (int)min(cl, U - u0), locate<BS>(a.seq_lens, S, Hkv, cap, u0)};
+        return Chunk{u0, (int)min(cl, U - u0), locate<BS>(lens, S, Hkv, cap, u0)};
     }
     const int lane = lane_id();
     int L[4], nb[4], incl[4], tot[4];
@@ -391,7 +400,7 @@ __device__ Chunk my_chunk(const DecodeArgs &a, int w, int W)
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int s = 64 * k + lane;
-        L[k] = (64 * k < S && s < S) ? a.seq_lens[s] : 0;
+        L[k] = (64 * k < S && s < S) ? lens[s] : 0;
     }
     int64_t U = 0;
 #pragma unroll

@@ -110,9 +110,12 @@ struct StepPrepArgs {
 // (kvh, split p, row block) attends the row block's rows to blocks
 // [p * bps, min(N, (p + 1) * bps)) of the shared prefix (row 0 of the block
 // table) and writes, per row, the partial (m, l, acc) to
-// p_acc/p_ml[(p * Hkv + kvh) * R + r].  The same launch writes the suffix
-// pass's batch (each sequence's table from block N on, its length less the
-// prefix) and checks the shared-prefix contract.
+// p_acc/p_ml[(p * Hkv + kvh) * R + r].
+//
+// Suffix pass: the single-query decode over the batch viewed from block N on
+// (tables from column N, lengths less N * bs), partials only.  Both passes and
+// check_wgs workgroups checking the shared-prefix contract run in one
+// launch: items first, then the check, then the decode's workgroups.
 struct CascadePrefixArgs {
     const void *q;                // [S, H, D] bf16
     const void *key_cache, *value_cache;
@@ -120,13 +123,11 @@ struct CascadePrefixArgs {
     const int32_t *seq_lens;      // [S]
     uint16_t *p_acc;              // [P, Hkv, R, D] bf16
     float *p_ml;                  // [P, Hkv, R, 2]
-    int32_t *s_tables;            // [S, max_nb - N]
-    int32_t *s_lens;              // [S]
     uint32_t *err_flag;
     int32_t num_seqs, num_heads, num_kv_heads, max_nb, num_blocks, block_size;
     int32_t prefix_blocks, num_splits, split_blocks;   // N, P, bps
     int32_t rows, row_blocks;                          // R, row blocks per KV head
-    int32_t num_items, items_per_xcd, log2_group;
+    int32_t num_items, items_per_xcd, log2_group, check_wgs;
     float qk_scale_log2, v_scale;
 };
 
@@ -136,7 +137,9 @@ struct CascadeMergeArgs {
     void *out;                    // [S, H, D]
     const uint16_t *s_acc;        // suffix partials (bf16 acc, f32 m and l)
     const float *s_ml;
-    const int32_t *s_seg, *s_lens;
+    const int32_t *s_seg;
+    const int32_t *seq_lens;      // [S]; a sequence's suffix is its tokens past N * bs
+    int32_t prefix_tokens, capacity;   // N * bs, max_nb * bs
     const uint16_t *p_acc;        // prefix partials
     const float *p_ml;
     int32_t num_seqs, num_heads, num_kv_heads, num_splits;
@@ -177,10 +180,17 @@ hipError_t decode_mfma_occupancy(int kv_type, int head_dim, int block_size, int 
 hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int block_size,
                         hipStream_t stream);
 
-hipError_t launch_cascade_prefix(const CascadePrefixArgs &a, int kv_type, int head_dim,
-                                 int block_size, hipStream_t stream);
+// Prefix pass, contract check and suffix pass (s: partials only, tables
+// starting at column N, lengths counted from token N * bs, s.max_nb = max_nb -
+// N, s.num_waves wavefronts) in one launch.
+hipError_t launch_cascade(const CascadePrefixArgs &p, const DecodeArgs &s, int kv_type,
+                          int head_dim, int block_size, int group, hipStream_t stream);
 // Rows of one prefix-pass workgroup.
 int cascade_prefix_rows();
+// Suffix-pass wavefronts per compute unit of the cascade kernel: those of the
+// workgroups a compute unit holds at once beside one prefix workgroup.
+hipError_t cascade_suffix_occupancy(int kv_type, int head_dim, int block_size, int group,
+                                    int *waves_per_cu);
 hipError_t launch_cascade_merge(const CascadeMergeArgs &a, int out_type, int head_dim,
                                 hipStream_t stream);
 
