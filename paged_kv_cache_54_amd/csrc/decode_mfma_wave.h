@@ -57,9 +57,10 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
     constexpr int HALVES = Geo::HALVES;
     constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
     static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group must divide 16");
-    // bf16: two register tiles in flight.  e4m3 (32-token tiles) keeps one,
-    // which holds its register use at two wavefronts per SIMD.
-    constexpr bool PINGPONG = KT == KT_BF16;
+    // bf16: two register tiles in flight.  e4m3: two with fixed-size chunks
+    // (short chunks, many rounds of wavefronts: the second tile shortens each
+    // chunk's start), one with balanced chunks (measured faster there).
+    const bool pingpong = KT == KT_BF16 || a.chunk_units > 0;
 
     const int lane = threadIdx.x & 63;
     const int g4 = lane >> 4;                  // 16-lane group
@@ -257,7 +258,7 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
 
     // Loads are issued unconditionally (a missing block reads nothing), so the
     // wait before staging a tile counts exactly the loads issued after it.
-    if constexpr (PINGPONG) {
+    if (pingpong) {
         // Two register tiles: tile k+1 is loaded into the other tile before
         // tile k is waited on, so two tiles are in flight at the wait.
         Tile ta, tb;
