@@ -502,7 +502,10 @@ def main():
     if cascade:
         used = "cascade"
     achieved = nbytes["decode"] / (kernel_ms * 1e-3) / 1e9
-    traffic = traffic_for(used, args.workload)
+    kname = KERNEL_NAMES[used]
+    if multi and b.group_size * b.max_query_len > 16:
+        kname = "decode_mfma_multi_coop_kernel"     # more than one 16-column tile
+    traffic = traffic_for(used, args.workload, kname)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -528,7 +531,7 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "decode_seqs_per_s": round(b.num_seqs / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": nbytes["step"],
-        "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[used],
+        "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
