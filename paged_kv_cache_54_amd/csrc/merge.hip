@@ -62,20 +62,26 @@ __device__ __forceinline__ void lse_fold(Lse &s, const Lse &t)
     s.o.w = s.o.w * a + t.o.w * b;
 }
 
+// WPR wavefronts per row, or (WPR = 0) two rows per wavefront, one per
+// 32-lane half.
 template <int OT, int D, int WPR>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int block_size,
                                                                int64_t num_rows)
 {
     constexpr int LPP = D / 4;                   // lanes per partial row (4 floats each)
-    constexpr int PPW = 64 / LPP;                // partials per wavefront pass
+    constexpr int RW = WPR == 0 ? 2 : 1;         // rows per wavefront
+    constexpr int LPR = 64 / RW;                 // lanes per row
+    constexpr int PPW = LPR / LPP;               // partials per wavefront pass
     constexpr int UNROLL = 4;
-    constexpr int RPW = 4 / WPR;                 // rows per workgroup
+    constexpr int RPW = WPR == 0 ? 8 : 4 / WPR;  // rows per workgroup
     __shared__ Lse part[4][LPP];
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int sub = lane / LPP, col = (lane % LPP) * 4;
-    const int wr = wave % WPR;                   // wavefront within its row
-    const int64_t r = (int64_t)blockIdx.x * RPW + wave / WPR;
+    const int half = lane / LPR, hl = lane % LPR;
+    const int sub = hl / LPP, col = (hl % LPP) * 4;
+    const int wr = WPR > 1 ? wave % WPR : 0;     // wavefront within its row
+    const int64_t r =
+        (int64_t)blockIdx.x * RPW + (WPR == 0 ? 2 * wave + half : wave / (WPR > 0 ? WPR : 1));
     const int H = a.num_heads, G = a.num_heads / a.num_kv_heads;
     const int RPS = a.rows_per_slot;
 
@@ -83,14 +89,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
     // per sequence -- grid row s * H + h, partial row h % G; several -- grid
     // row (s * max_query_len + i) * H + h for query token i, partial row
     // i * G + h % G (absent when the sequence has at most i tokens).
+    // The segment record is read with the length (and the query span), not
+    // after it: the three loads are independent, so a row waits for one
+    // memory latency before its partials instead of two.  A sequence with no
+    // tokens has no record this call; its stale one is read and not used.
     bool live = r < num_rows;
     int s = 0, h = 0, prow = 0, L = 0, first = 0, n = 0;
     int64_t row = 0;
+    int2 rec = make_int2(0, 0);
     if (live) {
         if (a.query_start_loc) {
             h = (int)(r % H);
             const int i = (int)((r / H) % a.max_query_len);
             s = (int)(r / ((int64_t)H * a.max_query_len));
+            rec = *reinterpret_cast<const int2 *>(a.ws_seg + 2 * (s * a.num_kv_heads + h / G));
             L = min(a.seq_lens[s], a.max_nb * block_size);
             int qs, ql;
             query_span(a, s, max(L, 0), &qs, &ql, nullptr);
@@ -101,17 +113,16 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
             row = r;
             s = (int)(r / H);
             h = (int)(r % H);
+            rec = *reinterpret_cast<const int2 *>(a.ws_seg + 2 * (s * a.num_kv_heads + h / G));
             L = min(a.seq_lens[s], a.max_nb * block_size);
             prow = h % G;
         }
     }
     bool zero_row = live && L <= 0;
     if (live && L > 0) {
-        const int g = s * a.num_kv_heads + h / G;
-        first = a.ws_seg[2 * g];
-        const int last = a.ws_seg[2 * g + 1];
-        live = first != last;                    // else one chunk wrote the output
-        n = last - first + 1;
+        first = rec.x;
+        live = first != rec.y;                   // else one chunk wrote the output
+        n = rec.y - first + 1;
     }
 
     Lse st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
@@ -120,7 +131,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
         const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (int64_t)first * RPS + prow;
         using AT = typename std::conditional<OT == KT_F32, float, uint16_t>::type;
         const AT *acc = static_cast<const AT *>(a.ws_acc) + ((int64_t)first * RPS + prow) * D + col;
-        const int stride = WPR * PPW;
+        const int stride = (WPR > 1 ? WPR : 1) * PPW;
         for (int p0 = wr * PPW + sub; p0 < n; p0 += UNROLL * stride) {
             float2 mlv[UNROLL];
             float4 x[UNROLL];
@@ -146,9 +157,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(DecodeArgs a, int 
                     lse_add(st, mlv[u].x, mlv[u].y, x[u]);
         }
     }
-    // lane groups of the wavefront hold the same columns for different parts
+    // lane groups of the row hold the same columns for different parts
 #pragma unroll
-    for (int off = LPP; off < 64; off <<= 1) {
+    for (int off = LPP; off < LPR; off <<= 1) {
         Lse t;
         t.M = __shfl_xor(st.M, off);
         t.den = __shfl_xor(st.den, off);
@@ -189,13 +200,17 @@ hipError_t launch(const DecodeArgs &a, int block_size, int64_t rows, hipStream_t
 {
     // Few rows: their sequences are long and cut into many parts; give each
     // row a whole workgroup.
-    const bool wide = rows < 2048;
-    const int64_t wgs = wide ? rows : (rows + 3) / 4;
+    // Many rows (several query tokens per sequence): two rows per wavefront,
+    // so every row's loads are in flight in one round of wavefronts.
+    const bool wide = rows < 2048, packed = rows >= 8192;
+    const int64_t wgs = wide ? rows : packed ? (rows + 7) / 8 : (rows + 3) / 4;
     if (wgs > INT32_MAX)
         return hipErrorInvalidValue;
     dim3 grid((unsigned)wgs), block(kMergeThreads);
     if (wide)
         hipLaunchKernelGGL((merge_kernel<OT, D, 4>), grid, block, 0, stream, a, block_size, rows);
+    else if (packed)
+        hipLaunchKernelGGL((merge_kernel<OT, D, 0>), grid, block, 0, stream, a, block_size, rows);
     else
         hipLaunchKernelGGL((merge_kernel<OT, D, 1>), grid, block, 0, stream, a, block_size, rows);
     return hipGetLastError();
