@@ -435,17 +435,20 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(CascadeMergeArg
         return;
     const int s = (int)(r / H), h = (int)(r % H), kvh = h / G;
 
+    // The length and the suffix's segment record are loaded together, and the
+    // prefix parts (which need neither) are folded in first, so their loads
+    // overlap those two.  A sequence with no own tokens has no record this
+    // call; its stale one is read and not used.
+    const int2 rec = *reinterpret_cast<const int2 *>(a.s_seg + 2 * (s * Hkv + kvh));
+    const int L = a.seq_lens[s];
     Lse st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
-    if (min(a.seq_lens[s], a.capacity) > a.prefix_tokens) {   // the sequence's own blocks
-        const int g = s * Hkv + kvh;
-        add_parts<D>(st, a.s_acc, a.s_ml, a.s_seg[2 * g], a.s_seg[2 * g + 1], G, h % G, col,
-                     sub, PPW);
-    }
     {                                            // the shared prefix: one part per split
         const int64_t R = (int64_t)a.num_seqs * G;
         add_parts<D>(st, a.p_acc, a.p_ml, 0, a.num_splits - 1, Hkv * R,
                      kvh * R + (int64_t)s * G + h % G, col, sub, PPW);
     }
+    if (min(L, a.capacity) > a.prefix_tokens)    // the sequence's own blocks
+        add_parts<D>(st, a.s_acc, a.s_ml, rec.x, rec.y, G, h % G, col, sub, PPW);
 #pragma unroll
     for (int off = LPP; off < 64; off <<= 1) {
         Lse t;
