@@ -222,7 +222,9 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
         p->chunk_units = P / p->bs;
         p->waves = max_units > 0 ? (max_units + p->chunk_units - 1) / p->chunk_units : 1;
     } else {
-        // balanced: one chunk per wavefront the device holds at once
+        // balanced: one chunk per wavefront the device holds at once, but no
+        // more wavefronts than the largest batch of these shapes has units
+        // (a small batch then launches only the wavefronts it can use)
         p->chunk_units = 0;
         p->waves = 1;
         if (p->S > 0) {
@@ -230,6 +232,8 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
             if ((rc = device_cu_count(&cus)) || (rc = resident_waves_per_cu(*p, &per_cu)))
                 return rc;
             p->waves = (int64_t)cus * per_cu;
+            if (max_units > 0 && max_units < p->waves)
+                p->waves = max_units;
         }
     }
     if (p->waves > INT32_MAX / 2 || p->chunk_units > INT32_MAX)
@@ -466,6 +470,9 @@ int plan_cascade(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt, i
         if ((rc = device_cu_count(&cus)) || (rc = resident_waves_per_cu(c->suf, &per_cu, true)))
             return rc;
         c->suf.waves = (int64_t)cus * per_cu;
+        const int64_t max_units = c->suf.S * c->suf.Hkv * c->suf.max_nb;
+        if (max_units > 0 && max_units < c->suf.waves)
+            c->suf.waves = max_units;
         c->suf.slots = c->suf.waves + c->suf.S * c->suf.Hkv;
         c->suf.ws_bytes = workspace_bytes(c->suf);
     }

@@ -122,3 +122,26 @@ def test_segments_split_into_many_parts(variant):
                   variant=variant, partition_tokens=P)
         torch.cuda.synchronize()
         check_close(out, ref, "bf16", f"many parts v{variant} P{P}")
+
+
+@pytest.mark.parametrize("variant", [pa.VARIANT_VALU, pa.VARIANT_MFMA])
+def test_small_batch_launches_one_wavefront_per_unit(variant):
+    """A batch whose largest possible work list (S * Hkv * max_nb blocks) is
+    shorter than the device's resident wavefronts gets one wavefront per
+    block, not a full device of mostly idle ones: its workspace is that of
+    one-block chunks, and the result still matches the oracle."""
+    b = workloads.make_batch("llama3_8b_bf16", device=DEV, num_seqs=3, num_heads=8,
+                             num_kv_heads=2, head_dim=128, block_size=16,
+                             lens=("uniform", 1, 90), max_len=96, seed=57)
+    kc, vc = gpu_caches(b)
+    units = b.num_seqs * b.num_kv_heads * b.block_tables.shape[1]
+    G = b.num_heads // b.num_kv_heads
+    slots = units + b.num_seqs * b.num_kv_heads
+    acc = 4 if b.q_dtype == "f32" else 2          # partials in the output type
+    want = acc * slots * G * b.head_dim + 8 * slots * G + 8 * b.num_seqs * b.num_kv_heads
+    assert pa.decode_workspace_size(b.q, kc, b.block_tables, variant=variant) == want
+    print("CASE small batch", variant, flush=True)
+    ref, _, _ = oracle_step(b)
+    out = gpu_step(b, kc, vc, variant=variant)
+    torch.cuda.synchronize()
+    check_close(out, ref, b.cache_dtype, f"small batch variant {variant}")
