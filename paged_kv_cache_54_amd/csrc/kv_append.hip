@@ -16,15 +16,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Store one loaded 8-element chunk at element d of the cache (quantised to
+// e4m3 with the inverse scale `inv` for an fp8 cache, else copied).
 template <int IT, int CT>
-__device__ __forceinline__ void move8(const void *src, int64_t s, void *dst, int64_t d, float inv)
+__device__ __forceinline__ void store8(const Raw8<IT> &r, void *dst, int64_t d, float inv)
 {
     if constexpr (CT == KT_E4M3) {
         float x[8];
-        if constexpr (IT == KT_F32)
-            unpack8(load_raw8<KT_F32>(src, s), x);
-        else
-            unpack8(load_raw8<KT_BF16>(src, s), x);
+        unpack8(r, x);
         uint2 w;
         w.x = w.y = 0;
 #pragma unroll
@@ -34,13 +33,11 @@ __device__ __forceinline__ void move8(const void *src, int64_t s, void *dst, int
         }
         *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(dst) + d) = w;
     } else if constexpr (CT == KT_F32) {
-        const Raw8<KT_F32> r = load_raw8<KT_F32>(src, s);
         uint4 *p = reinterpret_cast<uint4 *>(static_cast<float *>(dst) + d);
         p[0] = r.a;
         p[1] = r.b;
     } else {
-        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(dst) + d) =
-            load_raw8<KT_BF16>(src, s).a;
+        *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(dst) + d) = r.a;
     }
 }
 
@@ -52,6 +49,11 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a)
     if (idx >= a.num_tokens * chunks)
         return;
     const int64_t t = idx / chunks, c = idx - t * chunks;
+    // The rows are read before the slot is known: the three loads do not
+    // depend on each other, so they share one memory latency.
+    const int64_t s = t * a.row_elems + c * 8;
+    const Raw8<IT> k = load_raw8<IT>(a.k, s);
+    const Raw8<IT> v = load_raw8<IT>(a.v, s);
     const int64_t slot = a.slots[t];
     if (slot < 0)
         return;                                  // padding token
@@ -60,10 +62,9 @@ __global__ __launch_bounds__(kThreads) void kv_append_kernel(AppendArgs a)
             raise_flag(a.err_flag, PA_DEVERR_SLOT);
         return;
     }
-    const int64_t s = t * a.row_elems + c * 8;
     const int64_t d = slot * a.row_elems + c * 8;
-    move8<IT, CT>(a.k, s, a.key_cache, d, a.k_inv_scale);
-    move8<IT, CT>(a.v, s, a.value_cache, d, a.v_inv_scale);
+    store8<IT, CT>(k, a.key_cache, d, a.k_inv_scale);
+    store8<IT, CT>(v, a.value_cache, d, a.v_inv_scale);
 }
 
 }  // namespace
