@@ -30,37 +30,16 @@
 namespace pa {
 namespace {
 
+// One wavefront's NT column tiles of a segment, columns col0 .. col0 + 16 NT
+// - 1: per tile the Q^T operand, accumulators, running max and lane-partial
+// sum, the causal bound and the output row; and the three steps both kernels
+// apply to them (start a segment, attend a staged tile, write the result).
 template <int KT, int D, int BS, int NT>
-__global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
-{
+struct MultiCols {
     using Geo = MfmaGeo<KT, D, BS>;
-    constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
-    constexpr int HALVES = Geo::HALVES;
-    constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
+    static constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
+    static constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
 
-    __shared__ __attribute__((aligned(16))) uint8_t kt[TILE * KROWB];
-    __shared__ __attribute__((aligned(16))) uint8_t vt[TILE * VROWB];
-
-    const int lane = threadIdx.x;
-    const int g4 = lane >> 4;                  // 16-lane group
-    const int c16 = lane & 15;                 // token row (K operand) / column (output)
-    const int H = a.num_heads, Hkv = a.num_kv_heads;
-    const int G = H / Hkv, lg = a.log2_group;  // G = 2^lg
-    const int RPS = a.rows_per_slot;           // partial rows per slot: G * max_query_len
-    const int cap = a.max_nb * BS;
-    const int w = blockIdx.x;
-
-    const Lens lens{a.seq_lens, 0};
-    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
-    if (chunk.n == 0)
-        return;
-
-    const MfmaLoader<Geo> loader(a, lane);
-    using Tile = MfmaTile<Geo>;
-    auto load_tile = [&](int id, int kvh, int half, Tile &t) { loader.load(id, kvh, half, t); };
-
-    // per-segment state, per column tile: Q^T operand, accumulators, running
-    // max and lane-partial sum, the causal bound and the output row
     bf16x8 qop[NT][NC];
     f32x4 acc[NT][ND];
     float m[NT], l[NT];
@@ -68,16 +47,25 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
     int64_t orow[NT];                          // (token * H + head), -1 = unused column
     int full_end = 0;                          // tiles ending by here need no mask
     bool seg_starts = false;
+    const int col0, g4, c16;
 
-    auto begin_segment = [&](const Cursor &c) {
+    __device__ __forceinline__ MultiCols(int col0_, int lane)
+        : col0(col0_), g4(lane >> 4), c16(lane & 15)
+    {
+    }
+
+    // Load the segment's query columns; `flag` (if set) takes layout errors.
+    __device__ __forceinline__ void begin(const DecodeArgs &a, const Cursor &c, uint32_t *flag)
+    {
+        const int H = a.num_heads, G = H / a.num_kv_heads, lg = a.log2_group;
         int qs, ql;
-        query_span(a, c.s, c.L, &qs, &ql, c.kvh == 0 && lane == 0 ? a.err_flag : nullptr);
+        query_span(a, c.s, c.L, &qs, &ql, flag);
         qs = __builtin_amdgcn_readfirstlane(qs);
         ql = __builtin_amdgcn_readfirstlane(ql);
         full_end = c.L - ql + 1;               // the first query token's bound, the smallest
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int col = 16 * nt + c16;
+            const int col = col0 + 16 * nt + c16;
             const int i = col >> lg, g = col & (G - 1);
             const bool valid = i < ql;
             lim[nt] = valid ? c.L - ql + i + 1 : 0;
@@ -95,15 +83,16 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
             l[nt] = 0.f;
         }
         seg_starts = c.j == 0;
-    };
+    }
 
-    auto finish_segment = [&](const Cursor &c, bool ends) {
-        const int g = c.s * Hkv + c.kvh;
-        const int slot = w + g;
-        record_segment(a, g, slot, seg_starts, ends);
+    // The segment's result: the output rows when this chunk covered the whole
+    // segment, else a partial in slot `slot`.
+    __device__ __forceinline__ void finish(const DecodeArgs &a, int slot, bool ends)
+    {
+        const int RPS = a.rows_per_slot;       // partial rows per slot: G * max_query_len
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const float lt = rows_sum(l[nt]);            // sum the four 16-lane groups
+            const float lt = rows_sum(l[nt]);  // sum the four 16-lane groups
             if (orow[nt] < 0)
                 continue;
             if (seg_starts && ends && !(a.flags & kPartialOnly)) {
@@ -115,7 +104,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
                         make_uint2(pack_bf16x2(acc[nt][d][0] * inv, acc[nt][d][1] * inv),
                                    pack_bf16x2(acc[nt][d][2] * inv, acc[nt][d][3] * inv));
             } else {
-                const int64_t pi = (int64_t)slot * RPS + 16 * nt + c16;
+                const int64_t pi = (int64_t)slot * RPS + col0 + 16 * nt + c16;
                 uint16_t *o = static_cast<uint16_t *>(a.ws_acc) + pi * D + 4 * g4;
 #pragma unroll
                 for (int d = 0; d < ND; ++d)
@@ -126,14 +115,14 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
                     *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m[nt], lt);
             }
         }
-    };
+    }
 
-    auto stage = [&](const Cursor &c, int half, const Tile &t) {
-        stage_tile<Geo>(loader, kt, vt, t, c.j * BS + half * TILE, c.L);
-    };
-
-    // QK^T for every column tile, online softmax per column, PV.
-    auto process = [&](const Cursor &c, int half) {
+    // QK^T for every column tile from the staged K tile, online softmax per
+    // column, PV from the staged V tile (each LDS operand read once for all
+    // NT tiles).
+    __device__ __forceinline__ void process(const DecodeArgs &a, const Cursor &c, int half,
+                                            const uint8_t *kt, const uint8_t *vt)
+    {
         const int tok_base = c.j * BS + half * TILE;
         const bool full = tok_base + TILE <= full_end;   // every column sees the whole tile
         f32x4 sc[MT][NT];
@@ -208,7 +197,31 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
                         as_bf16x4(raw), pop[h][nt], acc[nt][d], 0, 0, 0);
             }
         }
-    };
+    }
+};
+
+// One wavefront per chunk, all NT column tiles.
+template <int KT, int D, int BS, int NT>
+__global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
+{
+    using Geo = MfmaGeo<KT, D, BS>;
+    constexpr int TILE = Geo::TILE, HALVES = Geo::HALVES;
+    __shared__ __attribute__((aligned(16))) uint8_t kt[TILE * Geo::KROWB];
+    __shared__ __attribute__((aligned(16))) uint8_t vt[TILE * Geo::VROWB];
+
+    const int lane = threadIdx.x;
+    const int Hkv = a.num_kv_heads;
+    const int cap = a.max_nb * BS;
+    const int w = blockIdx.x;
+
+    const Lens lens{a.seq_lens, 0};
+    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
+    if (chunk.n == 0)
+        return;
+
+    const MfmaLoader<Geo> loader(a, lane);
+    using Tile = MfmaTile<Geo>;
+    MultiCols<KT, D, BS, NT> cols(0, lane);
 
     // Walk the chunk tile by tile with one register tile in flight: tile k is
     // staged into LDS, then the loads of tile k+1 are issued into the same
@@ -235,22 +248,25 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
 
     Tile t;
     int id = l_id, half = l_half;
-    load_tile(id, lc.kvh, half, t);
+    loader.load(id, lc.kvh, half, t);
     for (int k = 0; k < steps; ++k) {
         const int unit = k / HALVES;
         if (half == 0 && (unit == 0 || cc.j == 0))
-            begin_segment(cc);
+            cols.begin(a, cc, cc.kvh == 0 && lane == 0 ? a.err_flag : nullptr);
         if (id >= 0)
-            stage(cc, half, t);
+            stage_tile<Geo>(loader, kt, vt, t, cc.j * BS + half * TILE, cc.L);
         next_load(k + 1);
         const int id_next = l_id, half_next = l_half;
-        load_tile(id_next, lc.kvh, half_next, t);
+        loader.load(id_next, lc.kvh, half_next, t);
         if (id >= 0)
-            process(cc, half);
+            cols.process(a, cc, half, kt, vt);
         if (half == HALVES - 1) {
             const bool ends = cc.j == cc.nb - 1;
-            if (ends || unit == n - 1)
-                finish_segment(cc, ends);
+            if (ends || unit == n - 1) {
+                const int g = cc.s * Hkv + cc.kvh;
+                record_segment(a, g, w + g, cols.seg_starts, ends);
+                cols.finish(a, w + g, ends);
+            }
             if (unit + 1 < n)
                 advance<BS>(cc, lens, Hkv, cap);
         }
@@ -258,7 +274,6 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
         half = half_next;
     }
 }
-
 
 // Two wavefronts per chunk: the workgroup's wavefronts walk the same chunk,
 // wavefront 0 loading each tile's K rows and wavefront 1 its V rows into a
@@ -272,8 +287,7 @@ template <int KT, int D, int BS, int NTW, int DEPTH>
 __global__ __launch_bounds__(64 * kCoopWaves) void decode_mfma_multi_coop_kernel(DecodeArgs a)
 {
     using Geo = MfmaGeo<KT, D, BS>;
-    constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
-    constexpr int HALVES = Geo::HALVES, NLOAD = Geo::NLOAD;
+    constexpr int TILE = Geo::TILE, HALVES = Geo::HALVES, NLOAD = Geo::NLOAD;
     constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
 
     __shared__ __attribute__((aligned(16))) uint8_t kt_all[2][TILE * KROWB];
@@ -281,11 +295,7 @@ __global__ __launch_bounds__(64 * kCoopWaves) void decode_mfma_multi_coop_kernel
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int g4 = lane >> 4;
-    const int c16 = lane & 15;
-    const int H = a.num_heads, Hkv = a.num_kv_heads;
-    const int G = H / Hkv, lg = a.log2_group;
-    const int RPS = a.rows_per_slot;
+    const int Hkv = a.num_kv_heads;
     const int cap = a.max_nb * BS;
     const int w = blockIdx.x;
 
@@ -311,6 +321,7 @@ __global__ __launch_bounds__(64 * kCoopWaves) void decode_mfma_multi_coop_kernel
         for (int i = 0; i < NLOAD; ++i)
             p.v[i] = buf_load16(r, voff, soff + i * Geo::LROWS * slot_bytes);
     };
+    // K rows as they are; V rows at or past the sequence end as zeros
     auto stage_part = [&](const Part &p, int buf, int tok_base, int t1) {
         const bool mask = wave == 1 && tok_base + TILE > t1;
         uint8_t *tile = wave == 0 ? kt_all[buf] : vt_all[buf];
@@ -333,149 +344,7 @@ __global__ __launch_bounds__(64 * kCoopWaves) void decode_mfma_multi_coop_kernel
         }
     };
 
-    bf16x8 qop[NTW][NC];
-    f32x4 acc[NTW][ND];
-    float m[NTW], l[NTW];
-    int lim[NTW];
-    int64_t orow[NTW];
-    int full_end = 0;
-    bool seg_starts = false;
-
-    auto begin_segment = [&](const Cursor &c) {
-        int qs, ql;
-        query_span(a, c.s, c.L, &qs, &ql,
-                   c.kvh == 0 && lane == 0 && wave == 0 ? a.err_flag : nullptr);
-        qs = __builtin_amdgcn_readfirstlane(qs);
-        ql = __builtin_amdgcn_readfirstlane(ql);
-        full_end = c.L - ql + 1;
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            const int col = 16 * (nt + NTW * wave) + c16;
-            const int i = col >> lg, g = col & (G - 1);
-            const bool valid = i < ql;
-            lim[nt] = valid ? c.L - ql + i + 1 : 0;
-            orow[nt] = valid ? (int64_t)(qs + i) * H + c.kvh * G + g : -1;
-            const uint16_t *qrow =
-                static_cast<const uint16_t *>(a.q) + (valid ? orow[nt] : 0) * D + 8 * g4;
-#pragma unroll
-            for (int k = 0; k < NC; ++k)
-                qop[nt][k] = valid ? as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * k))
-                                   : as_bf16x8(make_uint4(0, 0, 0, 0));
-#pragma unroll
-            for (int d = 0; d < ND; ++d)
-                acc[nt][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-            m[nt] = -INFINITY;
-            l[nt] = 0.f;
-        }
-        seg_starts = c.j == 0;
-    };
-
-    auto finish_segment = [&](const Cursor &c, bool ends) {
-        const int g = c.s * Hkv + c.kvh;
-        const int slot = w + g;
-        if (wave == 0)
-            record_segment(a, g, slot, seg_starts, ends);
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            const float lt = rows_sum(l[nt]);
-            if (orow[nt] < 0)
-                continue;
-            if (seg_starts && ends && !(a.flags & kPartialOnly)) {
-                const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
-                uint16_t *o = static_cast<uint16_t *>(a.out) + orow[nt] * D + 4 * g4;
-#pragma unroll
-                for (int d = 0; d < ND; ++d)
-                    *reinterpret_cast<uint2 *>(o + 16 * d) =
-                        make_uint2(pack_bf16x2(acc[nt][d][0] * inv, acc[nt][d][1] * inv),
-                                   pack_bf16x2(acc[nt][d][2] * inv, acc[nt][d][3] * inv));
-            } else {
-                const int64_t pi = (int64_t)slot * RPS + 16 * (nt + NTW * wave) + c16;
-                uint16_t *o = static_cast<uint16_t *>(a.ws_acc) + pi * D + 4 * g4;
-#pragma unroll
-                for (int d = 0; d < ND; ++d)
-                    *reinterpret_cast<uint2 *>(o + 16 * d) = make_uint2(
-                        pack_bf16x2(acc[nt][d][0] * a.v_scale, acc[nt][d][1] * a.v_scale),
-                        pack_bf16x2(acc[nt][d][2] * a.v_scale, acc[nt][d][3] * a.v_scale));
-                if (g4 == 0)
-                    *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m[nt], lt);
-            }
-        }
-    };
-
-    auto process = [&](const Cursor &c, int half, int buf) {
-        const uint8_t *kt = kt_all[buf];
-        const uint8_t *vt = vt_all[buf];
-        const int tok_base = c.j * BS + half * TILE;
-        const bool full = tok_base + TILE <= full_end;
-        f32x4 sc[MT][NTW];
-#pragma unroll
-        for (int h = 0; h < MT; ++h) {
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-                sc[h][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint8_t *krow = kt + (16 * h + c16) * KROWB + 16 * g4;
-#pragma unroll
-            for (int k = 0; k < NC; ++k) {
-                const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4 *>(krow + 64 * k));
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    sc[h][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop, qop[nt][k],
-                                                                      sc[h][nt], 0, 0, 0);
-            }
-        }
-        bf16x4 pop[MT][NTW];
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            float bm = -INFINITY;
-#pragma unroll
-            for (int h = 0; h < MT; ++h)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = sc[h][nt][i] * a.qk_scale_log2;
-                    if (!full)
-                        v = tok_base + 16 * h + 4 * g4 + i < lim[nt] ? v : -INFINITY;
-                    sc[h][nt][i] = v;
-                    bm = fmaxf(bm, v);
-                }
-            const float tm = rows_max(bm);
-            if (__ballot(tm > m[nt] + kRebase)) {
-                const float mn = fmaxf(m[nt], tm);
-                const float alpha = (mn > m[nt]) ? __builtin_amdgcn_exp2f(m[nt] - mn) : 1.f;
-                l[nt] *= alpha;
-#pragma unroll
-                for (int d = 0; d < ND; ++d)
-                    acc[nt][d] *= alpha;
-                m[nt] = mn;
-            }
-#pragma unroll
-            for (int h = 0; h < MT; ++h) {
-                float p[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    p[i] = (!full && sc[h][nt][i] == -INFINITY)
-                               ? 0.f
-                               : __builtin_amdgcn_exp2f(sc[h][nt][i] - m[nt]);
-                    l[nt] += p[i];
-                }
-                pop[h][nt] = __builtin_bit_cast(
-                    bf16x4, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < MT; ++h) {
-            const int row = 16 * h + 4 * g4 + (c16 >> 2);
-#pragma unroll
-            for (int d = 0; d < ND; ++d) {
-                const int addr = row * VROWB + 32 * d + 8 * (c16 & 3);
-                const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)((__attribute__((address_space(3))) uint8_t *)vt + addr));
-#pragma unroll
-                for (int nt = 0; nt < NTW; ++nt)
-                    acc[nt][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                        as_bf16x4(raw), pop[h][nt], acc[nt][d], 0, 0, 0);
-            }
-        }
-    };
+    MultiCols<KT, D, BS, NTW> cols(16 * NTW * wave, lane);
 
     // Both wavefronts walk the same cursors, so every branch below and the
     // barrier are uniform over the workgroup.
@@ -517,7 +386,7 @@ __global__ __launch_bounds__(64 * kCoopWaves) void decode_mfma_multi_coop_kernel
             const int unit = k / HALVES;
             const int half = phalf[d], id = pid[d];
             if (half == 0 && (unit == 0 || cc.j == 0))
-                begin_segment(cc);
+                cols.begin(a, cc, cc.kvh == 0 && lane == 0 && wave == 0 ? a.err_flag : nullptr);
             if (id >= 0)
                 stage_part(pf[d], k & 1, cc.j * BS + half * TILE, cc.L);
             __syncthreads();
@@ -526,11 +395,15 @@ __global__ __launch_bounds__(64 * kCoopWaves) void decode_mfma_multi_coop_kernel
             phalf[d] = l_half;
             load_part(l_id, lc.kvh, l_half, pf[d]);
             if (id >= 0)
-                process(cc, half, k & 1);
+                cols.process(a, cc, half, kt_all[k & 1], vt_all[k & 1]);
             if (half == HALVES - 1) {
                 const bool ends = cc.j == cc.nb - 1;
-                if (ends || unit == n - 1)
-                    finish_segment(cc, ends);
+                if (ends || unit == n - 1) {
+                    const int g = cc.s * Hkv + cc.kvh;
+                    if (wave == 0)
+                        record_segment(a, g, w + g, cols.seg_starts, ends);
+                    cols.finish(a, w + g, ends);
+                }
                 if (unit + 1 < n)
                     advance<BS>(cc, lens, Hkv, cap);
             }
@@ -539,6 +412,15 @@ __global__ __launch_bounds__(64 * kCoopWaves) void decode_mfma_multi_coop_kernel
 }
 
 typedef void (*DecodeKernel)(DecodeArgs);
+
+// Tiles in flight with four column tiles (two per wavefront): three, except
+// for e4m3 32-token tiles, where three would take more than 256 registers
+// (one wavefront per SIMD) and two keep two.
+template <int KT, int BS>
+constexpr int coop_depth4()
+{
+    return (KT == KT_E4M3 && BS == 32) ? 2 : 3;
+}
 
 // Threads of a chunk's workgroup for nt column tiles.
 int threads_for(int nt) { return nt >= 2 ? 64 * kCoopWaves : 64; }
@@ -549,7 +431,7 @@ DecodeKernel pick_nt(int nt)
     switch (nt) {
     case 1: return decode_mfma_multi_kernel<KT, D, BS, 1>;
     case 2: return decode_mfma_multi_coop_kernel<KT, D, BS, 1, 3>;
-    case 4: return decode_mfma_multi_coop_kernel<KT, D, BS, 2, 3>;
+    case 4: return decode_mfma_multi_coop_kernel<KT, D, BS, 2, coop_depth4<KT, BS>()>;
     default: return nullptr;
     }
 }
