@@ -390,7 +390,7 @@ def bench_prep(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU only; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     import torch
 

@@ -1,6 +1,6 @@
 """Compile the C oracle into oracle/liboracle.so with gcc.
 
-Test infrastructure: building the checker is not using it.  Run directly
+Test infrastructure: compiling the oracle does not put it on the product path.  Run directly
 (``python oracle/build.py``) or through ``__graft_entry__.build()``.
 """
 import os
