@@ -256,7 +256,7 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
         }
     };
 
-    // Loads are issued unconditionally (a missing block reads nothing), so the
+    // Loads are issued unconditionally (a missing block reads block 0), so the
     // wait before staging a tile counts exactly the loads issued after it.
     if (pingpong) {
         // Two register tiles: tile k+1 is loaded into the other tile before
