@@ -194,16 +194,38 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
         }
 
         // O^T += V^T P^T, V^T read transposed from LDS
-#pragma unroll
-        for (int h = 0; h < MT; ++h) {
-            const int row = 16 * h + 4 * g4 + (c16 >> 2);
+        if constexpr (MT == 2) {
+            // A 32-token tile in one K = 32 product per 16 dimensions: the
+            // sum over tokens takes them in the order lane group g4 holds
+            // them, tokens 4*g4 .. 4*g4+3 of each 16-token half, in P and in
+            // the two transposed V reads alike.
+            const bf16x8 pp = __builtin_shufflevector(pop[0], pop[1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
-                const int addr = row * VROWB + 32 * d + 8 * (c16 & 3);
-                const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)((__attribute__((address_space(3))) uint8_t *)vt + addr));
-                acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(raw), pop[h],
-                                                                 acc[d], 0, 0, 0);
+                s16x4 raw[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int row = 16 * h + 4 * g4 + (c16 >> 2);
+                    raw[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4 *)((__attribute__((address_space(3))) uint8_t *)vt +
+                                      row * VROWB + 32 * d + 8 * (c16 & 3)));
+                }
+                const bf16x8 vv = __builtin_shufflevector(as_bf16x4(raw[0]), as_bf16x4(raw[1]), 0,
+                                                          1, 2, 3, 4, 5, 6, 7);
+                acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, pp, acc[d], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < MT; ++h) {
+                const int row = 16 * h + 4 * g4 + (c16 >> 2);
+#pragma unroll
+                for (int d = 0; d < ND; ++d) {
+                    const int addr = row * VROWB + 32 * d + 8 * (c16 & 3);
+                    const s16x4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4 *)((__attribute__((address_space(3))) uint8_t *)vt + addr));
+                    acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(raw), pop[h],
+                                                                     acc[d], 0, 0, 0);
+                }
             }
         }
     };
