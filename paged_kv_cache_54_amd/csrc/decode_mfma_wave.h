@@ -9,11 +9,12 @@
 // selection masking and the partial/merge contract are also the same; what
 // differs is how one block of one KV head is processed by a wavefront:
 //
-//   loads K and V arrive in 16-token tiles (a 32-token block is two tiles)
-//         through 16-byte row-contiguous buffer loads (a
-//         wavefront instruction reads whole 256-byte rows; reading K directly
-//         in MFMA operand order -- 16 rows x 64 bytes per instruction --
-//         measured 15-20 % slower) and are stored to LDS as bf16 rows.
+//   loads K and V arrive in tiles of 8 KB per KV head (16 bf16 tokens, a
+//         32-token bf16 block being two tiles, or 32 e4m3 tokens) through
+//         16-byte row-contiguous nontemporal loads (a wavefront instruction
+//         reads whole 256-byte rows; reading K directly in MFMA operand
+//         order -- 16 rows x 64 bytes per instruction -- measured 15-20 %
+//         slower) and are stored to LDS as bf16 rows.
 //   QK^T  v_mfma_f32_16x16x32_bf16, A = K tile (M = 16 tokens, K = 32 dims)
 //         read from LDS, B = Q^T (N = 16 columns; column n is query head
 //         n mod G of the group).  Lane l gets S[token 4*(l/16)+i][column l%16]
@@ -24,7 +25,8 @@
 //   PV    v_mfma_f32_16x16x16bf16_1k computing O^T = V^T P^T: B = P^T is
 //         exactly the QK accumulator layout (converted to bf16), A = V^T is
 //         read from LDS with ds_read_b64_tr_b16, which transposes 16-bit
-//         elements within each 16-lane group.
+//         elements within each 16-lane group.  A 32-token tile takes one
+//         v_mfma_f32_16x16x32_bf16 per 16 dimensions instead of two.
 //
 // An e4m3 cache is converted to bf16 (exact) in registers before K and V are
 // stored to LDS; k_scale is folded into the score scale
