@@ -1,0 +1,96 @@
+"""Calls on two streams at once: the library keeps no device state between
+calls (each call owns its workspace and error word), so two batches queued on
+two streams, interleaved, give the same bits as the same calls made one after
+the other on one stream.  Covers decode (both kernel families), the
+multi-token decode and the cascade."""
+import pytest
+import torch
+
+import paged_kv_cache_54_amd as pa
+import workloads
+from pa_cases import gpu_caches
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+def _calls(b, kc, vc, variant):
+    """A function that queues the batch's append and then its decode (kernel
+    family `variant`) on a stream and returns the outputs."""
+    def run(stream):
+        outs = []
+        pa.kv_append(b.k_new, b.v_new, b.slot_mapping, kc, vc, b.k_scale, b.v_scale,
+                     stream=stream)
+        outs.append(pa.decode(b.q, kc, vc, b.block_tables, b.seq_lens, b.scale,
+                              k_scale=b.k_scale, v_scale=b.v_scale, variant=variant,
+                              stream=stream))
+        return outs
+    return run
+
+
+def test_two_streams_match_one_stream():
+    a = workloads.make_batch("llama3_8b_bf16", device=DEV, num_seqs=24, lens=("uniform", 1, 900),
+                             max_len=900, seed=91)
+    b = workloads.make_batch("long_fp8", device=DEV, num_seqs=6, num_heads=16, num_kv_heads=2,
+                             lens=("uniform", 1, 2000), max_len=2048, seed=92)
+    runs = []
+    for batch, variant in ((a, pa.VARIANT_MFMA), (a, pa.VARIANT_VALU), (b, pa.VARIANT_MFMA)):
+        kc, vc = gpu_caches(batch)
+        runs.append((batch, variant, kc, vc))
+    # reference: one stream, one after the other, on copies of the caches
+    ref = []
+    for batch, variant, kc, vc in runs:
+        k2, v2 = kc.clone(), vc.clone()
+        ref.append(_calls(batch, k2, v2, variant)(None))
+    torch.cuda.synchronize()
+    # two streams, calls interleaved
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print("CASE two streams", flush=True)
+    got = []
+    for i, (batch, variant, kc, vc) in enumerate(runs):
+        s = s1 if i % 2 == 0 else s2
+        with torch.cuda.stream(s):
+            got.append(_calls(batch, kc, vc, variant)(s))
+    torch.cuda.synchronize()
+    for i, (r, g) in enumerate(zip(ref, got)):
+        for x, y in zip(r, g):
+            assert torch.equal(_bits(x), _bits(y)), f"call {i}"
+
+
+def test_multi_token_and_cascade_on_two_streams():
+    m = workloads.make_batch("llama3_8b_bf16_spec8", device=DEV, num_seqs=10,
+                             lens=("uniform", 8, 700), max_len=704, seed=93)
+    c = workloads.make_batch("shared_prefix_bf16", device=DEV, num_seqs=20,
+                             lens=("prefix", 320, 1, 120), max_len=320 + 128, seed=94)
+    km, vm = gpu_caches(m)
+    kc, vc = gpu_caches(c)
+    N = c.shared_prefix_blocks
+
+    def multi(k, v, stream):
+        pa.kv_append(m.k_new, m.v_new, m.slot_mapping, k, v, stream=stream)
+        return pa.decode_multi(m.q, m.query_start_loc, m.max_query_len, k, v, m.block_tables,
+                               m.seq_lens, m.scale, stream=stream)
+
+    def cascade(k, v, stream):
+        pa.kv_append(c.k_new, c.v_new, c.slot_mapping, k, v, stream=stream)
+        return pa.decode_cascade(c.q, k, v, c.block_tables, c.seq_lens, N, c.scale,
+                                 stream=stream)
+
+    ref_m = multi(km.clone(), vm.clone(), None)
+    ref_c = cascade(kc.clone(), vc.clone(), None)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print("CASE multi-token and cascade on two streams", flush=True)
+    with torch.cuda.stream(s1):
+        got_m = multi(km, vm, s1)
+    with torch.cuda.stream(s2):
+        got_c = cascade(kc, vc, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(got_m.view(torch.int16), ref_m.view(torch.int16))
+    assert torch.equal(got_c.view(torch.int16), ref_c.view(torch.int16))
