@@ -280,9 +280,12 @@ int block_op(const int32_t *ids, int64_t n, const void *const *src_bases,
         reinterpret_cast<uintptr_t>(dst_bases) % 8 ||
         reinterpret_cast<uintptr_t>(src_bases) % 8)
         return PA_ERR_ALIGN;
-    // every addressed byte offset must fit int64
+    // every addressed byte offset, and the operation's total bytes, must fit int64
     const int64_t max_blocks = dst_num_blocks > src_num_blocks ? dst_num_blocks : src_num_blocks;
-    if (max_blocks > INT64_MAX / block_stride)
+    int64_t item_regions = 0, total_bytes = 0;
+    if (max_blocks > INT64_MAX / block_stride ||
+        __builtin_mul_overflow(n, (int64_t)num_regions, &item_regions) ||
+        __builtin_mul_overflow(item_regions, block_bytes, &total_bytes))
         return PA_ERR_UNSUPPORTED;
 
     BlockOpArgs a;
@@ -302,7 +305,7 @@ int block_op(const int32_t *ids, int64_t n, const void *const *src_bases,
     int cus = 0, rc;
     if ((rc = device_cu_count(&cus)))
         return rc;
-    const int64_t units = n * num_regions * a.chunks;
+    const int64_t units = item_regions * a.chunks;
     const int64_t target = 8 * (int64_t)cus;
     int64_t g = units / target;
     a.group_items = (int32_t)(g < 1 ? 1 : (g > kMaxGroupItems ? kMaxGroupItems : g));
@@ -313,8 +316,8 @@ int block_op(const int32_t *ids, int64_t n, const void *const *src_bases,
     // Large operations with tables in device memory: one workgroup per (item,
     // region, piece).  Below 128 MiB the grouped kernel's fewer, longer
     // workgroups measured faster (a 57 MiB clear: 12.1 against 13.5 us).
-    const int64_t pieces = n * num_regions * (int64_t)a.pieces;
-    const bool large = n * num_regions * block_bytes >= (int64_t(128) << 20);
+    const int64_t pieces = item_regions * (int64_t)a.pieces;
+    const bool large = total_bytes >= (int64_t(128) << 20);
     const bool device_tables = large && in_device_memory(ids) && in_device_memory(dst_bases) &&
                                (!copy || in_device_memory(src_bases));
     hipError_t e = device_tables && pieces <= INT32_MAX
@@ -448,6 +451,9 @@ int plan_cascade(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt, i
         return PA_ERR_SHAPE;
     const int64_t S = q->shape[0], max_nb = bt->shape[1];
     if (N < 1 || N >= max_nb)
+        return PA_ERR_UNSUPPORTED;
+    // token positions of the whole table row (prefix included) are int32
+    if (kc->shape[1] > 0 && max_nb > INT32_MAX / kc->shape[1])
         return PA_ERR_UNSUPPORTED;
     if (q->shape[1] <= 0 || kc->shape[2] <= 0 || q->shape[1] % kc->shape[2])
         return PA_ERR_SHAPE;

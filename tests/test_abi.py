@@ -230,6 +230,11 @@ def test_block_op_validation_errors():
     assert L.pa_copy_blocks(ids + 4, 5, bases, bases, 4, 4096, 4096, 100, 100, None, None) \
         == PA_ERR_ALIGN                                                  # pairs need 8 bytes
     assert L.pa_zero_blocks(ids, 5, bases + 4, 4, 4096, 4096, 100, None, None) == PA_ERR_ALIGN
+    # ids x regions x block bytes beyond int64: refused before anything is launched
+    assert L.pa_zero_blocks(ids, 1 << 55, bases, 4, 4096, 4096, 100, None, None) \
+        == PA_ERR_UNSUPPORTED
+    assert L.pa_copy_blocks(ids, 1 << 60, bases, bases, 16, 4096, 4096, 100, 100, None, None) \
+        == PA_ERR_UNSUPPORTED
 
 
 def call_multi(a, qsl, qm, o=None, scale=0.125):
@@ -308,3 +313,7 @@ def test_decode_cascade_validation_errors():
     b = decode_args(S=4, H=8, Hkv=2, D=128, max_nb=8, qd=BF16, kd=BF16)
     b["bt"] = desc([3, 8], I32)
     assert call(b, 2) == PA_ERR_SHAPE
+    # a table row of more than 2^31 token positions, though its suffix is short
+    wide = (1 << 27) + 8
+    c = decode_args(S=4, H=8, Hkv=2, D=128, max_nb=wide, qd=BF16, kd=BF16)
+    assert call(c, wide - 4) == PA_ERR_UNSUPPORTED
