@@ -186,6 +186,19 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _torch_stream(stream):
+    """The torch stream object of a call's ``stream`` argument (None: the
+    current stream; a raw hipStream_t handle is wrapped).  Outputs and
+    workspaces a call allocates are allocated on it, so the caching allocator
+    reuses a freed workspace only for work queued after the call's kernels on
+    that stream, not while they still run."""
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(_stream(stream))
+
+
 def _check(fn: str, rc: int):
     if rc != 0:
         raise PaError(fn, rc)
@@ -225,17 +238,19 @@ def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, k
     allocator) when needed and not given.  ``events``: optional pair of raw
     hipEvent_t handles recorded around the attention kernel."""
     lib = _load()
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        need = decode_workspace_size(q, key_cache, block_tables, partition_tokens, variant)
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            need = decode_workspace_size(q, key_cache, block_tables, partition_tokens, variant)
+            if need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events)
     args = [describe(x) for x in (q, key_cache, value_cache, block_tables, seq_lens)]
     _check("pa_decode", lib.pa_decode(*[ctypes.byref(x) for x in args], float(scale),
                                       ctypes.byref(describe(out)), ctypes.byref(o),
-                                      _stream(stream)))
+                                      ts.cuda_stream))
     return out
 
 
@@ -259,19 +274,21 @@ def decode_cascade(q, key_cache, value_cache, block_tables, seq_lens, prefix_blo
     """pa_decode for a batch whose sequences share their first prefix_blocks
     blocks: the shared blocks are read once per group of sequences."""
     lib = _load()
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        need = decode_cascade_workspace_size(q, key_cache, block_tables, prefix_blocks,
-                                             partition_tokens, variant)
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            need = decode_cascade_workspace_size(q, key_cache, block_tables, prefix_blocks,
+                                                 partition_tokens, variant)
+            if need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events)
     args = [describe(x) for x in (q, key_cache, value_cache, block_tables, seq_lens)]
     _check("pa_decode_cascade",
            lib.pa_decode_cascade(*[ctypes.byref(x) for x in args], int(prefix_blocks),
                                  float(scale), ctypes.byref(describe(out)), ctypes.byref(o),
-                                 _stream(stream)))
+                                 ts.cuda_stream))
     return out
 
 
@@ -294,20 +311,22 @@ def decode_multi(q, query_start_loc, max_query_len, key_cache, value_cache, bloc
     """Paged attention of several new query tokens per sequence (causal within
     them); q, out [T, H, D] bf16, query_start_loc int32 [S+1]."""
     lib = _load()
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        need = decode_multi_workspace_size(q, max_query_len, key_cache, block_tables,
-                                           partition_tokens, variant)
-        if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            need = decode_multi_workspace_size(q, max_query_len, key_cache, block_tables,
+                                               partition_tokens, variant)
+            if need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events)
     d_q, d_qsl = describe(q), describe(query_start_loc)
     args = [describe(x) for x in (key_cache, value_cache, block_tables, seq_lens)]
     _check("pa_decode_multi",
            lib.pa_decode_multi(ctypes.byref(d_q), ctypes.byref(d_qsl), int(max_query_len),
                                *[ctypes.byref(x) for x in args], float(scale),
-                               ctypes.byref(describe(out)), ctypes.byref(o), _stream(stream)))
+                               ctypes.byref(describe(out)), ctypes.byref(o), ts.cuda_stream))
     return out
 
 
@@ -403,12 +422,15 @@ def prepare_step(idx_mapping, num_scheduled, num_computed, block_table, token_id
             block_table.shape[0] != num_computed.numel() or token_ids.shape[0] != num_computed.numel():
         raise ValueError("inconsistent state shapes")
     dev = idx_mapping.device
-    out = dict(query_start_loc=torch.empty(S + 1, dtype=torch.int32, device=dev),
-               seq_lens=torch.empty(S, dtype=torch.int32, device=dev),
-               positions=torch.empty(max_tokens, dtype=torch.int64, device=dev),
-               input_ids=torch.empty(max_tokens, dtype=torch.int32, device=dev),
-               slot_mapping=torch.empty(max_tokens, dtype=torch.int64, device=dev),
-               block_tables=torch.empty((S, block_table.shape[1]), dtype=torch.int32, device=dev))
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        out = dict(query_start_loc=torch.empty(S + 1, dtype=torch.int32, device=dev),
+                   seq_lens=torch.empty(S, dtype=torch.int32, device=dev),
+                   positions=torch.empty(max_tokens, dtype=torch.int64, device=dev),
+                   input_ids=torch.empty(max_tokens, dtype=torch.int32, device=dev),
+                   slot_mapping=torch.empty(max_tokens, dtype=torch.int64, device=dev),
+                   block_tables=torch.empty((S, block_table.shape[1]), dtype=torch.int32,
+                                            device=dev))
     st = PaStepState(num_computed.data_ptr(), block_table.data_ptr(), token_ids.data_ptr(),
                      num_computed.numel(), block_table.shape[1], token_ids.shape[1])
     io = PaStepInputs(out["query_start_loc"].data_ptr(), out["seq_lens"].data_ptr(),
@@ -419,5 +441,5 @@ def prepare_step(idx_mapping, num_scheduled, num_computed, block_table, token_id
     _check("pa_prepare_step",
            _load().pa_prepare_step(idx_mapping.data_ptr(), num_scheduled.data_ptr(), S,
                                    ctypes.byref(st), int(block_size), int(num_blocks),
-                                   ctypes.byref(io), ctypes.byref(o), _stream(stream)))
+                                   ctypes.byref(io), ctypes.byref(o), ts.cuda_stream))
     return out

@@ -94,3 +94,38 @@ def test_multi_token_and_cascade_on_two_streams():
     torch.cuda.synchronize()
     assert torch.equal(got_m.view(torch.int16), ref_m.view(torch.int16))
     assert torch.equal(got_c.view(torch.int16), ref_c.view(torch.int16))
+
+
+def test_stream_argument_other_than_current_stream():
+    """``stream=`` given as a torch stream and as a raw handle while torch's
+    current stream is another one: outputs and workspaces are allocated on the
+    launch stream, and the results equal a call on the current stream.  The
+    launch stream is kept busy with queued work first, so the calls' kernels
+    run after the wrappers have returned and freed their workspaces."""
+    b = workloads.make_batch("llama3_8b_bf16", device=DEV, num_seqs=16, lens=("uniform", 1, 1500),
+                             max_len=1500, seed=95)
+    m = workloads.make_batch("llama3_8b_bf16_spec8", device=DEV, num_seqs=6,
+                             lens=("uniform", 8, 600), max_len=608, seed=96)
+    kc, vc = gpu_caches(b)
+    km, vm = gpu_caches(m)
+    pa.kv_append(b.k_new, b.v_new, b.slot_mapping, kc, vc)
+    pa.kv_append(m.k_new, m.v_new, m.slot_mapping, km, vm)
+    ref = pa.decode(b.q, kc, vc, b.block_tables, b.seq_lens, b.scale)
+    ref_m = pa.decode_multi(m.q, m.query_start_loc, m.max_query_len, km, vm, m.block_tables,
+                            m.seq_lens, m.scale)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    x = torch.randn(2048, 2048, device=DEV)
+    print("CASE stream argument other than the current stream", flush=True)
+    for handle in (s, s.cuda_stream):
+        with torch.cuda.stream(s):
+            for _ in range(20):
+                x = torch.tanh(x @ x)                # queued work ahead of the calls
+        out = pa.decode(b.q, kc, vc, b.block_tables, b.seq_lens, b.scale, stream=handle)
+        out_m = pa.decode_multi(m.q, m.query_start_loc, m.max_query_len, km, vm,
+                                m.block_tables, m.seq_lens, m.scale, stream=handle)
+        junk = [torch.full((1 << 20,), 7, dtype=torch.uint8, device=DEV) for _ in range(8)]
+        torch.cuda.synchronize()
+        del junk
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"decode {handle}"
+        assert torch.equal(out_m.view(torch.int16), ref_m.view(torch.int16)), f"multi {handle}"
