@@ -9,9 +9,10 @@ namespace pa {
 namespace {
 
 // Wavefronts per workgroup.  Each wavefront walks its own chunk with its own
-// LDS tiles; packing two into a workgroup halves the workgroups the
-// dispatcher has to launch (measured ~1.3 % faster than one per workgroup on
-// the Llama- and Qwen-shaped batches; four or eight were no better).
+// LDS tiles.  Two per workgroup measured ~1.3 % faster than one on the Llama-
+// and Qwen-shaped batches when every resident wavefront had a chunk, and the
+// same as one with the bf16 split over half of them; four were slower in both
+// cases (9 % at half), eight no better.
 constexpr int kWavesPerGroup = 2;
 
 template <int KT, int D, int BS, int G>
