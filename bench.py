@@ -4,11 +4,16 @@ A step is the whole hot path for one batch: pa_kv_append of each sequence's
 new K/V row into its slot, then pa_decode (block-table walk, gather, QK,
 online softmax, PV, split-KV merge).  Inputs are generated on the GPU and are
 resident in HBM before timing starts.  W untimed warm-up steps, then exactly
-K timed steps between device synchronisations; the attention kernel's own
-duration is taken from HIP events the library records around it.
+K timed steps between device synchronisations.  Before every step a kernel
+reads and writes a 1 GiB scratch buffer, so no cache (the 4 MB L2 of each
+XCD, the 256 MB Infinity Cache) still holds the batch from the step before;
+HIP events bracket each step (the flush is outside them) and the library
+records a second pair around its attention kernel.  ``--warm`` runs the
+steps back to back instead, with no flush.
 
 Prints one JSON line.  ``value`` is the step's algorithmic HBM bytes divided
-by the wall time per step, in GB/s.
+by the median step time, in GB/s; the roofline fraction comes from the
+attention kernel's median time.
 """
 import argparse
 import ctypes
@@ -22,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak, 8 TB/s
+FLUSH_BYTES = 1 << 30      # scratch read and written before every timed step
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) + decode seqs/s"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
@@ -54,9 +60,10 @@ def parse():
                          "pa_decode_cascade")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="record the decode kernel's HIP events on every N-th timed step "
-                         "(an event record adds a small gap between kernels)")
+    ap.add_argument("--warm", action="store_true",
+                    help="run the timed steps back to back with no cache flush between them")
+    ap.add_argument("--bf16-partials", action="store_true",
+                    help="store split-KV partial accumulators as bf16 instead of fp32")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB "
                          "(3 launches) so hardware byte counters can be scaled against a known size")
@@ -65,6 +72,14 @@ def parse():
 
 def cdiv(a, b):
     return -(-a // b)
+
+
+def quantiles(ms):
+    """Median, p10 and p90 of a list of times in ms."""
+    import numpy as np
+    p10, med, p90 = np.percentile(np.asarray(ms, dtype=np.float64), [10, 50, 90])
+    return {"median": round(float(med), 5), "p10": round(float(p10), 5),
+            "p90": round(float(p90), 5)}
 
 
 def algorithmic_bytes(b):
@@ -153,12 +168,26 @@ class HipEvents:
             self.lib.hipEventDestroy(e)
 
 
+def cpu_model():
+    """The host CPU's model name and the number of CPUs this process may use."""
+    name = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return name, len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(b, budget_s):
-    """The oracle, as it stands, on the host cores: whole (sequence, KV-head)
-    groups of this batch in a seeded random order, cycling through the batch,
-    until about budget_s seconds of oracle work; reported in the step's unit
-    (algorithmic GB/s of the groups computed)."""
-    import numpy as np
+    """The oracle, as it stands, on the host cores: one call over the whole
+    batch (every query row; OpenMP over rows), the median of 3 runs -- fewer
+    when one run already takes more than budget_s -- after the host caches are
+    filled (not timed).  Reported in the step's unit: algorithmic GB/s of the
+    decode, plus seconds per batch and decode sequences per second."""
+    import statistics
 
     import oracle
     NB, bs, Hkv, D = b.num_blocks, b.block_size, b.num_kv_heads, b.head_dim
@@ -166,37 +195,27 @@ def cpu_baseline(b, budget_s):
                                b.value_pool.cpu().view(NB * bs, Hkv, D))
     oracle.kv_append(b.k_new.cpu(), b.v_new.cpu(), b.slot_mapping.cpu(), kc, vc, b.k_scale,
                      b.v_scale)
-    q = b.q.cpu()
-    tables = b.block_tables.cpu().numpy()
-    lens = b.seq_lens.cpu().numpy()
-    G = b.group_size
-    groups = np.random.default_rng(0).permutation(b.num_seqs * Hkv)
-    qsl = None if b.query_start_loc is None else b.query_start_loc.cpu().numpy()
-    done, nbytes, t_total = 0, 0, 0.0
-    per_tok = D * b.kv_elem_bytes * 2
-    while t_total < budget_s:
-        g = int(groups[done % len(groups)])
-        s, kvh = divmod(g, Hkv)
-        if qsl is None:
-            rows = [s * b.num_heads + kvh * G + i for i in range(G)]
-        else:
-            rows = [tok * b.num_heads + kvh * G + i for tok in range(qsl[s], qsl[s + 1])
-                    for i in range(G)]
+    q, tables, lens = b.q.cpu(), b.block_tables.cpu(), b.seq_lens.cpu()
+    rows = q.shape[0] * b.num_heads
+    times = []
+    while len(times) < 3 and (not times or sum(times) < budget_s):
         t0 = time.perf_counter()
-        if qsl is None:
-            oracle.decode(q, kc, vc, tables, lens, b.scale, b.k_scale, b.v_scale, rows=rows)
+        if b.query_start_loc is None:
+            oracle.decode(q, kc, vc, tables, lens, b.scale, b.k_scale, b.v_scale)
         else:
             oracle.decode_multi(q, b.query_start_loc.cpu(), kc, vc, tables, lens, b.scale,
-                                b.k_scale, b.v_scale, rows=rows)
-        t_total += time.perf_counter() - t0
-        nbytes += int(lens[s]) * per_tok + 2 * len(rows) * D * b.q_elem_bytes
-        done += 1
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(nbytes / t_total / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{done} (sequence, kv-head) groups of this batch ({done / len(groups):.2f} "
-                      f"passes over its {len(groups)} groups, {done * G} query rows) in "
-                      f"{t_total:.1f} s; fp64 C oracle, OpenMP over query rows"}
+                                b.k_scale, b.v_scale)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    nbytes = algorithmic_bytes(b)["decode"]
+    threads = min(oracle.num_threads(), rows)
+    model, ncpu = cpu_model()
+    return {"value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds_per_batch": round(t, 3),
+            "decode_seqs_per_s": round(b.num_seqs / t, 2),
+            "sample": f"the whole batch ({rows} query rows) in one call, median of "
+                      f"{len(times)} run(s): {t:.2f} s; fp64 C oracle, OpenMP over query rows on "
+                      f"{threads} threads; host {model}, {ncpu} CPUs available"}
 
 
 def block_cpu_baseline(case, budget_s):
@@ -263,17 +282,22 @@ def bench_blocks(args):
         if k is not None:
             ev.record(2 * k + 1, stream)
 
+    flush = None if args.warm else torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
     for _ in range(args.warmup):
+        if flush is not None:
+            flush.add_(1)
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if flush is not None:
+            flush.add_(1)                      # read + write 1 GiB, outside the events
         step(k)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = sum(ev.elapsed_ms(2 * k, 2 * k + 1) for k in range(args.steps)) / args.steps
+    kern_q = quantiles([ev.elapsed_ms(2 * k, 2 * k + 1) for k in range(args.steps)])
     ev.close()
-    ms = wall / args.steps * 1e3
+    kernel_ms = ms = kern_q["median"]          # a step is the one launch
     value = nbytes / (ms * 1e-3) / 1e9
     achieved = nbytes / (kernel_ms * 1e-3) / 1e9
     # the library's choice: one workgroup per 4 KiB piece for operations of
@@ -289,13 +313,18 @@ def bench_blocks(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
         "config": {"workload": args.workload, "op": case.op, "items": n, "regions": R,
                    "block_bytes": case.block_bytes, "num_blocks": case.num_blocks},
+        "timing": {"protocol": "back to back, no flush" if args.warm else
+                   "1 GiB read+write flush before each step, outside the events",
+                   "kernel_ms": kern_q, "wall_ms_per_step": round(wall / args.steps * 1e3, 5)},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "algorithmic_bytes_per_step": nbytes,
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel_ms": round(kernel_ms, 5),
-                     "kernel_ms_from": f"HIP events around each of the {args.steps} launches",
+                     "kernel_ms_from": f"median of HIP events around each of the {args.steps} "
+                                       f"launches" + ("" if args.warm else
+                                                      ", caches flushed before each"),
                      "algorithmic_bytes_per_launch": nbytes},
     }
     res["cpu_baseline"] = None if args.no_cpu_baseline else block_cpu_baseline(
@@ -435,14 +464,15 @@ def main():
     multi = b.query_start_loc is not None
     cascade = (b.shared_prefix_blocks > 0 and not args.no_cascade and b.q_dtype == "bf16"
                and variant != pa.VARIANT_VALU)
+    bf16p = args.bf16_partials
     if cascade:
         ws_bytes = pa.decode_cascade_workspace_size(b.q, kc, b.block_tables,
-                                                    b.shared_prefix_blocks, P, variant)
+                                                    b.shared_prefix_blocks, P, variant, bf16p)
     elif multi:
         ws_bytes = pa.decode_multi_workspace_size(b.q, b.max_query_len, kc, b.block_tables, P,
-                                                  variant)
+                                                  variant, bf16p)
     else:
-        ws_bytes = pa.decode_workspace_size(b.q, kc, b.block_tables, P, variant)
+        ws_bytes = pa.decode_workspace_size(b.q, kc, b.block_tables, P, variant, bf16p)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
     # descriptors built once; each step is two C calls
@@ -456,18 +486,19 @@ def main():
     o.k_scale, o.v_scale = b.k_scale, b.v_scale
     o.partition_tokens, o.variant = P, variant
     o.workspace, o.workspace_bytes = ws.data_ptr(), ws.numel()
+    o.partials = pa.PARTIALS_BF16 if bf16p else pa.PARTIALS_F32
     stream = torch.cuda.current_stream().cuda_stream
-    timed = [i for i in range(args.steps) if i % max(args.event_every, 1) == 0]
-    ev = HipEvents(2 * len(timed))
-    ev_slot = {step_i: k for k, step_i in enumerate(timed)}
+    # per timed step: step start, kernel start, kernel end, step end
+    ev = HipEvents(4 * args.steps)
+    flush = None if args.warm else torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
     by = ctypes.byref
 
     def step(i=None):
-        k = ev_slot.get(i)
-        if k is None:
+        if i is None:
             o.kernel_events[0] = o.kernel_events[1] = None
         else:
-            o.kernel_events[0], o.kernel_events[1] = ev.ev[2 * k], ev.ev[2 * k + 1]
+            o.kernel_events[0], o.kernel_events[1] = ev.ev[4 * i + 1], ev.ev[4 * i + 2]
+            ev.record(4 * i, stream)
         rc = lib.pa_kv_append(by(d_k), by(d_v), by(d_slot), by(d_kc), by(d_vc), by(o), stream)
         if cascade:
             rc = rc or lib.pa_decode_cascade(by(d_q), by(d_kc), by(d_vc), by(d_bt), by(d_len),
@@ -482,20 +513,29 @@ def main():
                                      ctypes.c_float(b.scale), by(d_out), by(o), stream)
         if rc:
             raise pa.PaError("step", rc)
+        if i is not None:
+            ev.record(4 * i + 3, stream)
 
     for _ in range(args.warmup):
+        if flush is not None:
+            flush.add_(1)
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.add_(1)                      # read + write 1 GiB, outside the events
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = sum(ev.elapsed_ms(2 * k, 2 * k + 1) for k in range(len(timed))) / len(timed)
+    step_t = [ev.elapsed_ms(4 * i, 4 * i + 3) for i in range(args.steps)]
+    kern_t = [ev.elapsed_ms(4 * i + 1, 4 * i + 2) for i in range(args.steps)]
     ev.close()
+    step_q, kern_q = quantiles(step_t), quantiles(kern_t)
+    kernel_ms = kern_q["median"]
 
     nbytes = algorithmic_bytes(b)
-    ms_per_step = wall / args.steps * 1e3
+    ms_per_step = step_q["median"]
     value = nbytes["step"] / (ms_per_step * 1e-3) / 1e9
     used = "mfma_multi" if multi else "mfma" if (variant == pa.VARIANT_MFMA or (
         variant == pa.VARIANT_AUTO and _mfma_ok(pa, b, kc))) else "valu"
@@ -518,6 +558,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3"}[b.cache_dtype],
+        "timing": {"protocol": "back to back, no flush" if args.warm else
+                   "1 GiB read+write flush before each step, outside the events",
+                   "step_ms": step_q, "kernel_ms": kern_q,
+                   "wall_ms_per_step": round(wall / args.steps * 1e3, 5)},
         "data": "synthetic",
         "config": {"workload": args.workload, "num_seqs": b.num_seqs, "num_heads": b.num_heads,
                    "num_kv_heads": b.num_kv_heads, "head_dim": b.head_dim,
@@ -525,6 +569,7 @@ def main():
                    "mean_seq_len": round(nbytes["logical_tokens"] / b.num_seqs, 1),
                    "q_dtype": b.q_dtype, "cache_dtype": b.cache_dtype,
                    "partition_tokens": P or "auto", "variant": used,
+                   "partials": "bf16" if bf16p and b.q_dtype == "bf16" else "f32",
                    **({"shared_prefix_blocks": b.shared_prefix_blocks} if cascade else {}),
                    **({"query_tokens": b.q.shape[0], "max_query_len": b.max_query_len}
                       if multi else {})},
@@ -535,8 +580,9 @@ def main():
                      "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
-                     "kernel_ms_from": f"HIP events around the decode kernel on {len(timed)} of "
-                                       f"the {args.steps} timed steps",
+                     "kernel_ms_from": f"median of HIP events around the attention kernel on "
+                                       f"each of the {args.steps} timed steps"
+                                       + ("" if args.warm else ", caches flushed before each"),
                      "algorithmic_bytes_per_launch": nbytes["decode"]},
     }
     if nbytes["logical_decode"] != nbytes["decode"]:

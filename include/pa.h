@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 1
+#define PA_VERSION 2
 
 typedef enum pa_dtype {
     PA_F32 = 0,       /* IEEE binary32 */
@@ -100,6 +100,12 @@ typedef struct pa_tensor {
     int64_t stride[4];  /* in elements; must be dense row-major */
 } pa_tensor;
 
+/* Storage type of split-KV partial accumulators (pa_opts.partials). */
+#define PA_PARTIALS_F32 0   /* fp32 (default): a split segment's accumulators are merged
+                               exactly as they were accumulated */
+#define PA_PARTIALS_BF16 1  /* bf16 for a bf16 output (f32 outputs keep fp32): half the
+                               workspace bytes, one extra bf16 rounding per partial */
+
 /* Decode kernel families (pa_opts.variant). */
 #define PA_VARIANT_AUTO 0  /* library choice: MFMA where supported, else VALU */
 #define PA_VARIANT_VALU 1  /* vector-ALU kernel: every supported dtype and group size */
@@ -123,14 +129,18 @@ typedef struct pa_opts {
                                    16-byte aligned; no initial contents needed */
     size_t workspace_bytes;
     uint32_t *err_flag;         /* optional device word, see PA_DEVERR_* */
-    /* Optional pair of hipEvent_t recorded on hip_stream immediately before
-       and after the attention kernel of pa_decode (not the merge), so callers
-       can time that kernel alone.  NULL to skip. */
+    /* Profiling hook: an optional pair of hipEvent_t recorded on hip_stream
+       immediately before and after the attention kernel of pa_decode,
+       pa_decode_multi or pa_decode_cascade (not the merge), so callers can
+       time that kernel alone.  NULL to skip (the default). */
     void *kernel_events[2];
+    /* PA_PARTIALS_*: how split-KV partial accumulators are stored in the
+       workspace (the workspace size depends on it). */
+    int32_t partials;
 } pa_opts;
 
 /* Fills *opts with the defaults: scales 1.0, library partition choice,
-   automatic variant, no workspace, no error word, no events. */
+   automatic variant, no workspace, no error word, no events, fp32 partials. */
 void pa_opts_init(pa_opts *opts);
 
 /*
@@ -171,7 +181,9 @@ int pa_kv_append(const pa_tensor *k, const pa_tensor *v, const pa_tensor *slot_m
  * G = H / Hkv in {1, 2, 4, 8}.  opts->workspace (pa_decode_workspace_size
  * bytes) is required whenever S > 0: it receives the partial results of KV
  * heads whose sequence is split between chunks (see partition_tokens) and a
- * second kernel merges them by log-sum-exp.  Accumulation is in fp32.
+ * second kernel merges them by log-sum-exp.  Accumulation is in fp32, and so
+ * are the partials unless opts->partials asks for bf16.  With S > 0 the pool
+ * must hold at least one block (NB >= 1), else PA_ERR_SHAPE.
  */
 int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *value_cache,
               const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,

@@ -64,10 +64,17 @@ def _load():
         lib.oracle_e4m3_encode_array.argtypes = [c_vp, c_vp, c_i64]
         lib.oracle_e4m3_decode_array.argtypes = [c_vp, c_vp, c_i64]
         lib.oracle_bf16_decode_array.argtypes = [c_vp, c_vp, c_i64]
+        lib.oracle_num_threads.restype = c_i32
+        lib.oracle_num_threads.argtypes = []
         lib.oracle_e4m3_from_f32.restype = ctypes.c_uint8
         lib.oracle_e4m3_from_f32.argtypes = [ctypes.c_float]
         _lib = lib
     return _lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops run on."""
+    return _load().oracle_num_threads()
 
 
 def _as_host_array(x, dtype_hint=None):

@@ -44,12 +44,16 @@
  * (no fast-math: the fp32 multiply in the append must round like IEEE binary32).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_E4M3 = 2 };
 enum { OR_OK = 0, OR_EARG = 1, OR_EBLOCK = 2, OR_ESLOT = 3, OR_ENOMEM = 4, OR_ELEN = 5 };
+
+/* Threads an OpenMP loop of this library runs on (for reporting only). */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* ---------------------------------------------------------------- codecs */
 

@@ -30,7 +30,8 @@ __all__ = ["kv_append", "decode", "decode_workspace_size", "decode_multi", "deco
            "decode_cascade_workspace_size",
            "decode_multi_workspace_size", "zero_blocks", "copy_blocks",
            "region_table", "Regions", "prepare_step", "PaError", "status_string", "version", "library_path",
-           "VARIANT_AUTO", "VARIANT_VALU", "VARIANT_MFMA", "DEVERR_BLOCK_ID", "DEVERR_SEQ_LEN",
+           "VARIANT_AUTO", "VARIANT_VALU", "VARIANT_MFMA", "PARTIALS_F32", "PARTIALS_BF16",
+           "DEVERR_BLOCK_ID", "DEVERR_SEQ_LEN",
            "DEVERR_SLOT", "DEVERR_REGION", "DEVERR_QUERY", "DEVERR_STEP", "DEVERR_PREFIX"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +39,7 @@ _LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3, PA_I32, PA_I64 = 0, 1, 2, 3, 4
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
+PARTIALS_F32, PARTIALS_BF16 = 0, 1
 DEVERR_BLOCK_ID, DEVERR_SEQ_LEN, DEVERR_SLOT, DEVERR_REGION, DEVERR_QUERY = 0x1, 0x2, 0x4, 0x8, 0x10
 DEVERR_STEP, DEVERR_PREFIX = 0x20, 0x40
 
@@ -54,7 +56,8 @@ class PaOpts(ctypes.Structure):
     _fields_ = [("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float),
                 ("partition_tokens", ctypes.c_int32), ("variant", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("err_flag", ctypes.c_void_p), ("kernel_events", ctypes.c_void_p * 2)]
+                ("err_flag", ctypes.c_void_p), ("kernel_events", ctypes.c_void_p * 2),
+                ("partials", ctypes.c_int32)]
 
 
 class PaStepState(ctypes.Structure):
@@ -160,13 +163,15 @@ def describe(t: torch.Tensor) -> PaTensor:
 
 
 def _opts(k_scale=1.0, v_scale=1.0, partition_tokens=0, variant=VARIANT_AUTO, workspace=None,
-          err_flag=None, events: Optional[Sequence[int]] = None) -> PaOpts:
+          err_flag=None, events: Optional[Sequence[int]] = None,
+          bf16_partials=False) -> PaOpts:
     o = PaOpts()
     _load().pa_opts_init(ctypes.byref(o))
     o.k_scale = float(k_scale)
     o.v_scale = float(v_scale)
     o.partition_tokens = int(partition_tokens)
     o.variant = int(variant)
+    o.partials = PARTIALS_BF16 if bf16_partials else PARTIALS_F32
     if workspace is not None:
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -217,9 +222,9 @@ def kv_append(k, v, slot_mapping, key_cache, value_cache, k_scale=1.0, v_scale=1
 
 
 def decode_workspace_size(q, key_cache, block_tables, partition_tokens=0,
-                          variant=VARIANT_AUTO) -> int:
+                          variant=VARIANT_AUTO, bf16_partials=False) -> int:
     lib = _load()
-    o = _opts(partition_tokens=partition_tokens, variant=variant)
+    o = _opts(partition_tokens=partition_tokens, variant=variant, bf16_partials=bf16_partials)
     n = ctypes.c_size_t(0)
     _check("pa_decode_workspace_size",
            lib.pa_decode_workspace_size(ctypes.byref(describe(q)), ctypes.byref(describe(key_cache)),
@@ -230,23 +235,27 @@ def decode_workspace_size(q, key_cache, block_tables, partition_tokens=0,
 
 def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, k_scale=1.0,
            v_scale=1.0, partition_tokens=0, variant=VARIANT_AUTO, workspace=None,
-           err_flag=None, events=None, stream=None):
+           err_flag=None, events=None, stream=None, bf16_partials=False):
     """Paged decode attention; returns ``out`` [S, H, D] (same dtype as q).
 
     ``workspace``: optional uint8 device tensor of at least
     ``decode_workspace_size(...)`` bytes; allocated here (torch caching
     allocator) when needed and not given.  ``events``: optional pair of raw
-    hipEvent_t handles recorded around the attention kernel."""
+    hipEvent_t handles recorded around the attention kernel.
+    ``bf16_partials``: store split-KV partial accumulators as bf16 instead of
+    fp32 (bf16 outputs only)."""
     lib = _load()
     ts = _torch_stream(stream)
     with torch.cuda.stream(ts):
         if out is None:
             out = torch.empty_like(q)
         if workspace is None:
-            need = decode_workspace_size(q, key_cache, block_tables, partition_tokens, variant)
+            need = decode_workspace_size(q, key_cache, block_tables, partition_tokens, variant,
+                                         bf16_partials)
             if need:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events)
+    o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events,
+              bf16_partials)
     args = [describe(x) for x in (q, key_cache, value_cache, block_tables, seq_lens)]
     _check("pa_decode", lib.pa_decode(*[ctypes.byref(x) for x in args], float(scale),
                                       ctypes.byref(describe(out)), ctypes.byref(o),
@@ -255,9 +264,9 @@ def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, k
 
 
 def decode_cascade_workspace_size(q, key_cache, block_tables, prefix_blocks, partition_tokens=0,
-                                  variant=VARIANT_AUTO) -> int:
+                                  variant=VARIANT_AUTO, bf16_partials=False) -> int:
     lib = _load()
-    o = _opts(partition_tokens=partition_tokens, variant=variant)
+    o = _opts(partition_tokens=partition_tokens, variant=variant, bf16_partials=bf16_partials)
     n = ctypes.c_size_t(0)
     _check("pa_decode_cascade_workspace_size",
            lib.pa_decode_cascade_workspace_size(ctypes.byref(describe(q)),
@@ -270,7 +279,7 @@ def decode_cascade_workspace_size(q, key_cache, block_tables, prefix_blocks, par
 
 def decode_cascade(q, key_cache, value_cache, block_tables, seq_lens, prefix_blocks, scale,
                    out=None, k_scale=1.0, v_scale=1.0, partition_tokens=0, variant=VARIANT_AUTO,
-                   workspace=None, err_flag=None, events=None, stream=None):
+                   workspace=None, err_flag=None, events=None, stream=None, bf16_partials=False):
     """pa_decode for a batch whose sequences share their first prefix_blocks
     blocks: the shared blocks are read once per group of sequences."""
     lib = _load()
@@ -280,10 +289,11 @@ def decode_cascade(q, key_cache, value_cache, block_tables, seq_lens, prefix_blo
             out = torch.empty_like(q)
         if workspace is None:
             need = decode_cascade_workspace_size(q, key_cache, block_tables, prefix_blocks,
-                                                 partition_tokens, variant)
+                                                 partition_tokens, variant, bf16_partials)
             if need:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events)
+    o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events,
+              bf16_partials)
     args = [describe(x) for x in (q, key_cache, value_cache, block_tables, seq_lens)]
     _check("pa_decode_cascade",
            lib.pa_decode_cascade(*[ctypes.byref(x) for x in args], int(prefix_blocks),
@@ -293,9 +303,9 @@ def decode_cascade(q, key_cache, value_cache, block_tables, seq_lens, prefix_blo
 
 
 def decode_multi_workspace_size(q, max_query_len, key_cache, block_tables, partition_tokens=0,
-                                variant=VARIANT_AUTO) -> int:
+                                variant=VARIANT_AUTO, bf16_partials=False) -> int:
     lib = _load()
-    o = _opts(partition_tokens=partition_tokens, variant=variant)
+    o = _opts(partition_tokens=partition_tokens, variant=variant, bf16_partials=bf16_partials)
     n = ctypes.c_size_t(0)
     _check("pa_decode_multi_workspace_size",
            lib.pa_decode_multi_workspace_size(ctypes.byref(describe(q)), int(max_query_len),
@@ -307,7 +317,8 @@ def decode_multi_workspace_size(q, max_query_len, key_cache, block_tables, parti
 
 def decode_multi(q, query_start_loc, max_query_len, key_cache, value_cache, block_tables,
                  seq_lens, scale, out=None, k_scale=1.0, v_scale=1.0, partition_tokens=0,
-                 variant=VARIANT_AUTO, workspace=None, err_flag=None, events=None, stream=None):
+                 variant=VARIANT_AUTO, workspace=None, err_flag=None, events=None, stream=None,
+                 bf16_partials=False):
     """Paged attention of several new query tokens per sequence (causal within
     them); q, out [T, H, D] bf16, query_start_loc int32 [S+1]."""
     lib = _load()
@@ -317,10 +328,11 @@ def decode_multi(q, query_start_loc, max_query_len, key_cache, value_cache, bloc
             out = torch.empty_like(q)
         if workspace is None:
             need = decode_multi_workspace_size(q, max_query_len, key_cache, block_tables,
-                                               partition_tokens, variant)
+                                               partition_tokens, variant, bf16_partials)
             if need:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events)
+    o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events,
+              bf16_partials)
     d_q, d_qsl = describe(q), describe(query_start_loc)
     args = [describe(x) for x in (key_cache, value_cache, block_tables, seq_lens)]
     _check("pa_decode_multi",

@@ -298,12 +298,7 @@ __device__ __forceinline__ void prefix_item(const CascadePrefixArgs &a, int item
         const int r = row0 + 16 * nt + c16;
         if (r >= R)
             continue;
-        uint16_t *o = a.p_acc + (pbase + r) * D + 4 * g4;
-#pragma unroll
-        for (int d = 0; d < ND; ++d)
-            *reinterpret_cast<uint2 *>(o + 16 * d) =
-                make_uint2(pack_bf16x2(acc[nt][d][0] * a.v_scale, acc[nt][d][1] * a.v_scale),
-                           pack_bf16x2(acc[nt][d][2] * a.v_scale, acc[nt][d][3] * a.v_scale));
+        store_partial<ND>(a.p_acc, pbase + r, g4, acc[nt], a.v_scale, a.partials_bf16);
         if (g4 == 0)
             *reinterpret_cast<float2 *>(a.p_ml + (pbase + r) * 2) = make_float2(m[nt], lt);
     }
@@ -393,28 +388,34 @@ __device__ __forceinline__ void lse_fold(Lse &s, const Lse &t)
 }
 
 // Fold parts [first, last] of one partial source (part stride rps rows, row
-// prow) into st; the lanes' groups take parts p0, p0 + step, ...
-template <int D>
-__device__ __forceinline__ void add_parts(Lse &st, const uint16_t *acc_ws, const float *ml_ws,
+// prow; accumulators f32, or bf16 with ACC_BF16) into st; the lanes' groups
+// take parts p0, p0 + step, ...
+template <int D, bool ACC_BF16>
+__device__ __forceinline__ void add_parts(Lse &st, const void *acc_ws, const float *ml_ws,
                                           int first, int last, int64_t rps, int64_t prow, int col,
                                           int p0, int step)
 {
     const float2 *ml = reinterpret_cast<const float2 *>(ml_ws) + (int64_t)first * rps + prow;
-    const uint16_t *acc = acc_ws + ((int64_t)first * rps + prow) * D + col;
+    const int64_t acc0 = ((int64_t)first * rps + prow) * D + col;
     const int n = last - first + 1;
-    auto bf16x4_at = [&](int p) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(acc + (int64_t)p * rps * D);
-        return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                           __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+    auto acc_at = [&](int p) {
+        const int64_t e = acc0 + (int64_t)p * rps * D;
+        if constexpr (ACC_BF16) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(acc_ws) + e);
+            return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+        } else {
+            return *reinterpret_cast<const float4 *>(static_cast<const float *>(acc_ws) + e);
+        }
     };
     for (int p = p0; p < n; p += 2 * step) {
         float2 m0 = make_float2(-INFINITY, 0.f), m1 = m0;
         float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
         m0 = ml[(int64_t)p * rps];
-        x0 = bf16x4_at(p);
+        x0 = acc_at(p);
         if (p + step < n) {
             m1 = ml[(int64_t)(p + step) * rps];
-            x1 = bf16x4_at(p + step);
+            x1 = acc_at(p + step);
         }
         lse_add(st, m0.x, m0.y, x0);
         lse_add(st, m1.x, m1.y, x1);
@@ -422,7 +423,7 @@ __device__ __forceinline__ void add_parts(Lse &st, const uint16_t *acc_ws, const
 }
 
 // One wavefront per (sequence, head) row, four rows per workgroup.
-template <int OT, int D>
+template <int OT, bool ACC_BF16, int D>
 __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(CascadeMergeArgs a)
 {
     constexpr int LPP = D / 4;                   // lanes per partial row
@@ -444,11 +445,11 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(CascadeMergeArg
     Lse st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
     {                                            // the shared prefix: one part per split
         const int64_t R = (int64_t)a.num_seqs * G;
-        add_parts<D>(st, a.p_acc, a.p_ml, 0, a.num_splits - 1, Hkv * R,
+        add_parts<D, ACC_BF16>(st, a.p_acc, a.p_ml, 0, a.num_splits - 1, Hkv * R,
                      kvh * R + (int64_t)s * G + h % G, col, sub, PPW);
     }
     if (min(L, a.capacity) > a.prefix_tokens)    // the sequence's own blocks
-        add_parts<D>(st, a.s_acc, a.s_ml, rec.x, rec.y, G, h % G, col, sub, PPW);
+        add_parts<D, ACC_BF16>(st, a.s_acc, a.s_ml, rec.x, rec.y, G, h % G, col, sub, PPW);
 #pragma unroll
     for (int off = LPP; off < 64; off <<= 1) {
         Lse t;
@@ -545,10 +546,16 @@ hipError_t launch_cascade_merge(const CascadeMergeArgs &a, int out_type, int hea
 {
     const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
     dim3 grid((unsigned)((rows + 3) / 4)), block(kThreads);
-    if (out_type == KT_BF16 && head_dim == 64)
-        hipLaunchKernelGGL((cascade_merge_kernel<KT_BF16, 64>), grid, block, 0, stream, a);
-    else if (out_type == KT_BF16 && head_dim == 128)
-        hipLaunchKernelGGL((cascade_merge_kernel<KT_BF16, 128>), grid, block, 0, stream, a);
+    if (out_type != KT_BF16)
+        return hipErrorInvalidValue;
+    if (head_dim == 64 && a.partials_bf16)
+        hipLaunchKernelGGL((cascade_merge_kernel<KT_BF16, true, 64>), grid, block, 0, stream, a);
+    else if (head_dim == 64)
+        hipLaunchKernelGGL((cascade_merge_kernel<KT_BF16, false, 64>), grid, block, 0, stream, a);
+    else if (head_dim == 128 && a.partials_bf16)
+        hipLaunchKernelGGL((cascade_merge_kernel<KT_BF16, true, 128>), grid, block, 0, stream, a);
+    else if (head_dim == 128)
+        hipLaunchKernelGGL((cascade_merge_kernel<KT_BF16, false, 128>), grid, block, 0, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

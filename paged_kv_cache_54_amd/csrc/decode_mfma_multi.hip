@@ -105,12 +105,7 @@ struct MultiCols {
                                    pack_bf16x2(acc[nt][d][2] * inv, acc[nt][d][3] * inv));
             } else {
                 const int64_t pi = (int64_t)slot * RPS + col0 + 16 * nt + c16;
-                uint16_t *o = static_cast<uint16_t *>(a.ws_acc) + pi * D + 4 * g4;
-#pragma unroll
-                for (int d = 0; d < ND; ++d)
-                    *reinterpret_cast<uint2 *>(o + 16 * d) = make_uint2(
-                        pack_bf16x2(acc[nt][d][0] * a.v_scale, acc[nt][d][1] * a.v_scale),
-                        pack_bf16x2(acc[nt][d][2] * a.v_scale, acc[nt][d][3] * a.v_scale));
+                store_partial<ND>(a.ws_acc, pi, g4, acc[nt], a.v_scale, a.flags & kPartialsBf16);
                 if (g4 == 0)
                     *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m[nt], lt);
             }

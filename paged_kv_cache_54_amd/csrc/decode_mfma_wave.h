@@ -118,12 +118,7 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
                                pack_bf16x2(acc[d][2] * inv, acc[d][3] * inv));
         } else {
             const int64_t pi = (int64_t)slot * G + c16;
-            uint16_t *o = static_cast<uint16_t *>(a.ws_acc) + pi * D + 4 * g4;
-#pragma unroll
-            for (int d = 0; d < ND; ++d)
-                *reinterpret_cast<uint2 *>(o + 16 * d) =
-                    make_uint2(pack_bf16x2(acc[d][0] * a.v_scale, acc[d][1] * a.v_scale),
-                               pack_bf16x2(acc[d][2] * a.v_scale, acc[d][3] * a.v_scale));
+            store_partial<ND>(a.ws_acc, pi, g4, acc, a.v_scale, a.flags & kPartialsBf16);
             if (g4 == 0)
                 *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m, lt);
         }

@@ -113,7 +113,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a)
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     o[i] = acc[g][i] * a.v_scale;
-                store8<QT>(a.ws_acc, pi * D + ch * 8, o);
+                if (QT == KT_BF16 && (a.flags & kPartialsBf16))
+                    store8<KT_BF16>(a.ws_acc, pi * D + ch * 8, o);
+                else
+                    store8<KT_F32>(a.ws_acc, pi * D + ch * 8, o);
                 if (ch == 0)
                     *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m[g], l[g]);
             }

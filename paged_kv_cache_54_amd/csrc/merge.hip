@@ -65,8 +65,9 @@ __device__ __forceinline__ void lse_fold(Lse &s, const Lse &t)
 }
 
 // WPR wavefronts per row, or (WPR = 0) two rows per wavefront, one per
-// 32-lane half; NW wavefronts per workgroup.
-template <int OT, int D, int WPR, int NW = 4>
+// 32-lane half; NW wavefronts per workgroup.  Partial accumulators are f32,
+// or bf16 with ACC_BF16.
+template <int OT, bool ACC_BF16, int D, int WPR, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void merge_kernel(DecodeArgs a, int block_size,
                                                         int64_t num_rows)
 {
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(64 * NW) void merge_kernel(DecodeArgs a, int block_
     if (live && !zero_row) {
         // partial p of this row: slot first + p, row prow
         const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (int64_t)first * RPS + prow;
-        using AT = typename std::conditional<OT == KT_F32, float, uint16_t>::type;
+        using AT = typename std::conditional<ACC_BF16, uint16_t, float>::type;
         const AT *acc = static_cast<const AT *>(a.ws_acc) + ((int64_t)first * RPS + prow) * D + col;
         const int stride = (WPR > 1 ? WPR : 1) * PPW;
         for (int p0 = wr * PPW + sub; p0 < n; p0 += UNROLL * stride) {
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(64 * NW) void merge_kernel(DecodeArgs a, int block_
                 const int p = p0 + u * stride;
                 if (p < n) {
                     mlv[u] = ml[(int64_t)p * RPS];
-                    if constexpr (OT == KT_F32) {
+                    if constexpr (!ACC_BF16) {
                         x[u] = *reinterpret_cast<const float4 *>(acc + (int64_t)p * RPS * D);
                     } else {
                         const uint2 v = *reinterpret_cast<const uint2 *>(acc + (int64_t)p * RPS * D);
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(64 * NW) void merge_kernel(DecodeArgs a, int block_
     }
 }
 
-template <int OT, int D>
+template <int OT, bool ACC_BF16, int D>
 hipError_t launch(const DecodeArgs &a, int block_size, int64_t rows, hipStream_t stream)
 {
     // Few rows: their sequences are long and cut into many parts; give each
@@ -210,12 +211,12 @@ hipError_t launch(const DecodeArgs &a, int block_size, int64_t rows, hipStream_t
         return hipErrorInvalidValue;
     dim3 grid((unsigned)wgs), block(kMergeThreads);
     if (wide)
-        hipLaunchKernelGGL((merge_kernel<OT, D, 8, 8>), grid, dim3(512), 0, stream, a, block_size,
+        hipLaunchKernelGGL((merge_kernel<OT, ACC_BF16, D, 8, 8>), grid, dim3(512), 0, stream, a, block_size,
                            rows);
     else if (packed)
-        hipLaunchKernelGGL((merge_kernel<OT, D, 0>), grid, block, 0, stream, a, block_size, rows);
+        hipLaunchKernelGGL((merge_kernel<OT, ACC_BF16, D, 0>), grid, block, 0, stream, a, block_size, rows);
     else
-        hipLaunchKernelGGL((merge_kernel<OT, D, 1>), grid, block, 0, stream, a, block_size, rows);
+        hipLaunchKernelGGL((merge_kernel<OT, ACC_BF16, D, 1>), grid, block, 0, stream, a, block_size, rows);
     return hipGetLastError();
 }
 
@@ -226,14 +227,17 @@ hipError_t launch_merge(const DecodeArgs &a, int out_type, int head_dim, int blo
 {
     const int64_t rows = (int64_t)a.num_seqs * a.num_heads *
                          (a.query_start_loc ? a.max_query_len : 1);
-    if (out_type == KT_F32 && head_dim == 64)
-        return launch<KT_F32, 64>(a, block_size, rows, stream);
-    if (out_type == KT_F32 && head_dim == 128)
-        return launch<KT_F32, 128>(a, block_size, rows, stream);
+    const bool acc_bf16 = (a.flags & kPartialsBf16) != 0;
+    if (out_type == KT_F32 && !acc_bf16 && head_dim == 64)
+        return launch<KT_F32, false, 64>(a, block_size, rows, stream);
+    if (out_type == KT_F32 && !acc_bf16 && head_dim == 128)
+        return launch<KT_F32, false, 128>(a, block_size, rows, stream);
     if (out_type == KT_BF16 && head_dim == 64)
-        return launch<KT_BF16, 64>(a, block_size, rows, stream);
+        return acc_bf16 ? launch<KT_BF16, true, 64>(a, block_size, rows, stream)
+                        : launch<KT_BF16, false, 64>(a, block_size, rows, stream);
     if (out_type == KT_BF16 && head_dim == 128)
-        return launch<KT_BF16, 128>(a, block_size, rows, stream);
+        return acc_bf16 ? launch<KT_BF16, true, 128>(a, block_size, rows, stream)
+                        : launch<KT_BF16, false, 128>(a, block_size, rows, stream);
     return hipErrorInvalidValue;
 }
 

@@ -51,6 +51,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// Store one column's unnormalised partial accumulator row `row` of a
+// workspace whose rows are D = 16 * ND values: lane group g4 holds dims
+// 16 * d + 4 * g4 .. + 3 of the MFMA output in acc[d].  Each value is
+// multiplied by `scale`, then stored as f32 (16-byte stores) or, with bf16,
+// rounded to nearest even bf16.
+template <int ND>
+__device__ __forceinline__ void store_partial(void *ws_acc, int64_t row, int g4,
+                                              const f32x4 (&acc)[ND], float scale, bool bf16)
+{
+    constexpr int D = 16 * ND;
+    if (bf16) {
+        uint16_t *o = static_cast<uint16_t *>(ws_acc) + row * D + 4 * g4;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            *reinterpret_cast<uint2 *>(o + 16 * d) =
+                make_uint2(pack_bf16x2(acc[d][0] * scale, acc[d][1] * scale),
+                           pack_bf16x2(acc[d][2] * scale, acc[d][3] * scale));
+    } else {
+        float *o = static_cast<float *>(ws_acc) + row * D + 4 * g4;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+            *reinterpret_cast<float4 *>(o + 16 * d) =
+                make_float4(acc[d][0] * scale, acc[d][1] * scale, acc[d][2] * scale,
+                            acc[d][3] * scale);
+    }
+}
+
 // Max and sum over the four 16-lane rows (lanes c, c + 16, c + 32, c + 48):
 // gfx950's row-swap permutes exchange rows 0<->1, 2<->3 (16-lane swap) and
 // the two halves (32-lane swap) on the vector ALU, with no LDS round trip.

@@ -101,15 +101,16 @@ struct DecodePlan {
     int64_t chunk_units;     // units per chunk, 0 = balanced over the waves
     int64_t waves;           // grid size
     int64_t slots;           // partial slots = waves + segments
+    bool acc_bf16;           // partial accumulators stored as bf16
     size_t ws_bytes;
 };
 
-// Workspace layout: acc [slots, rows, D] f32 | ml [slots, rows, 2] f32 | seg [S*Hkv, 2] i32
-// Partial accumulators are stored in the output's type (bf16 halves the
-// bytes a split segment writes and the merge reads), (m, l) in f32.
+// Workspace layout: acc [slots, rows, D] | ml [slots, rows, 2] f32 | seg [S*Hkv, 2] i32
+// Partial accumulators are f32; PA_PARTIALS_BF16 stores them as bf16 for a
+// bf16 output (half the bytes a split segment writes and the merge reads).
 size_t acc_bytes(const DecodePlan &p)
 {
-    return (p.q_type == KT_F32 ? 4 : 2) * (size_t)(p.slots * p.rows) * (size_t)p.D;
+    return (p.acc_bf16 ? 2 : 4) * (size_t)(p.slots * p.rows) * (size_t)p.D;
 }
 
 size_t workspace_bytes(const DecodePlan &p)
@@ -190,6 +191,11 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
         return PA_ERR_UNSUPPORTED;
     p->q_type = kv_type_of(q->dtype);
     p->kv_type = kvt;
+
+    const int partials = opts ? opts->partials : PA_PARTIALS_F32;
+    if (partials != PA_PARTIALS_F32 && partials != PA_PARTIALS_BF16)
+        return PA_ERR_UNSUPPORTED;
+    p->acc_bf16 = partials == PA_PARTIALS_BF16 && p->q_type == KT_BF16;
 
     const int variant = opts ? opts->variant : PA_VARIANT_AUTO;
     const bool mfma_ok = mfma_supported(p->q_type, kvt, (int)p->D, (int)p->bs, (int)p->G);
@@ -362,6 +368,9 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
         return PA_ERR_SHAPE;
     if (!isfinite(scale))
         return PA_ERR_UNSUPPORTED;
+    // a call with work reads table entries, each of which must name a block
+    if (S > 0 && q->shape[0] > 0 && key_cache->shape[0] < 1)
+        return PA_ERR_SHAPE;
     const bool fp8 = key_cache->dtype == PA_FP8_E4M3;
     const float ks = (fp8 && opts) ? opts->k_scale : 1.0f;
     const float vs = (fp8 && opts) ? opts->v_scale : 1.0f;
@@ -402,7 +411,7 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     a.log2_group = __builtin_ctz((unsigned)p.G);
     a.qk_scale_log2 = scale * kLog2e * ks;
     a.v_scale = vs;
-    a.flags = 0;
+    a.flags = p.acc_bf16 ? kPartialsBf16 : 0;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     hipEvent_t ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);
@@ -519,7 +528,7 @@ int plan_cascade(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt, i
         return PA_ERR_UNSUPPORTED;
     const size_t prow = (size_t)(c->P * Hkv * c->R);
     c->acc_off = 0;
-    c->ml_off = c->acc_off + align256(sizeof(uint16_t) * prow * (size_t)D);
+    c->ml_off = c->acc_off + align256((c->suf.acc_bf16 ? 2 : 4) * prow * (size_t)D);
     c->suf_off = c->ml_off + align256(sizeof(float) * prow * 2);
     c->total = S > 0 ? c->suf_off + align256(c->suf.ws_bytes) : 0;
     return PA_OK;
@@ -759,6 +768,8 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
         return PA_ERR_UNSUPPORTED;
     if (q->dtype != PA_BF16 || (opts && opts->variant == PA_VARIANT_VALU))
         return PA_ERR_UNSUPPORTED;
+    if (q->shape[0] > 0 && key_cache->shape[0] < 1)
+        return PA_ERR_SHAPE;
     const bool fp8 = key_cache->dtype == PA_FP8_E4M3;
     const float ks = (fp8 && opts) ? opts->k_scale : 1.0f;
     const float vs = (fp8 && opts) ? opts->v_scale : 1.0f;
@@ -782,7 +793,7 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     pr.value_cache = value_cache->data;
     pr.block_tables = static_cast<const int32_t *>(block_tables->data);
     pr.seq_lens = static_cast<const int32_t *>(seq_lens->data);
-    pr.p_acc = reinterpret_cast<uint16_t *>(ws + c.acc_off);
+    pr.p_acc = ws + c.acc_off;
     pr.p_ml = reinterpret_cast<float *>(ws + c.ml_off);
     pr.err_flag = opts->err_flag;
     pr.num_seqs = (int32_t)c.S;
@@ -800,6 +811,7 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     pr.items_per_xcd = (int32_t)c.per_xcd;
     pr.log2_group = __builtin_ctz((unsigned)c.G);
     pr.check_wgs = 0;   // the launcher sizes the check
+    pr.partials_bf16 = sp.acc_bf16;
     pr.qk_scale_log2 = scale * kLog2e * ks;
     pr.v_scale = vs;
 
@@ -830,11 +842,11 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     sa.log2_group = __builtin_ctz((unsigned)sp.G);
     sa.qk_scale_log2 = scale * kLog2e * ks;
     sa.v_scale = vs;
-    sa.flags = kPartialOnly;
+    sa.flags = kPartialOnly | (sp.acc_bf16 ? kPartialsBf16 : 0);
 
     CascadeMergeArgs ma;
     ma.out = out->data;
-    ma.s_acc = static_cast<const uint16_t *>(sa.ws_acc);
+    ma.s_acc = sa.ws_acc;
     ma.s_ml = sa.ws_ml;
     ma.s_seg = sa.ws_seg;
     ma.seq_lens = pr.seq_lens;
@@ -846,6 +858,7 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     ma.num_heads = (int32_t)sp.H;
     ma.num_kv_heads = (int32_t)sp.Hkv;
     ma.num_splits = (int32_t)c.P;
+    ma.partials_bf16 = sp.acc_bf16;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     hipEvent_t ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);

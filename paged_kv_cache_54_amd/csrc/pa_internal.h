@@ -25,8 +25,8 @@ struct DecodeArgs {
     const int32_t *block_tables; // [S, max_nb]
     const int32_t *seq_lens;     // [S]
     void *out;                   // [S, H, D]
-    void *ws_acc;                // [slots, rows, D] unnormalised partial outputs, in the
-                                 // output's type (bf16 or f32)
+    void *ws_acc;                // [slots, rows, D] unnormalised partial outputs: f32, or
+                                 // bf16 with kPartialsBf16
     float *ws_ml;                // [slots, rows, 2] (softmax base in log2 units, sum)
     int32_t *ws_seg;             // [S * Hkv, 2]   first and last slot of each segment
     uint32_t *err_flag;          // optional
@@ -41,13 +41,15 @@ struct DecodeArgs {
     int32_t log2_group;          // G = 2^log2_group
     float qk_scale_log2;         // scale * log2(e) * k_scale (k_scale = 1 unless fp8)
     float v_scale;               // 1 unless fp8
-    int32_t flags;               // kPartialOnly
+    int32_t flags;               // kPartialOnly | kPartialsBf16
 };
 
-// DecodeArgs.flags (matrix-core kernels).  kPartialOnly: every segment ends
+// DecodeArgs.flags.  kPartialOnly (matrix-core kernels): every segment ends
 // as a partial (acc, m, l), also one a single chunk covers, so that a second
-// pass can combine it with another source.
+// pass can combine it with another source.  kPartialsBf16: partial
+// accumulators are stored as bf16 (bf16 outputs only); otherwise f32.
 constexpr int32_t kPartialOnly = 1;
+constexpr int32_t kPartialsBf16 = 2;
 
 struct AppendArgs {
     const void *k;               // [T, Hkv, D]
@@ -121,13 +123,14 @@ struct CascadePrefixArgs {
     const void *key_cache, *value_cache;
     const int32_t *block_tables;  // [S, max_nb]
     const int32_t *seq_lens;      // [S]
-    uint16_t *p_acc;              // [P, Hkv, R, D] bf16
+    void *p_acc;                  // [P, Hkv, R, D] f32, or bf16 with partials_bf16
     float *p_ml;                  // [P, Hkv, R, 2]
     uint32_t *err_flag;
     int32_t num_seqs, num_heads, num_kv_heads, max_nb, num_blocks, block_size;
     int32_t prefix_blocks, num_splits, split_blocks;   // N, P, bps
     int32_t rows, row_blocks;                          // R, row blocks per KV head
     int32_t num_items, items_per_xcd, log2_group, check_wgs;
+    int32_t partials_bf16;        // prefix partial accumulators stored as bf16
     float qk_scale_log2, v_scale;
 };
 
@@ -135,14 +138,15 @@ struct CascadePrefixArgs {
 // prefix partials (layout above).
 struct CascadeMergeArgs {
     void *out;                    // [S, H, D]
-    const uint16_t *s_acc;        // suffix partials (bf16 acc, f32 m and l)
+    const void *s_acc;            // suffix partials (acc f32 or bf16, m and l f32)
     const float *s_ml;
     const int32_t *s_seg;
     const int32_t *seq_lens;      // [S]; a sequence's suffix is its tokens past N * bs
     int32_t prefix_tokens, capacity;   // N * bs, max_nb * bs
-    const uint16_t *p_acc;        // prefix partials
+    const void *p_acc;            // prefix partials (same types)
     const float *p_ml;
     int32_t num_seqs, num_heads, num_kv_heads, num_splits;
+    int32_t partials_bf16;        // both accumulators stored as bf16
 };
 
 // Launchers (defined in the .hip translation units).  Each returns a

@@ -45,48 +45,6 @@ def oracle_step(b):
     return oracle.reference_step(b)
 
 
-def oracle_rows(b, rows):
-    """Oracle output for flat rows s*H + h only: the host caches get the pool
-    rows of just the sequences those rows belong to (quantised by the oracle's
-    own append for an fp8 cache), then every new row, then decode."""
-    rows = np.asarray(rows, dtype=np.int64)
-    seqs = np.unique(rows // b.num_heads)
-    NB, bs, Hkv, D = b.num_blocks, b.block_size, b.num_kv_heads, b.head_dim
-    tables = b.block_tables.cpu().numpy()
-    lens = b.seq_lens.cpu().numpy()
-    blocks = np.unique(np.concatenate([tables[s, :-(-int(lens[s]) // bs)] for s in seqs]))
-    slots = (blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1)
-    slots_t = torch.from_numpy(slots)
-    kp = b.key_pool.view(NB * bs, Hkv, D)[slots_t.to(b.key_pool.device)].cpu()
-    vp = b.value_pool.view(NB * bs, Hkv, D)[slots_t.to(b.key_pool.device)].cpu()
-    kc, vc = oracle.fill_cache(b, kp, vp, slots_t)
-    oracle.kv_append(b.k_new.cpu(), b.v_new.cpu(), b.slot_mapping.cpu(), kc, vc, b.k_scale,
-                     b.v_scale)
-    out = oracle.decode(b.q.cpu(), kc, vc, tables, lens, b.scale, b.k_scale, b.v_scale, rows=rows)
-    return out, kc, vc, slots
-
-
-def oracle_rows_multi(b, rows):
-    """Oracle output for flat rows token*H + h of a multi-token batch: host
-    caches hold the pool blocks of those rows' sequences (the oracle's own
-    append), then every new row; then multi-token decode of those rows."""
-    rows = np.asarray(rows, dtype=np.int64)
-    qsl = b.query_start_loc.cpu().numpy()
-    seqs = np.unique(np.searchsorted(qsl, rows // b.num_heads, side="right") - 1)
-    NB, bs, Hkv, D = b.num_blocks, b.block_size, b.num_kv_heads, b.head_dim
-    tables = b.block_tables.cpu().numpy()
-    lens = b.seq_lens.cpu().numpy()
-    blocks = np.unique(np.concatenate([tables[s, :-(-int(lens[s]) // bs)] for s in seqs]))
-    slots_t = torch.from_numpy((blocks[:, None] * bs + np.arange(bs)[None, :]).reshape(-1))
-    kp = b.key_pool.view(NB * bs, Hkv, D)[slots_t.to(b.key_pool.device)].cpu()
-    vp = b.value_pool.view(NB * bs, Hkv, D)[slots_t.to(b.key_pool.device)].cpu()
-    kc, vc = oracle.fill_cache(b, kp, vp, slots_t)
-    oracle.kv_append(b.k_new.cpu(), b.v_new.cpu(), b.slot_mapping.cpu(), kc, vc, b.k_scale,
-                     b.v_scale)
-    return oracle.decode_multi(b.q.cpu(), b.query_start_loc.cpu(), kc, vc, tables, lens,
-                               b.scale, b.k_scale, b.v_scale, rows=rows)
-
-
 def check_close(got, ref, cache_dtype, what=""):
     """The tolerances of the decode path: f32 max abs error <= 1e-5; bf16
     |gpu - ref| <= 1e-2 + 1e-2 |ref| elementwise; fp8 KV max abs error <= 3e-2
@@ -106,14 +64,26 @@ def check_close(got, ref, cache_dtype, what=""):
     return float(err.max())
 
 
-def sample_rows(b, n=12, seed=0):
-    """Flat rows s*H + h covering the longest and shortest sequence, the
-    first and last head, and random others."""
-    rng = np.random.default_rng(seed)
+def negative_control(b, out, hk, hv):
+    """Show that the whole-batch comparison can fail: the oracle is rerun on
+    the host caches with one block-table entry of the shortest sequence
+    pointing at the block before it (the mistake a wrong table walk would
+    make), and that sequence's GPU rows must then fall outside the
+    tolerance.  The wrong entry is planted only in the oracle's input."""
     lens = b.seq_lens.cpu().numpy()
-    H = b.num_heads
-    picks = {int(np.argmax(lens)) * H + H - 1, int(np.argmin(lens)) * H, 0,
-             (b.num_seqs - 1) * H + H // 2}
-    while len(picks) < min(n, b.num_seqs * H):
-        picks.add(int(rng.integers(0, b.num_seqs * H)))
-    return np.array(sorted(picks), dtype=np.int64)
+    s = int(np.argmin(lens))
+    nb = -(-int(lens[s]) // b.block_size)
+    assert nb >= 2, "the control needs a sequence of two blocks or more"
+    j = nb // 2
+    tables = b.block_tables.cpu().numpy().copy()
+    tables[s, j] = tables[s, j - 1]
+    H, D = b.num_heads, b.head_dim
+    rows = np.arange(s * H, (s + 1) * H, dtype=np.int64)
+    wrong = oracle.decode(b.q.cpu(), hk, hv, tables, lens, b.scale, b.k_scale, b.v_scale,
+                          rows=rows)
+    got = out.reshape(-1, D)[torch.from_numpy(rows).to(out.device)]
+    try:
+        check_close(got, wrong, b.cache_dtype, "negative control")
+    except AssertionError:
+        return s, j
+    raise AssertionError(f"a wrong block (sequence {s}, block {j}) went undetected")

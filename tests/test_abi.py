@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert pa.version() == 1
+    assert pa.version() == 2
     for code in range(9):
         assert pa.status_string(code) and pa.status_string(code) != "unknown status"
     assert pa.status_string(99) == "unknown status"
@@ -63,6 +63,7 @@ def test_opts_init_defaults():
     assert (o.k_scale, o.v_scale, o.partition_tokens, o.variant) == (1.0, 1.0, 0, 0)
     assert not o.workspace and o.workspace_bytes == 0 and not o.err_flag
     assert not o.kernel_events[0] and not o.kernel_events[1]
+    assert o.partials == pa.PARTIALS_F32
 
 
 def desc(shape, dtype, data=FAKE, strides=None):
@@ -137,6 +138,11 @@ def test_decode_validation_errors():
     assert call_decode(decode_args(), opts(variant=2)) == PA_ERR_UNSUPPORTED   # no MFMA for f32
     assert call_decode(decode_args(qd=BF16, kd=FP8), opts(k_scale=0.0)) == PA_ERR_UNSUPPORTED
     assert call_decode(decode_args(), scale=float("nan")) == PA_ERR_UNSUPPORTED
+    assert call_decode(decode_args(), opts(partials=2)) == PA_ERR_UNSUPPORTED
+    # a pool with no blocks cannot hold any table entry a kernel would read
+    assert call_decode(decode_args(NB=0), opts(partition_tokens=16)) == PA_ERR_SHAPE
+    assert call_decode(decode_args(NB=0, qd=BF16, kd=BF16)) == PA_ERR_SHAPE
+    assert call_decode(decode_args(NB=0, S=0)) == PA_OK                  # nothing to launch
     # every call with work needs a workspace of the planned size
     assert call_decode(decode_args(), opts(partition_tokens=16)) == PA_ERR_WORKSPACE
     assert call_decode(decode_args(), opts(partition_tokens=1024)) == PA_ERR_WORKSPACE
@@ -146,8 +152,8 @@ def test_decode_validation_errors():
 
 def ws_bytes(S, H, Hkv, D, max_nb, chunk_units, acc_elt=4, rows=None):
     """Workspace of a fixed-chunk plan: partial slots = chunks + segments, each
-    holding `rows` (G) rows of D accumulators in the output's type (acc_elt
-    bytes) plus an f32 (max, sum); two ints per segment."""
+    holding `rows` (G) rows of D accumulators (acc_elt bytes: 4 for fp32
+    partials, 2 for bf16 ones) plus an f32 (max, sum); two ints per segment."""
     rows = H // Hkv if rows is None else rows
     chunks = -(-S * Hkv * max_nb // chunk_units)
     slots = chunks + S * Hkv
@@ -164,15 +170,20 @@ def test_workspace_size_formula():
                                             ctypes.byref(n))
         assert rc == PA_OK
         assert n.value == ws_bytes(3, 8, 2, 64, 10, P // 16)
-    # a bf16 output keeps its partial accumulators in bf16
+    # a bf16 output keeps fp32 partial accumulators unless bf16 ones are asked for;
+    # an f32 output keeps fp32 ones either way
     b = decode_args(S=3, H=8, Hkv=2, D=64, bs=16, max_nb=10, qd=BF16, kd=BF16)
     for P in (32, 160):
-        rc = lib().pa_decode_workspace_size(ctypes.byref(b["q"]), ctypes.byref(b["kc"]),
-                                            ctypes.byref(b["bt"]),
-                                            ctypes.byref(opts(partition_tokens=P)),
-                                            ctypes.byref(n))
-        assert rc == PA_OK
-        assert n.value == ws_bytes(3, 8, 2, 64, 10, P // 16, acc_elt=2)
+        for partials, elt in ((pa.PARTIALS_F32, 4), (pa.PARTIALS_BF16, 2)):
+            rc = lib().pa_decode_workspace_size(
+                ctypes.byref(b["q"]), ctypes.byref(b["kc"]), ctypes.byref(b["bt"]),
+                ctypes.byref(opts(partition_tokens=P, partials=partials)), ctypes.byref(n))
+            assert rc == PA_OK
+            assert n.value == ws_bytes(3, 8, 2, 64, 10, P // 16, acc_elt=elt)
+        rc = lib().pa_decode_workspace_size(
+            ctypes.byref(a["q"]), ctypes.byref(a["kc"]), ctypes.byref(a["bt"]),
+            ctypes.byref(opts(partition_tokens=P, partials=pa.PARTIALS_BF16)), ctypes.byref(n))
+        assert rc == PA_OK and n.value == ws_bytes(3, 8, 2, 64, 10, P // 16)
     assert lib().pa_decode_workspace_size(None, ctypes.byref(a["kc"]), ctypes.byref(a["bt"]),
                                           None, ctypes.byref(n)) == PA_ERR_NULL
 
@@ -266,6 +277,7 @@ def test_decode_multi_validation_errors():
     b["lens"] = desc([2], I32)
     assert call_multi(b, qsl, 4) == PA_ERR_SHAPE
     assert call_multi(a, qsl, 4, opts(partition_tokens=16)) == PA_ERR_WORKSPACE
+    assert call_multi(*multi_args(NB=0), 4, opts(partition_tokens=16)) == PA_ERR_SHAPE
 
 
 def test_decode_multi_workspace_formula():
@@ -277,7 +289,7 @@ def test_decode_multi_workspace_formula():
                                                   ctypes.byref(opts(partition_tokens=P)),
                                                   ctypes.byref(n))
         assert rc == PA_OK
-        assert n.value == ws_bytes(3, 8, 2, 64, 10, P // 16, acc_elt=2, rows=4 * qm)
+        assert n.value == ws_bytes(3, 8, 2, 64, 10, P // 16, acc_elt=4, rows=4 * qm)
 
 
 def test_prepare_step_validation_errors():
@@ -313,6 +325,8 @@ def test_decode_cascade_validation_errors():
     b = decode_args(S=4, H=8, Hkv=2, D=128, max_nb=8, qd=BF16, kd=BF16)
     b["bt"] = desc([3, 8], I32)
     assert call(b, 2) == PA_ERR_SHAPE
+    assert call(decode_args(S=4, H=8, Hkv=2, D=128, NB=0, max_nb=8, qd=BF16, kd=BF16), 2) \
+        == PA_ERR_SHAPE                                            # empty pool
     # a table row of more than 2^31 token positions, though its suffix is short
     wide = (1 << 27) + 8
     c = decode_args(S=4, H=8, Hkv=2, D=128, max_nb=wide, qd=BF16, kd=BF16)
