@@ -78,7 +78,7 @@ __device__ __forceinline__ void stage_chunk(uint8_t *tile, int row, int chunk, u
 // one of two LDS buffers (kt0/vt0 + buffer * tile bytes) and, after a
 // barrier, read by all four.  DEPTH tiles are in flight in registers.  Every
 // prefix token is valid (the contract), so no masking.
-template <int KT, int D, int BS, int NTW>
+template <int KT, int D, int BS, int NTW, bool AB>
 __device__ __forceinline__ void prefix_item(const CascadePrefixArgs &a, int item, uint8_t *kt0,
                                             uint8_t *vt0)
 {
@@ -298,7 +298,7 @@ __device__ __forceinline__ void prefix_item(const CascadePrefixArgs &a, int item
         const int r = row0 + 16 * nt + c16;
         if (r >= R)
             continue;
-        store_partial<ND>(a.p_acc, pbase + r, g4, acc[nt], a.v_scale, a.partials_bf16);
+        store_partial<ND, AB>(a.p_acc, pbase + r, g4, acc[nt], a.v_scale);
         if (g4 == 0)
             *reinterpret_cast<float2 *>(a.p_ml + (pbase + r) * 2) = make_float2(m[nt], lt);
     }
@@ -324,7 +324,8 @@ constexpr int cascade_waves_per_simd()
     return (KT == KT_BF16 && D == 128 && BS == 16) ? 3 : 1;
 }
 
-template <int KT, int D, int BS, int NTW, int G>
+// AB: partial accumulators (prefix and suffix) stored as bf16, else f32.
+template <int KT, int D, int BS, int NTW, int G, bool AB>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(cascade_waves_per_simd<KT, D, BS>()))) void cascade_kernel(
     CascadePrefixArgs p, DecodeArgs s)
@@ -340,7 +341,7 @@ __attribute__((amdgpu_waves_per_eu(cascade_waves_per_simd<KT, D, BS>()))) void c
     if (wg < item_wgs) {
         const int item = (wg & 7) * p.items_per_xcd + (wg >> 3);
         if (item < p.num_items)
-            prefix_item<KT, D, BS, NTW>(p, item, lds, vt0);
+            prefix_item<KT, D, BS, NTW, AB>(p, item, lds, vt0);
         return;
     }
     wg -= item_wgs;
@@ -352,7 +353,7 @@ __attribute__((amdgpu_waves_per_eu(cascade_waves_per_simd<KT, D, BS>()))) void c
     const int wave = threadIdx.x >> 6;
     // wavefronts past s.num_waves get no chunk
     const TableView view{p.max_nb, p.prefix_blocks * p.block_size};
-    decode_mfma_wave<KT, D, BS, G>(s, view, wg * kSuffixWaves + wave, lds + wave * KTILE,
+    decode_mfma_wave<KT, D, BS, G, AB>(s, view, wg * kSuffixWaves + wave, lds + wave * KTILE,
                                    vt0 + wave * VTILE);
 }
 
@@ -478,25 +479,36 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(CascadeMergeArg
 
 typedef void (*CascadeKernel)(CascadePrefixArgs, DecodeArgs);
 
-template <int KT, int D, int BS>
+template <int KT, int D, int BS, bool AB>
 CascadeKernel pick_g(int group)
 {
     switch (group) {
-    case 1: return cascade_kernel<KT, D, BS, kPrefixColTiles, 1>;
-    case 2: return cascade_kernel<KT, D, BS, kPrefixColTiles, 2>;
-    case 4: return cascade_kernel<KT, D, BS, kPrefixColTiles, 4>;
-    case 8: return cascade_kernel<KT, D, BS, kPrefixColTiles, 8>;
+    case 1: return cascade_kernel<KT, D, BS, kPrefixColTiles, 1, AB>;
+    case 2: return cascade_kernel<KT, D, BS, kPrefixColTiles, 2, AB>;
+    case 4: return cascade_kernel<KT, D, BS, kPrefixColTiles, 4, AB>;
+    case 8: return cascade_kernel<KT, D, BS, kPrefixColTiles, 8, AB>;
     default: return nullptr;
     }
 }
 
-template <int KT>
+template <int KT, bool AB>
 CascadeKernel pick_shape(int d, int bs, int group)
 {
-    if (d == 64 && bs == 16) return pick_g<KT, 64, 16>(group);
-    if (d == 64 && bs == 32) return pick_g<KT, 64, 32>(group);
-    if (d == 128 && bs == 16) return pick_g<KT, 128, 16>(group);
-    if (d == 128 && bs == 32) return pick_g<KT, 128, 32>(group);
+    if (d == 64 && bs == 16) return pick_g<KT, 64, 16, AB>(group);
+    if (d == 64 && bs == 32) return pick_g<KT, 64, 32, AB>(group);
+    if (d == 128 && bs == 16) return pick_g<KT, 128, 16, AB>(group);
+    if (d == 128 && bs == 32) return pick_g<KT, 128, 32, AB>(group);
+    return nullptr;
+}
+
+CascadeKernel pick(int kv_type, int d, int bs, int group, bool acc_bf16)
+{
+    if (kv_type == KT_BF16)
+        return acc_bf16 ? pick_shape<KT_BF16, true>(d, bs, group)
+                        : pick_shape<KT_BF16, false>(d, bs, group);
+    if (kv_type == KT_E4M3)
+        return acc_bf16 ? pick_shape<KT_E4M3, true>(d, bs, group)
+                        : pick_shape<KT_E4M3, false>(d, bs, group);
     return nullptr;
 }
 
@@ -505,11 +517,9 @@ CascadeKernel pick_shape(int d, int bs, int group)
 int cascade_prefix_rows() { return kPrefixWaves * 16 * kPrefixColTiles; }
 
 hipError_t cascade_suffix_occupancy(int kv_type, int head_dim, int block_size, int group,
-                                    int *waves_per_cu)
+                                    bool acc_bf16, int *waves_per_cu)
 {
-    const CascadeKernel k = kv_type == KT_BF16   ? pick_shape<KT_BF16>(head_dim, block_size, group)
-                            : kv_type == KT_E4M3 ? pick_shape<KT_E4M3>(head_dim, block_size, group)
-                                                 : nullptr;
+    const CascadeKernel k = pick(kv_type, head_dim, block_size, group, acc_bf16);
     if (!k)
         return hipErrorInvalidValue;
     int wgs = 0;
@@ -522,9 +532,7 @@ hipError_t cascade_suffix_occupancy(int kv_type, int head_dim, int block_size, i
 hipError_t launch_cascade(const CascadePrefixArgs &p, const DecodeArgs &s, int kv_type,
                           int head_dim, int block_size, int group, hipStream_t stream)
 {
-    const CascadeKernel k = kv_type == KT_BF16   ? pick_shape<KT_BF16>(head_dim, block_size, group)
-                            : kv_type == KT_E4M3 ? pick_shape<KT_E4M3>(head_dim, block_size, group)
-                                                 : nullptr;
+    const CascadeKernel k = pick(kv_type, head_dim, block_size, group, p.partials_bf16 != 0);
     if (!k)
         return hipErrorInvalidValue;
     // item workgroups, those for the contract check (about 1k elements

@@ -34,7 +34,7 @@ namespace {
 // - 1: per tile the Q^T operand, accumulators, running max and lane-partial
 // sum, the causal bound and the output row; and the three steps both kernels
 // apply to them (start a segment, attend a staged tile, write the result).
-template <int KT, int D, int BS, int NT>
+template <int KT, int D, int BS, int NT, bool AB>
 struct MultiCols {
     using Geo = MfmaGeo<KT, D, BS>;
     static constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
@@ -105,7 +105,7 @@ struct MultiCols {
                                    pack_bf16x2(acc[nt][d][2] * inv, acc[nt][d][3] * inv));
             } else {
                 const int64_t pi = (int64_t)slot * RPS + col0 + 16 * nt + c16;
-                store_partial<ND>(a.ws_acc, pi, g4, acc[nt], a.v_scale, a.flags & kPartialsBf16);
+                store_partial<ND, AB>(a.ws_acc, pi, g4, acc[nt], a.v_scale);
                 if (g4 == 0)
                     *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m[nt], lt);
             }
@@ -195,8 +195,8 @@ struct MultiCols {
     }
 };
 
-// One wavefront per chunk, all NT column tiles.
-template <int KT, int D, int BS, int NT>
+// One wavefront per chunk, all NT column tiles.  AB: bf16 partial accumulators.
+template <int KT, int D, int BS, int NT, bool AB>
 __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
 {
     using Geo = MfmaGeo<KT, D, BS>;
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
 
     const MfmaLoader<Geo> loader(a, lane);
     using Tile = MfmaTile<Geo>;
-    MultiCols<KT, D, BS, NT> cols(0, lane);
+    MultiCols<KT, D, BS, NT, AB> cols(0, lane);
 
     // Walk the chunk tile by tile with one register tile in flight: tile k is
     // staged into LDS, then the loads of tile k+1 are issued into the same
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
 // and is never staged.
 constexpr int kCoopWaves = 2;
 
-template <int KT, int D, int BS, int NTW, int DEPTH>
+template <int KT, int D, int BS, int NTW, int DEPTH, bool AB>
 __global__ __launch_bounds__(64 * kCoopWaves) void decode_mfma_multi_coop_kernel(DecodeArgs a)
 {
     using Geo = MfmaGeo<KT, D, BS>;
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(64 * kCoopWaves) void decode_mfma_multi_coop_kernel
         }
     };
 
-    MultiCols<KT, D, BS, NTW> cols(16 * NTW * wave, lane);
+    MultiCols<KT, D, BS, NTW, AB> cols(16 * NTW * wave, lane);
 
     // Both wavefronts walk the same cursors, so every branch below and the
     // barrier are uniform over the workgroup.
@@ -427,33 +427,35 @@ constexpr int coop_depth4()
 // Threads of a chunk's workgroup for nt column tiles.
 int threads_for(int nt) { return nt >= 2 ? 64 * kCoopWaves : 64; }
 
-template <int KT, int D, int BS>
+template <int KT, int D, int BS, bool AB>
 DecodeKernel pick_nt(int nt)
 {
     switch (nt) {
-    case 1: return decode_mfma_multi_kernel<KT, D, BS, 1>;
-    case 2: return decode_mfma_multi_coop_kernel<KT, D, BS, 1, 3>;
-    case 4: return decode_mfma_multi_coop_kernel<KT, D, BS, 2, coop_depth4<KT, BS>()>;
+    case 1: return decode_mfma_multi_kernel<KT, D, BS, 1, AB>;
+    case 2: return decode_mfma_multi_coop_kernel<KT, D, BS, 1, 3, AB>;
+    case 4: return decode_mfma_multi_coop_kernel<KT, D, BS, 2, coop_depth4<KT, BS>(), AB>;
     default: return nullptr;
     }
 }
 
-template <int KT>
+template <int KT, bool AB>
 DecodeKernel pick_shape(int d, int bs, int nt)
 {
-    if (d == 64 && bs == 16) return pick_nt<KT, 64, 16>(nt);
-    if (d == 64 && bs == 32) return pick_nt<KT, 64, 32>(nt);
-    if (d == 128 && bs == 16) return pick_nt<KT, 128, 16>(nt);
-    if (d == 128 && bs == 32) return pick_nt<KT, 128, 32>(nt);
+    if (d == 64 && bs == 16) return pick_nt<KT, 64, 16, AB>(nt);
+    if (d == 64 && bs == 32) return pick_nt<KT, 64, 32, AB>(nt);
+    if (d == 128 && bs == 16) return pick_nt<KT, 128, 16, AB>(nt);
+    if (d == 128 && bs == 32) return pick_nt<KT, 128, 32, AB>(nt);
     return nullptr;
 }
 
-DecodeKernel pick(int kv_type, int d, int bs, int nt)
+DecodeKernel pick(int kv_type, int d, int bs, int nt, bool acc_bf16)
 {
     if (kv_type == KT_BF16)
-        return pick_shape<KT_BF16>(d, bs, nt);
+        return acc_bf16 ? pick_shape<KT_BF16, true>(d, bs, nt)
+                        : pick_shape<KT_BF16, false>(d, bs, nt);
     if (kv_type == KT_E4M3)
-        return pick_shape<KT_E4M3>(d, bs, nt);
+        return acc_bf16 ? pick_shape<KT_E4M3, true>(d, bs, nt)
+                        : pick_shape<KT_E4M3, false>(d, bs, nt);
     return nullptr;
 }
 
@@ -462,7 +464,8 @@ DecodeKernel pick(int kv_type, int d, int bs, int nt)
 hipError_t launch_decode_mfma_multi(const DecodeArgs &a, int kv_type, int head_dim,
                                     int block_size, int col_tiles, hipStream_t stream)
 {
-    const DecodeKernel k = pick(kv_type, head_dim, block_size, col_tiles);
+    const DecodeKernel k =
+        pick(kv_type, head_dim, block_size, col_tiles, (a.flags & kPartialsBf16) != 0);
     if (!k)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(k, dim3(a.num_waves), dim3(threads_for(col_tiles)), 0, stream, a);
@@ -470,9 +473,9 @@ hipError_t launch_decode_mfma_multi(const DecodeArgs &a, int kv_type, int head_d
 }
 
 hipError_t decode_mfma_multi_occupancy(int kv_type, int head_dim, int block_size, int col_tiles,
-                                       int *waves_per_cu)
+                                       bool acc_bf16, int *waves_per_cu)
 {
-    const DecodeKernel k = pick(kv_type, head_dim, block_size, col_tiles);
+    const DecodeKernel k = pick(kv_type, head_dim, block_size, col_tiles, acc_bf16);
     if (!k)
         return hipErrorInvalidValue;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(

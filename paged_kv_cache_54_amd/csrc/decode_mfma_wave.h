@@ -50,7 +50,8 @@ struct TableView {
     int stride, len_offset;
 };
 
-template <int KT, int D, int BS, int G>
+// AB: partial accumulators stored as bf16 (else f32).
+template <int KT, int D, int BS, int G, bool AB>
 __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView v, int w,
                                                  uint8_t *const kt, uint8_t *const vt)
 {
@@ -118,7 +119,7 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
                                pack_bf16x2(acc[d][2] * inv, acc[d][3] * inv));
         } else {
             const int64_t pi = (int64_t)slot * G + c16;
-            store_partial<ND>(a.ws_acc, pi, g4, acc, a.v_scale, a.flags & kPartialsBf16);
+            store_partial<ND, AB>(a.ws_acc, pi, g4, acc, a.v_scale);
             if (g4 == 0)
                 *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m, lt);
         }

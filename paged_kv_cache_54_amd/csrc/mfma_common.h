@@ -54,27 +54,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 // Store one column's unnormalised partial accumulator row `row` of a
 // workspace whose rows are D = 16 * ND values: lane group g4 holds dims
 // 16 * d + 4 * g4 .. + 3 of the MFMA output in acc[d].  Each value is
-// multiplied by `scale`, then stored as f32 (16-byte stores) or, with bf16,
-// rounded to nearest even bf16.
-template <int ND>
+// multiplied by `scale` in place (the caller's accumulators are dead after
+// the store; scaling in place needs no extra registers), then stored as f32
+// (16-byte stores) or, with BF16, rounded to nearest even bf16.  The storage
+// type is a template parameter of the kernels: a run-time choice between the
+// two stores cost registers (the two-wavefront verify kernel fell to one
+// wavefront per SIMD).
+template <int ND, bool BF16>
 __device__ __forceinline__ void store_partial(void *ws_acc, int64_t row, int g4,
-                                              const f32x4 (&acc)[ND], float scale, bool bf16)
+                                              f32x4 (&acc)[ND], float scale)
 {
     constexpr int D = 16 * ND;
-    if (bf16) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+        acc[d] *= scale;
+    if constexpr (BF16) {
         uint16_t *o = static_cast<uint16_t *>(ws_acc) + row * D + 4 * g4;
 #pragma unroll
         for (int d = 0; d < ND; ++d)
             *reinterpret_cast<uint2 *>(o + 16 * d) =
-                make_uint2(pack_bf16x2(acc[d][0] * scale, acc[d][1] * scale),
-                           pack_bf16x2(acc[d][2] * scale, acc[d][3] * scale));
+                make_uint2(pack_bf16x2(acc[d][0], acc[d][1]), pack_bf16x2(acc[d][2], acc[d][3]));
     } else {
         float *o = static_cast<float *>(ws_acc) + row * D + 4 * g4;
 #pragma unroll
         for (int d = 0; d < ND; ++d)
-            *reinterpret_cast<float4 *>(o + 16 * d) =
-                make_float4(acc[d][0] * scale, acc[d][1] * scale, acc[d][2] * scale,
-                            acc[d][3] * scale);
+            *reinterpret_cast<f32x4 *>(o + 16 * d) = acc[d];
     }
 }
 

@@ -129,9 +129,9 @@ int resident_waves_per_cu(const DecodePlan &p, int *waves, bool cascade = false)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return PA_ERR_HIP;
-    const long long key = ((((((((long long)dev * 4 + p.variant) * 4 + p.q_type) * 4 + p.kv_type) *
-                             256 + p.D) * 64 + p.bs) * 32 + p.G) * 8 + p.col_tiles) * 2 +
-                         cascade;
+    const long long key = (((((((((long long)dev * 4 + p.variant) * 4 + p.q_type) * 4 + p.kv_type) *
+                              256 + p.D) * 64 + p.bs) * 32 + p.G) * 8 + p.col_tiles) * 2 +
+                          cascade) * 2 + p.acc_bf16;
     std::lock_guard<std::mutex> lock(mu);
     for (auto &kv : cache)
         if (kv.first == key) {
@@ -140,11 +140,12 @@ int resident_waves_per_cu(const DecodePlan &p, int *waves, bool cascade = false)
         }
     int n = 0;
     hipError_t e =
-        cascade    ? cascade_suffix_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G, &n)
+        cascade    ? cascade_suffix_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G,
+                                            p.acc_bf16, &n)
         : p.QM > 0 ? decode_mfma_multi_occupancy(p.kv_type, (int)p.D, (int)p.bs,
-                                               (int)p.col_tiles, &n)
+                                               (int)p.col_tiles, p.acc_bf16, &n)
         : p.variant == PA_VARIANT_MFMA
-            ? decode_mfma_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G, &n)
+            ? decode_mfma_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G, p.acc_bf16, &n)
             : decode_valu_occupancy(p.q_type, p.kv_type, (int)p.D, (int)p.bs, (int)p.G, &n);
     if (e != hipSuccess || n <= 0)
         return PA_ERR_HIP;

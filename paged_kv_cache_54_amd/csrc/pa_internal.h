@@ -168,14 +168,14 @@ bool mfma_supported(int q_type, int kv_type, int head_dim, int block_size, int g
 hipError_t launch_decode_mfma_multi(const DecodeArgs &a, int kv_type, int head_dim,
                                     int block_size, int col_tiles, hipStream_t stream);
 hipError_t decode_mfma_multi_occupancy(int kv_type, int head_dim, int block_size, int col_tiles,
-                                       int *waves_per_cu);
+                                       bool acc_bf16, int *waves_per_cu);
 
-// Wavefronts (one-wavefront workgroups) of the matching decode kernel that one
-// compute unit holds at once.
+// Wavefronts of the matching decode kernel that one compute unit holds at
+// once (acc_bf16: the instance storing bf16 partial accumulators).
 hipError_t decode_valu_occupancy(int q_type, int kv_type, int head_dim, int block_size, int group,
                                  int *waves_per_cu);
 hipError_t decode_mfma_occupancy(int kv_type, int head_dim, int block_size, int group,
-                                 int *waves_per_cu);
+                                 bool acc_bf16, int *waves_per_cu);
 
 // Log-sum-exp merge of the chunk partials of every segment that more than
 // one chunk touched; zero rows for empty sequences.  Grid (S * H), or
@@ -194,7 +194,7 @@ int cascade_prefix_rows();
 // Suffix-pass wavefronts per compute unit of the cascade kernel: those of the
 // workgroups a compute unit holds at once beside one prefix workgroup.
 hipError_t cascade_suffix_occupancy(int kv_type, int head_dim, int block_size, int group,
-                                    int *waves_per_cu);
+                                    bool acc_bf16, int *waves_per_cu);
 hipError_t launch_cascade_merge(const CascadeMergeArgs &a, int out_type, int head_dim,
                                 hipStream_t stream);
 
