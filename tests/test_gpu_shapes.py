@@ -137,7 +137,7 @@ def test_small_batch_launches_one_wavefront_per_unit(variant):
     units = b.num_seqs * b.num_kv_heads * b.block_tables.shape[1]
     G = b.num_heads // b.num_kv_heads
     slots = units + b.num_seqs * b.num_kv_heads
-    acc = 4 if b.q_dtype == "f32" else 2          # partials in the output type
+    acc = 4                                        # fp32 partial accumulators
     want = acc * slots * G * b.head_dim + 8 * slots * G + 8 * b.num_seqs * b.num_kv_heads
     assert pa.decode_workspace_size(b.q, kc, b.block_tables, variant=variant) == want
     print("CASE small batch", variant, flush=True)
