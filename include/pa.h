@@ -58,6 +58,9 @@ extern "C" {
 
 #define PA_VERSION 2
 
+/* Bytes of the static workspace of pa_decode_noalloc (see there). */
+#define PA_NOALLOC_MAX_WORKSPACE ((size_t)96 << 20)
+
 typedef enum pa_dtype {
     PA_F32 = 0,       /* IEEE binary32 */
     PA_BF16 = 1,      /* bfloat16 */
@@ -75,7 +78,9 @@ typedef enum pa_status {
     PA_ERR_ALIGN = 5,        /* data pointer not 16-byte aligned */
     PA_ERR_UNSUPPORTED = 6,  /* head_dim, block_size, group size or option not supported */
     PA_ERR_WORKSPACE = 7,    /* split-KV workspace missing or too small */
-    PA_ERR_HIP = 8           /* the HIP runtime reported an error */
+    PA_ERR_HIP = 8,          /* the HIP runtime reported an error */
+    PA_ERR_SCRATCH = 9       /* pa_decode_noalloc: the call needs more workspace than the
+                                library's static buffer holds */
 } pa_status;
 
 /* Bits OR-ed into *opts->err_flag by a kernel that met broken device data. */
@@ -199,6 +204,29 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
 int pa_decode_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
                              const pa_tensor *block_tables, const pa_opts *opts,
                              size_t *bytes);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results, but the split-KV
+ * workspace is a fixed device buffer the library owns, so the caller passes
+ * only inputs and outputs and the call allocates nothing.
+ *
+ *   arguments as pa_decode; opts may be NULL; opts->workspace and
+ *   opts->workspace_bytes are ignored.
+ *
+ * The buffer holds PA_NOALLOC_MAX_WORKSPACE bytes (96 MiB) on each device
+ * the library runs on, kept until the process ends.  A call whose
+ * pa_decode_workspace_size exceeds it returns PA_ERR_SCRATCH and queues
+ * nothing.  Every call on one device shares that device's buffer, and it
+ * keeps the last call's contents (nothing in it needs to start at zero):
+ * calls whose kernels may overlap on one device -- queued on different
+ * streams without an order between them -- race and must not be made.
+ */
+int pa_decode_noalloc(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *value_cache,
+                      const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,
+                      pa_tensor *out, const pa_opts *opts, void *hip_stream);
+
 
 /*
  * pa_decode_multi -- paged attention for several new query tokens per

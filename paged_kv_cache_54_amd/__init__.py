@@ -26,7 +26,8 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["kv_append", "decode", "decode_workspace_size", "decode_multi", "decode_cascade",
+__all__ = ["kv_append", "decode", "decode_workspace_size", "decode_noalloc", "decode_multi",
+           "decode_cascade", "NOALLOC_MAX_WORKSPACE",
            "decode_cascade_workspace_size",
            "decode_multi_workspace_size", "zero_blocks", "copy_blocks",
            "region_table", "Regions", "prepare_step", "PaError", "status_string", "version", "library_path",
@@ -40,6 +41,7 @@ _LIB_PATH = os.path.join(_HERE, "libpa.so")
 PA_F32, PA_BF16, PA_FP8_E4M3, PA_I32, PA_I64 = 0, 1, 2, 3, 4
 VARIANT_AUTO, VARIANT_VALU, VARIANT_MFMA = 0, 1, 2
 PARTIALS_F32, PARTIALS_BF16 = 0, 1
+NOALLOC_MAX_WORKSPACE = 96 << 20           # PA_NOALLOC_MAX_WORKSPACE
 DEVERR_BLOCK_ID, DEVERR_SEQ_LEN, DEVERR_SLOT, DEVERR_REGION, DEVERR_QUERY = 0x1, 0x2, 0x4, 0x8, 0x10
 DEVERR_STEP, DEVERR_PREFIX = 0x20, 0x40
 
@@ -117,6 +119,10 @@ def _load():
         lib.pa_decode_multi_workspace_size.argtypes = [P(PaTensor), ctypes.c_int32, P(PaTensor),
                                                        P(PaTensor), P(PaOpts),
                                                        P(ctypes.c_size_t)]
+        lib.pa_decode_noalloc.restype = ctypes.c_int
+        lib.pa_decode_noalloc.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor), P(PaTensor),
+                                          P(PaTensor), ctypes.c_float, P(PaTensor), P(PaOpts),
+                                          ctypes.c_void_p]
         lib.pa_decode_workspace_size.restype = ctypes.c_int
         lib.pa_decode_workspace_size.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor),
                                                  P(PaOpts), P(ctypes.c_size_t)]
@@ -260,6 +266,22 @@ def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, k
     _check("pa_decode", lib.pa_decode(*[ctypes.byref(x) for x in args], float(scale),
                                       ctypes.byref(describe(out)), ctypes.byref(o),
                                       ts.cuda_stream))
+    return out
+
+
+def decode_noalloc(q, key_cache, value_cache, block_tables, seq_lens, scale, out, k_scale=1.0,
+                   v_scale=1.0, partition_tokens=0, variant=VARIANT_AUTO, err_flag=None,
+                   stream=None, bf16_partials=False):
+    """pa_decode_noalloc: pa_decode with the library's static device
+    workspace (NOALLOC_MAX_WORKSPACE bytes per device, shared by every call
+    on that device: calls that may overlap on one device race).  ``out``
+    [S, H, D] is required; nothing is allocated, here or in the library."""
+    lib = _load()
+    o = _opts(k_scale, v_scale, partition_tokens, variant, None, err_flag, None, bf16_partials)
+    args = [describe(x) for x in (q, key_cache, value_cache, block_tables, seq_lens)]
+    _check("pa_decode_noalloc",
+           lib.pa_decode_noalloc(*[ctypes.byref(x) for x in args], float(scale),
+                                 ctypes.byref(describe(out)), ctypes.byref(o), _stream(stream)))
     return out
 
 

@@ -18,7 +18,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.cpp", "kv_append.hip", "decode_valu.hip", "decode_mfma.hip",
-           "decode_mfma_multi.hip", "merge.hip", "blocks.hip", "step_prep.hip", "cascade.hip"]
+           "decode_mfma_multi.hip", "merge.hip", "blocks.hip", "step_prep.hip", "cascade.hip",
+           "static_scratch.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC,

@@ -343,11 +343,12 @@ int block_op(const int32_t *ids, int64_t n, const void *const *src_bases,
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-// pa_decode (qsl == NULL, qm == 0) and pa_decode_multi.
+// pa_decode (qsl == NULL, qm == 0), pa_decode_multi, and pa_decode_noalloc
+// (use_static: the workspace is the library's static device buffer).
 int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_tensor *key_cache,
                const pa_tensor *value_cache, const pa_tensor *block_tables,
                const pa_tensor *seq_lens, float scale, pa_tensor *out, const pa_opts *opts,
-               void *hip_stream)
+               void *hip_stream, bool use_static = false)
 {
     int rc;
     if ((rc = check_tensor(q, 3, 16)) || (rc = check_tensor(key_cache, 4, 16)) ||
@@ -382,9 +383,20 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
         return rc;
     if (p.S == 0 || p.T == 0)
         return PA_OK;
-    if (!opts || !opts->workspace || opts->workspace_bytes < p.ws_bytes)
+    pa_opts o;
+    pa_opts_init(&o);
+    if (opts)
+        o = *opts;
+    if (use_static) {
+        if (p.ws_bytes > kStaticScratchBytes)
+            return PA_ERR_SCRATCH;
+        if ((rc = static_scratch(&o.workspace)))
+            return rc;
+        o.workspace_bytes = kStaticScratchBytes;
+    }
+    if (!o.workspace || o.workspace_bytes < p.ws_bytes)
         return PA_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(opts->workspace) % 16)
+    if (reinterpret_cast<uintptr_t>(o.workspace) % 16)
         return PA_ERR_ALIGN;
 
     DecodeArgs a;
@@ -394,10 +406,10 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     a.block_tables = static_cast<const int32_t *>(block_tables->data);
     a.seq_lens = static_cast<const int32_t *>(seq_lens->data);
     a.out = out->data;
-    a.ws_acc = opts->workspace;
-    a.ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(opts->workspace) + acc_bytes(p));
+    a.ws_acc = o.workspace;
+    a.ws_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(o.workspace) + acc_bytes(p));
     a.ws_seg = reinterpret_cast<int32_t *>(a.ws_ml + p.slots * p.rows * 2);
-    a.err_flag = opts->err_flag;
+    a.err_flag = o.err_flag;
     a.num_seqs = (int32_t)p.S;
     a.num_heads = (int32_t)p.H;
     a.num_kv_heads = (int32_t)p.Hkv;
@@ -415,8 +427,8 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     a.flags = p.acc_bf16 ? kPartialsBf16 : 0;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-    hipEvent_t ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);
-    hipEvent_t ev1 = static_cast<hipEvent_t>(opts->kernel_events[1]);
+    hipEvent_t ev0 = static_cast<hipEvent_t>(o.kernel_events[0]);
+    hipEvent_t ev1 = static_cast<hipEvent_t>(o.kernel_events[1]);
     if (ev0 && hipEventRecord(ev0, stream) != hipSuccess)
         return PA_ERR_HIP;
     hipError_t e;
@@ -563,6 +575,8 @@ const char *pa_status_string(int status)
     case PA_ERR_UNSUPPORTED: return "head_dim, block_size, group size or option not supported";
     case PA_ERR_WORKSPACE: return "split-KV workspace missing or too small";
     case PA_ERR_HIP: return "the HIP runtime reported an error";
+    case PA_ERR_SCRATCH:
+        return "the call needs more workspace than the static buffer of pa_decode_noalloc holds";
     default: return "unknown status";
     }
 }
@@ -721,6 +735,14 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
 {
     return run_decode(q, nullptr, 0, key_cache, value_cache, block_tables, seq_lens, scale, out,
                       opts, hip_stream);
+}
+
+int pa_decode_noalloc(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *value_cache,
+                      const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,
+                      pa_tensor *out, const pa_opts *opts, void *hip_stream)
+{
+    return run_decode(q, nullptr, 0, key_cache, value_cache, block_tables, seq_lens, scale, out,
+                      opts, hip_stream, true);
 }
 
 int pa_decode_cascade_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,

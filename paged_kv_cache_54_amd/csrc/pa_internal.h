@@ -198,6 +198,11 @@ hipError_t cascade_suffix_occupancy(int kv_type, int head_dim, int block_size, i
 hipError_t launch_cascade_merge(const CascadeMergeArgs &a, int out_type, int head_dim,
                                 hipStream_t stream);
 
+// The static device buffer of pa_decode_noalloc: its bytes, and its address
+// on the current device (looked up once per device).
+constexpr size_t kStaticScratchBytes = PA_NOALLOC_MAX_WORKSPACE;
+int static_scratch(void **ptr);
+
 // Step metadata from the state table; num_reqs <= kMaxPrepReqs.
 hipError_t launch_step_prep(const StepPrepArgs &a, hipStream_t stream);
 

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
 
 PA_OK, PA_ERR_NULL, PA_ERR_DTYPE, PA_ERR_SHAPE, PA_ERR_LAYOUT, PA_ERR_ALIGN = 0, 1, 2, 3, 4, 5
-PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = 6, 7, 8
+PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_SCRATCH = 6, 7, 8, 9
 F32, BF16, FP8, I32, I64 = 0, 1, 2, 3, 4
 FAKE = 0x7F0000000000          # a 16-byte-aligned address that is never dereferenced
 
@@ -37,7 +37,7 @@ def test_header_declares_the_expected_entry_points():
         ["pa_kv_append", "pa_decode", "pa_decode_workspace_size", "pa_opts_init",
          "pa_status_string", "pa_version", "pa_zero_blocks", "pa_copy_blocks",
          "pa_decode_multi", "pa_decode_multi_workspace_size", "pa_prepare_step",
-         "pa_decode_cascade", "pa_decode_cascade_workspace_size"])
+         "pa_decode_cascade", "pa_decode_cascade_workspace_size", "pa_decode_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert pa.version() == 2
-    for code in range(9):
+    for code in range(10):
         assert pa.status_string(code) and pa.status_string(code) != "unknown status"
     assert pa.status_string(99) == "unknown status"
 
@@ -331,3 +331,37 @@ def test_decode_cascade_validation_errors():
     wide = (1 << 27) + 8
     c = decode_args(S=4, H=8, Hkv=2, D=128, max_nb=wide, qd=BF16, kd=BF16)
     assert call(c, wide - 4) == PA_ERR_UNSUPPORTED
+
+
+def test_decode_noalloc_validation_errors():
+    """pa_decode_noalloc validates like pa_decode and refuses, before any
+    device query, a call whose workspace would exceed its static buffer."""
+    r = lambda x: None if x is None else ctypes.byref(x)
+
+    def call(a, o=None, scale=0.125):
+        return lib().pa_decode_noalloc(r(a["q"]), r(a["kc"]), r(a["vc"]), r(a["bt"]),
+                                       r(a["lens"]), scale, r(a["out"]), r(o), None)
+    assert call(decode_args(S=0)) == PA_OK                                 # nothing to do
+    a = decode_args()
+    a["q"] = None
+    assert call(a) == PA_ERR_NULL
+    assert call(decode_args(qd=BF16, kd=F32)) == PA_ERR_DTYPE
+    assert call(decode_args(NB=0), opts(partition_tokens=16)) == PA_ERR_SHAPE
+    # the long-context shape cut into one-block chunks: 262,144 chunks of 8
+    # fp32 rows of 128 dims need about 1 GiB, beyond the 96 MiB buffer
+    big = decode_args(S=8, H=64, Hkv=8, D=128, bs=32, NB=32768, max_nb=4096, qd=BF16, kd=FP8)
+    n = ctypes.c_size_t(0)
+    assert lib().pa_decode_workspace_size(r(big["q"]), r(big["kc"]), r(big["bt"]),
+                                          r(opts(partition_tokens=32)), ctypes.byref(n)) == PA_OK
+    assert n.value > pa.NOALLOC_MAX_WORKSPACE
+    assert call(big, opts(partition_tokens=32)) == PA_ERR_SCRATCH
+    # ... while 512-token chunks of the same batch fit
+    assert lib().pa_decode_workspace_size(r(big["q"]), r(big["kc"]), r(big["bt"]),
+                                          r(opts(partition_tokens=512)), ctypes.byref(n)) == PA_OK
+    assert n.value <= pa.NOALLOC_MAX_WORKSPACE
+
+
+def test_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PA_NOALLOC_MAX_WORKSPACE \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.NOALLOC_MAX_WORKSPACE
