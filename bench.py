@@ -7,9 +7,10 @@ resident in HBM before timing starts.  W untimed warm-up steps, then exactly
 K timed steps between device synchronisations.  Before every step a kernel
 reads and writes a 1 GiB scratch buffer, so no cache (the 4 MB L2 of each
 XCD, the 256 MB Infinity Cache) still holds the batch from the step before;
-HIP events bracket each step (the flush is outside them) and the library
-records a second pair around its attention kernel.  ``--warm`` runs the
-steps back to back instead, with no flush.
+HIP events bracket each step (the flush is outside them); on every second
+step the library records a second pair around its attention kernel, and the
+step times come from the other steps, which have no event records inside.
+``--warm`` runs the steps back to back instead, with no flush.
 
 Prints one JSON line.  ``value`` is the step's algorithmic HBM bytes divided
 by the median step time, in GB/s; the roofline fraction comes from the
@@ -493,11 +494,15 @@ def main():
     flush = None if args.warm else torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
     by = ctypes.byref
 
+    # Even timed steps also record the attention kernel's events (the kernel's
+    # median comes from them); odd steps run without those two records inside
+    # the step (the step's median comes from them).
     def step(i=None):
-        if i is None:
+        if i is None or i % 2:
             o.kernel_events[0] = o.kernel_events[1] = None
         else:
             o.kernel_events[0], o.kernel_events[1] = ev.ev[4 * i + 1], ev.ev[4 * i + 2]
+        if i is not None:
             ev.record(4 * i, stream)
         rc = lib.pa_kv_append(by(d_k), by(d_v), by(d_slot), by(d_kc), by(d_vc), by(o), stream)
         if cascade:
@@ -528,8 +533,9 @@ def main():
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_t = [ev.elapsed_ms(4 * i, 4 * i + 3) for i in range(args.steps)]
-    kern_t = [ev.elapsed_ms(4 * i + 1, 4 * i + 2) for i in range(args.steps)]
+    step_t = [ev.elapsed_ms(4 * i, 4 * i + 3) for i in range(1, args.steps, 2)] or \
+        [ev.elapsed_ms(0, 3)]
+    kern_t = [ev.elapsed_ms(4 * i + 1, 4 * i + 2) for i in range(0, args.steps, 2)]
     ev.close()
     step_q, kern_q = quantiles(step_t), quantiles(kern_t)
     kernel_ms = kern_q["median"]
@@ -560,6 +566,8 @@ def main():
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3"}[b.cache_dtype],
         "timing": {"protocol": "back to back, no flush" if args.warm else
                    "1 GiB read+write flush before each step, outside the events",
+                   "step_ms_from": f"median of HIP events around the {len(step_t)} odd-numbered "
+                                   f"timed steps (no event records inside them)",
                    "step_ms": step_q, "kernel_ms": kern_q,
                    "wall_ms_per_step": round(wall / args.steps * 1e3, 5)},
         "data": "synthetic",
@@ -581,8 +589,9 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel_ms": round(kernel_ms, 5),
                      "kernel_ms_from": f"median of HIP events around the attention kernel on "
-                                       f"each of the {args.steps} timed steps"
-                                       + ("" if args.warm else ", caches flushed before each"),
+                                       f"the {len(kern_t)} even-numbered of the {args.steps} timed "
+                                       f"steps" + ("" if args.warm else
+                                                   ", caches flushed before each step"),
                      "algorithmic_bytes_per_launch": nbytes["decode"]},
     }
     if nbytes["logical_decode"] != nbytes["decode"]:

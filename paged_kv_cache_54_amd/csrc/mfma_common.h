@@ -28,14 +28,15 @@ __device__ __forceinline__ bf16x4 as_bf16x4(s16x4 v)
     return __builtin_bit_cast(bf16x4, v);
 }
 
-// Two e4m3 codes (byte pair HI of w) -> two packed bf16.  An e4m3 value has
-// at most 4 significant bits, so its binary32 form ends in 16 zero bits and
-// the upper halves are its exact bf16 encoding.
+// Two e4m3 codes (byte pair HI of w) -> two packed bf16, in one gfx950
+// instruction (v_cvt_scalef32_pk_bf16_fp8; a scale of 1.0 scales by 2^0).
+// Every e4m3 value, subnormals included, has an exact bf16 encoding; over all
+// 65,536 byte pairs this gives the same bits as converting to binary32 and
+// keeping the upper halves (v_cvt_pk_f32_fp8 + v_perm, two instructions).
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w)
 {
-    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-    return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 __device__ __forceinline__ uint4 e4m3x8_to_bf16x8(uint2 v)
