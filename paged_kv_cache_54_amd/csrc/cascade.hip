@@ -440,7 +440,9 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(CascadeMergeArg
     // The length and the suffix's segment record are loaded together, and the
     // prefix parts (which need neither) are folded in first, so their loads
     // overlap those two.  A sequence with no own tokens has no record this
-    // call; its stale one is read and not used.
+    // call; its stale one is read and not used.  A record outside the
+    // workspace's slots (never written so by the suffix pass) is not
+    // followed.
     const int2 rec = *reinterpret_cast<const int2 *>(a.s_seg + 2 * (s * Hkv + kvh));
     const int L = a.seq_lens[s];
     Lse st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
@@ -449,7 +451,8 @@ __global__ __launch_bounds__(kThreads) void cascade_merge_kernel(CascadeMergeArg
         add_parts<D, ACC_BF16>(st, a.p_acc, a.p_ml, 0, a.num_splits - 1, Hkv * R,
                      kvh * R + (int64_t)s * G + h % G, col, sub, PPW);
     }
-    if (min(L, a.capacity) > a.prefix_tokens)    // the sequence's own blocks
+    if (min(L, a.capacity) > a.prefix_tokens && rec.x >= 0 && rec.y >= rec.x &&
+        rec.y < a.num_slots)                     // the sequence's own blocks
         add_parts<D, ACC_BF16>(st, a.s_acc, a.s_ml, rec.x, rec.y, G, h % G, col, sub, PPW);
 #pragma unroll
     for (int off = LPP; off < 64; off <<= 1) {

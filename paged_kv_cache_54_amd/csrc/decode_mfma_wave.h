@@ -50,66 +50,84 @@ struct TableView {
     int stride, len_offset;
 };
 
-// AB: partial accumulators stored as bf16 (else f32).
+// One wavefront's attention state for the G query heads of one KV head over
+// a run of staged tiles: the Q^T operand, the fp32 accumulators, the running
+// softmax base and the lane-partial sum.  begin() starts a segment (a
+// sequence's KV head, or the part of it a chunk holds), attend() takes one
+// tile staged in LDS, finish() writes the segment's output rows or its
+// partial.  AB: partial accumulators stored as bf16 (else f32).
+// Partials of G <= 8 rows written by lane pairs in whole lines.
+constexpr bool kPairedPartials = true;
+
 template <int KT, int D, int BS, int G, bool AB>
-__device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView v, int w,
-                                                 uint8_t *const kt, uint8_t *const vt)
-{
+struct WaveAttn {
     using Geo = MfmaGeo<KT, D, BS>;
-    constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
-    constexpr int HALVES = Geo::HALVES;
-    constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
+    static constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
+    static constexpr int KROWB = Geo::KROWB, VROWB = Geo::VROWB;
     static_assert(G >= 1 && G <= 16 && 16 % G == 0, "group must divide 16");
-    // bf16: two register tiles in flight.  e4m3: two with fixed-size chunks
-    // (short chunks, many rounds of wavefronts: the second tile shortens each
-    // chunk's start), one with balanced chunks (measured faster there).
-    const bool pingpong = KT == KT_BF16 || a.chunk_units > 0;
 
-    const int lane = threadIdx.x & 63;
-    const int g4 = lane >> 4;                  // 16-lane group
-    const int c16 = lane & 15;                 // token row (K operand) / column (output)
-    const int H = a.num_heads, Hkv = a.num_kv_heads;
-    const int cap = a.max_nb * BS;
-
-    const Lens lens{a.seq_lens, v.len_offset};
-    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
-    if (chunk.n == 0)
-        return;
-
-    const MfmaLoader<Geo> loader(a, lane);
-    using Tile = MfmaTile<Geo>;
-    auto load_tile = [&](int id, int kvh, int half, Tile &t) { loader.load(id, kvh, half, t); };
-
-    // per-segment state
+    const int g4, c16;                         // 16-lane group; token row / output column
     bf16x8 qop[NC];
     f32x4 acc[ND];
     float m = -INFINITY, l = 0.f;
     bool seg_starts = false;
 
-    auto begin_segment = [&](const Cursor &c) {
-        // Q^T operand: column c16 is query head kvh*G + c16 % G; 8 dims per lane per MFMA
+    __device__ __forceinline__ explicit WaveAttn(int lane) : g4(lane >> 4), c16(lane & 15) {}
+
+    // Q^T operand of the segment's query rows: column c16 is query head
+    // kvh*G + c16 % G; 8 dims per lane per MFMA.
+    __device__ __forceinline__ void load_q(const DecodeArgs &a, const Cursor &c)
+    {
         const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
-                               ((int64_t)c.s * H + c.kvh * G + (c16 % G)) * D + 8 * g4;
+                               ((int64_t)c.s * a.num_heads + c.kvh * G + (c16 % G)) * D + 8 * g4;
 #pragma unroll
         for (int k = 0; k < NC; ++k)
             qop[k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * k));
+    }
+
+    // Empty accumulators and softmax state for a run of tiles starting at c.
+    __device__ __forceinline__ void reset(const Cursor &c)
+    {
 #pragma unroll
         for (int d = 0; d < ND; ++d)
             acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
         m = -INFINITY;
         l = 0.f;
         seg_starts = c.j == 0;
-    };
+    }
 
-    auto finish_segment = [&](const Cursor &c, bool ends) {
+    __device__ __forceinline__ void begin(const DecodeArgs &a, const Cursor &c)
+    {
+        load_q(a, c);
+        reset(c);
+    }
+
+    // The segment's result in partial slot `slot` (segment record too): the
+    // output rows when this run of tiles covered the whole segment, else the
+    // partial (m, l, acc).  ST: partial accumulators written with
+    // nontemporal stores (G <= 8).
+    template <bool ST = false>
+    __device__ __forceinline__ void finish(const DecodeArgs &a, const Cursor &c, int slot,
+                                           bool ends)
+    {
         const float lt = rows_sum(l);          // sum the four 16-lane groups
-        const int g = c.s * Hkv + c.kvh;
-        const int slot = w + g;
+        const int g = c.s * a.num_kv_heads + c.kvh;
         record_segment(a, g, slot, seg_starts, ends);
+        const bool whole = seg_starts && ends && !(a.flags & kPartialOnly);
+        if constexpr (kPairedPartials && G <= 8) {
+            if (!whole) {
+                store_partial_pairs<ND, AB, G, ST>(a.ws_acc, (int64_t)slot * G, g4, c16, acc,
+                                                   a.v_scale);
+                if (g4 == 0 && c16 < G)
+                    *reinterpret_cast<float2 *>(a.ws_ml + ((int64_t)slot * G + c16) * 2) =
+                        make_float2(m, lt);
+                return;
+            }
+        }
         if (c16 >= G)
             return;                            // replicated columns
-        const int64_t row = (int64_t)c.s * H + c.kvh * G + c16;
-        if (seg_starts && ends && !(a.flags & kPartialOnly)) {
+        const int64_t row = (int64_t)c.s * a.num_heads + c.kvh * G + c16;
+        if (whole) {
             const float inv = lt > 0.f ? a.v_scale / lt : 0.f;
             uint16_t *o = static_cast<uint16_t *>(a.out) + row * D + 4 * g4;
 #pragma unroll
@@ -123,19 +141,14 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
             if (g4 == 0)
                 *reinterpret_cast<float2 *>(a.ws_ml + pi * 2) = make_float2(m, lt);
         }
-    };
+    }
 
-    // Stage a tile of the current segment into LDS as bf16 (V rows past the
-    // sequence end as zeros).
-    auto stage = [&](const Cursor &c, int half, const Tile &t) {
-        stage_tile<Geo>(loader, kt, vt, t, c.j * BS + half * TILE, c.L);
-    };
-
-    // QK^T, online softmax and PV of the staged tile.
-    auto process = [&](const Cursor &c, int half) {
-        const int tok_base = c.j * BS + half * TILE;
-        const int t1 = c.L;
-
+    // QK^T, online softmax and PV of the tile staged in kt / vt, whose first
+    // token is tok_base; tokens at or beyond t1 (the sequence's length) are
+    // masked by selection.
+    __device__ __forceinline__ void attend(const DecodeArgs &a, const uint8_t *kt,
+                                           const uint8_t *vt, int tok_base, int t1)
+    {
         // S = K Q^T per 16-token sub-tile; K operand: token c16, dims 32k + 8*g4
         f32x4 sc[MT];
 #pragma unroll
@@ -226,7 +239,37 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
                 }
             }
         }
-    };
+    }
+};
+
+// A wavefront's whole share of single-query decode: its chunk of the work list
+// (balanced or fixed), walked tile by tile through its own LDS tiles kt and vt
+// (TILE * KROWB and TILE * VROWB bytes).  AB as WaveAttn.
+template <int KT, int D, int BS, int G, bool AB>
+__device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView v, int w,
+                                                 uint8_t *const kt, uint8_t *const vt)
+{
+    using Geo = MfmaGeo<KT, D, BS>;
+    constexpr int TILE = Geo::TILE, HALVES = Geo::HALVES;
+    // bf16: two register tiles in flight.  e4m3: two with fixed-size chunks
+    // (short chunks, many rounds of wavefronts: the second tile shortens each
+    // chunk's start), one with balanced chunks (measured faster there).
+    const bool pingpong = KT == KT_BF16 || a.chunk_units > 0;
+
+    const int lane = threadIdx.x & 63;
+    const int Hkv = a.num_kv_heads;
+    const int cap = a.max_nb * BS;
+
+    const Lens lens{a.seq_lens, v.len_offset};
+    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
+    if (chunk.n == 0)
+        return;
+
+    const MfmaLoader<Geo> loader(a, lane);
+    using Tile = MfmaTile<Geo>;
+    auto load_tile = [&](int id, int kvh, int half, Tile &t) { loader.load(id, kvh, half, t); };
+
+    WaveAttn<KT, D, BS, G, AB> att(lane);
 
     // Walk the chunk tile by tile: the load cursor runs one tile ahead of the
     // compute cursor, across block and segment boundaries.
@@ -258,19 +301,20 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
     auto pre_step = [&](int k, int half) {
         const int unit = k / HALVES;
         if (half == 0 && (unit == 0 || cc.j == 0))
-            begin_segment(cc);
+            att.begin(a, cc);
     };
     auto step = [&](int k, int id, int half, const Tile &t, auto issue_next) {
         const int unit = k / HALVES;
-        if (id >= 0)
-            stage(cc, half, t);
+        const int tok_base = cc.j * BS + half * TILE;
+        if (id >= 0)           // stage as bf16, V rows past the sequence end as zeros
+            stage_tile<Geo>(loader, kt, vt, t, tok_base, cc.L);
         issue_next();
         if (id >= 0)
-            process(cc, half);
+            att.attend(a, kt, vt, tok_base, cc.L);
         if (half == HALVES - 1) {
             const bool ends = cc.j == cc.nb - 1;
             if (ends || unit == n - 1)
-                finish_segment(cc, ends);
+                att.finish(a, cc, w + cc.s * Hkv + cc.kvh, ends);
             if (unit + 1 < n)
                 advance<BS>(cc, lens, Hkv, cap);
         }

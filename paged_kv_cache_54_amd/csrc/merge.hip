@@ -10,8 +10,8 @@
 // taken online (M raised part by part, earlier terms rescaled), so every
 // partial is read once, in one pass.  Partials with no tokens (m_p = -inf)
 // get weight 0 by selection.  The segment record gives the first and last
-// slot of the segment; equal slots mean a single chunk covered the segment and
-// already wrote the output.
+// slot of the segment (its slots step by a.slot_stride); equal slots mean a
+// single chunk covered the segment and already wrote the output.
 //
 // Layout: WPR wavefronts per output row.  A partial row (D floats) is read
 // by D/4 lanes, so a wavefront reads 64/(D/4) partials per pass, four passes
@@ -122,15 +122,21 @@ __global__ __launch_bounds__(64 * NW) void merge_kernel(DecodeArgs a, int block_
         }
     }
     bool zero_row = live && L <= 0;
+    const int ss = a.slot_stride;                // slots of a segment: first, first + ss, ..
     if (live && L > 0) {
+        // The decode pass writes both ends of every segment with tokens.  A
+        // record outside the workspace's slots (a workspace that an
+        // overlapping call overwrote) is not followed: the row becomes zeros.
         first = rec.x;
-        live = first != rec.y;                   // else one chunk wrote the output
-        n = rec.y - first + 1;
+        const bool valid = first >= 0 && rec.y >= first && rec.y < a.num_slots;
+        zero_row = !valid;
+        live = valid && first != rec.y;          // else one chunk wrote the output
+        n = (rec.y - first) / ss + 1;
     }
 
     Lse st{-INFINITY, 0.f, make_float4(0.f, 0.f, 0.f, 0.f)};
     if (live && !zero_row) {
-        // partial p of this row: slot first + p, row prow
+        // partial p of this row: slot first + p * ss, row prow
         const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + (int64_t)first * RPS + prow;
         using AT = typename std::conditional<ACC_BF16, uint16_t, float>::type;
         const AT *acc = static_cast<const AT *>(a.ws_acc) + ((int64_t)first * RPS + prow) * D + col;
@@ -142,11 +148,12 @@ __global__ __launch_bounds__(64 * NW) void merge_kernel(DecodeArgs a, int block_
             for (int u = 0; u < UNROLL; ++u) {
                 const int p = p0 + u * stride;
                 if (p < n) {
-                    mlv[u] = ml[(int64_t)p * RPS];
+                    const int64_t ps = (int64_t)p * ss * RPS;
+                    mlv[u] = ml[ps];
                     if constexpr (!ACC_BF16) {
-                        x[u] = *reinterpret_cast<const float4 *>(acc + (int64_t)p * RPS * D);
+                        x[u] = *reinterpret_cast<const float4 *>(acc + ps * D);
                     } else {
-                        const uint2 v = *reinterpret_cast<const uint2 *>(acc + (int64_t)p * RPS * D);
+                        const uint2 v = *reinterpret_cast<const uint2 *>(acc + ps * D);
                         x[u] = make_float4(__uint_as_float(v.x << 16),
                                            __uint_as_float(v.x & 0xffff0000u),
                                            __uint_as_float(v.y << 16),

@@ -16,6 +16,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v)
@@ -80,6 +81,52 @@ __device__ __forceinline__ void store_partial(void *ws_acc, int64_t row, int g4,
 #pragma unroll
         for (int d = 0; d < ND; ++d)
             *reinterpret_cast<f32x4 *>(o + 16 * d) = acc[d];
+    }
+}
+
+// store_partial for the single-query kernels' output layout with G <= 8
+// query heads per KV head: lanes c16 and c16 + 8 hold the same column
+// (c16 mod G), so the pair writes two consecutive 16-dimension slices of row
+// r = c16 & 7 in one instruction -- lane c16 slice 2p, lane c16 + 8 slice
+// 2p + 1 -- and every store covers whole 128-byte lines of a row (f32)
+// instead of their halves, in half as many instructions.  Rows r >= G store
+// nothing.
+//
+// ST: nontemporal stores, which leave the lines out of L2 (for calls whose
+// partials outgrow the L2s: their dirty lines, written back in among the KV
+// reads, cost more than the bytes).  A template parameter: a run-time choice
+// between two stores of the same value to the same address is merged by the
+// compiler into one cached store.
+template <int ND, bool BF16, int G, bool ST>
+__device__ __forceinline__ void store_partial_pairs(void *ws_acc, int64_t slot_row0, int g4,
+                                                    int c16, f32x4 (&acc)[ND], float scale)
+{
+    static_assert(G <= 8 && ND % 2 == 0, "pairs need replicated columns");
+    constexpr int D = 16 * ND;
+    const int r = c16 & 7, hi = c16 >> 3;
+    if (r >= G)
+        return;
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+        acc[d] *= scale;
+    const int64_t base = (slot_row0 + r) * D + 4 * g4 + 16 * hi;
+#pragma unroll
+    for (int p = 0; p < ND / 2; ++p) {
+        const f32x4 v = hi ? acc[2 * p + 1] : acc[2 * p];
+        if constexpr (BF16) {
+            u32x2 *o = reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(ws_acc) + base + 32 * p);
+            const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            if constexpr (ST)
+                __builtin_nontemporal_store(w, o);
+            else
+                *o = w;
+        } else {
+            f32x4 *o = reinterpret_cast<f32x4 *>(static_cast<float *>(ws_acc) + base + 32 * p);
+            if constexpr (ST)
+                __builtin_nontemporal_store(v, o);
+            else
+                *o = v;
+        }
     }
 }
 

@@ -99,11 +99,25 @@ struct DecodePlan {
     int q_type, kv_type;
     int variant;             // PA_VARIANT_VALU or PA_VARIANT_MFMA
     int64_t chunk_units;     // units per chunk, 0 = balanced over the waves
-    int64_t waves;           // grid size
+    int64_t heads;           // > 0: the e4m3 kernel whose workgroups hold one wavefront
+                             // per KV head (heads = Hkv) and walk (sequence, block) units
+    int64_t waves;           // grid size in wavefronts; with heads > 0, partitions * heads
+    int64_t groups;          // heads > 0: workgroups to launch (fixed partitions: at most
+                             // the partition count, capped at launch by the resident ones)
     int64_t slots;           // partial slots = waves + segments
     bool acc_bf16;           // partial accumulators stored as bf16
     size_t ws_bytes;
 };
+
+// Partial accumulator bytes above which the per-block e4m3 kernel writes
+// them with nontemporal stores: the combined L2 of the device (8 x 4 MB).
+// Above it dirty partial lines written back in among the KV reads cost more
+// than their bytes (131072-token e4m3 batch in 512-token partitions, 64 MB:
+// 423 us cached, 374 us streamed, 350 us with no accumulator stores at all);
+// below it the merge rereads them from L2 (Llama-shaped bf16 batch, 3 MB of
+// partials: 104.9 us kernel / 112.2 us step cached, 105.7 / 114.6 streamed).
+// The bf16 kernels keep cached stores (their workloads' partials are small).
+constexpr size_t kStreamPartialBytes = size_t(32) << 20;
 
 // Workspace layout: acc [slots, rows, D] | ml [slots, rows, 2] f32 | seg [S*Hkv, 2] i32
 // Partial accumulators are f32; PA_PARTIALS_BF16 stores them as bf16 for a
@@ -129,9 +143,9 @@ int resident_waves_per_cu(const DecodePlan &p, int *waves, bool cascade = false)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return PA_ERR_HIP;
-    const long long key = (((((((((long long)dev * 4 + p.variant) * 4 + p.q_type) * 4 + p.kv_type) *
+    const long long key = ((((((((((long long)dev * 4 + p.variant) * 4 + p.q_type) * 4 + p.kv_type) *
                               256 + p.D) * 64 + p.bs) * 32 + p.G) * 8 + p.col_tiles) * 2 +
-                          cascade) * 2 + p.acc_bf16;
+                          cascade) * 2 + p.acc_bf16) * 16 + p.heads;
     std::lock_guard<std::mutex> lock(mu);
     for (auto &kv : cache)
         if (kv.first == key) {
@@ -144,11 +158,15 @@ int resident_waves_per_cu(const DecodePlan &p, int *waves, bool cascade = false)
                                             p.acc_bf16, &n)
         : p.QM > 0 ? decode_mfma_multi_occupancy(p.kv_type, (int)p.D, (int)p.bs,
                                                (int)p.col_tiles, p.acc_bf16, &n)
+        : p.heads > 0 ? decode_mfma_heads_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G,
+                                                  (int)p.heads, p.acc_bf16, &n)
         : p.variant == PA_VARIANT_MFMA
             ? decode_mfma_occupancy(p.kv_type, (int)p.D, (int)p.bs, (int)p.G, p.acc_bf16, &n)
             : decode_valu_occupancy(p.q_type, p.kv_type, (int)p.D, (int)p.bs, (int)p.G, &n);
     if (e != hipSuccess || n <= 0)
         return PA_ERR_HIP;
+    if (p.heads > 0 && !cascade)
+        n *= (int)p.heads;                   // workgroups -> wavefronts
     cache.emplace_back(key, n);
     *waves = n;
     return PA_OK;
@@ -157,8 +175,10 @@ int resident_waves_per_cu(const DecodePlan &p, int *waves, bool cascade = false)
 // Shapes, dtypes and options common to the decode entry points and their
 // workspace queries.  qm = 0: one query token per sequence (q [S, H, D]);
 // qm > 0: several per sequence, at most qm (q [T, H, D], S from the tables).
+// allow_heads: single-query e4m3 decode may use the per-block kernel (not for
+// the cascade's suffix pass, which runs the per-wavefront body).
 int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
-                const pa_opts *opts, int64_t qm, DecodePlan *p)
+                const pa_opts *opts, int64_t qm, DecodePlan *p, bool allow_heads = true)
 {
     if (!q || !kc || !bt)
         return PA_ERR_NULL;
@@ -218,13 +238,46 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
         p->variant = PA_VARIANT_MFMA;
     else
         return PA_ERR_UNSUPPORTED;
+    // e4m3 cache, one query token: workgroups of one wavefront per KV head
+    // that read each block's K and V whole (every head of a token slot
+    // together) where that kernel has an instance.
+    p->heads = allow_heads && p->variant == PA_VARIANT_MFMA && qm == 0 &&
+                       decode_mfma_heads_supported(kvt, (int)p->D, (int)p->bs, (int)p->G,
+                                                   (int)p->Hkv)
+                   ? p->Hkv
+                   : 0;
 
-    // Chunking of the (sequence, KV head, block) work list.
+    // Chunking of the (sequence, KV head, block) work list, or of the
+    // (sequence, block) list with heads > 0.
     const int64_t P = opts ? opts->partition_tokens : 0;
     if (P < 0 || P % p->bs)
         return PA_ERR_UNSUPPORTED;
     const int64_t max_units = p->S * p->Hkv * p->max_nb;
-    if (P > 0) {
+    p->groups = 0;
+    if (p->heads > 0) {
+        // partitions of the (sequence, block) list; each workgroup walks a run
+        const int64_t max_blocks = p->S * p->max_nb;
+        int64_t groups = 1;
+        if (P > 0) {
+            p->chunk_units = P / p->bs;
+            groups = max_blocks > 0 ? (max_blocks + p->chunk_units - 1) / p->chunk_units : 1;
+        } else {
+            // balanced: one chunk per workgroup the device holds at once
+            p->chunk_units = 0;
+            if (p->S > 0) {
+                int cus = 0, per_cu = 0, rc;
+                if ((rc = device_cu_count(&cus)) || (rc = resident_waves_per_cu(*p, &per_cu)))
+                    return rc;
+                groups = (int64_t)cus * (per_cu / p->heads);
+                if (max_blocks > 0 && max_blocks < groups)
+                    groups = max_blocks;
+            }
+        }
+        if (groups > INT32_MAX / 16)
+            return PA_ERR_UNSUPPORTED;
+        p->groups = groups;
+        p->waves = groups * p->heads;
+    } else if (P > 0) {
         // fixed chunks: enough wavefronts for the largest possible batch
         p->chunk_units = P / p->bs;
         p->waves = max_units > 0 ? (max_units + p->chunk_units - 1) / p->chunk_units : 1;
@@ -424,7 +477,22 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     a.log2_group = __builtin_ctz((unsigned)p.G);
     a.qk_scale_log2 = scale * kLog2e * ks;
     a.v_scale = vs;
-    a.flags = p.acc_bf16 ? kPartialsBf16 : 0;
+    a.flags = (p.acc_bf16 ? kPartialsBf16 : 0) |
+              (p.heads > 0 && acc_bytes(p) > kStreamPartialBytes ? kStreamPartials : 0);
+    a.slot_stride = p.heads > 0 ? (int32_t)p.heads : 1;
+    a.num_slots = (int32_t)p.slots;
+
+    // Fixed partitions on the per-block e4m3 kernel: no more workgroups than
+    // the device holds at once, each walking an equal run of partitions.
+    int64_t groups = p.groups;
+    if (p.heads > 0 && p.chunk_units > 0) {
+        int cus = 0, per_cu = 0;
+        if ((rc = device_cu_count(&cus)) || (rc = resident_waves_per_cu(p, &per_cu)))
+            return rc;
+        const int64_t resident = (int64_t)cus * (per_cu / p.heads);
+        if (resident > 0 && resident < groups)
+            groups = resident;
+    }
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     hipEvent_t ev0 = static_cast<hipEvent_t>(o.kernel_events[0]);
@@ -434,6 +502,9 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     hipError_t e;
     if (qm > 0)
         e = launch_decode_mfma_multi(a, p.kv_type, (int)p.D, (int)p.bs, (int)p.col_tiles, stream);
+    else if (p.heads > 0)
+        e = launch_decode_mfma_heads(a, p.kv_type, (int)p.D, (int)p.bs, (int)p.G,
+                                     (int)groups, stream);
     else if (p.variant == PA_VARIANT_MFMA)
         e = launch_decode_mfma(a, p.kv_type, (int)p.D, (int)p.bs, (int)p.G, stream);
     else
@@ -499,7 +570,7 @@ int plan_cascade(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt, i
     o.variant = PA_VARIANT_MFMA;
     const pa_tensor bt_suf = reshaped(bt, {S, max_nb - N});
     int rc;
-    if ((rc = plan_decode(q, kc, &bt_suf, &o, 0, &c->suf)))
+    if ((rc = plan_decode(q, kc, &bt_suf, &o, 0, &c->suf, false)))
         return rc;
     if (c->suf.chunk_units == 0 && S > 0) {
         // balanced chunks: the suffix wavefronts the cascade kernel holds
@@ -866,6 +937,8 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     sa.qk_scale_log2 = scale * kLog2e * ks;
     sa.v_scale = vs;
     sa.flags = kPartialOnly | (sp.acc_bf16 ? kPartialsBf16 : 0);
+    sa.slot_stride = 1;
+    sa.num_slots = (int32_t)sp.slots;
 
     CascadeMergeArgs ma;
     ma.out = out->data;
@@ -882,6 +955,7 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     ma.num_kv_heads = (int32_t)sp.Hkv;
     ma.num_splits = (int32_t)c.P;
     ma.partials_bf16 = sp.acc_bf16;
+    ma.num_slots = (int32_t)sp.slots;
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
     hipEvent_t ev0 = static_cast<hipEvent_t>(opts->kernel_events[0]);

@@ -370,6 +370,48 @@ struct BlockIds {
     }
 };
 
+// BlockIds whose following 64 entries of the same table row are read one
+// window ahead, so a walk along a sequence waits for the table only at its
+// first block (and at a jump), not every 64 blocks.
+struct BlockIdsAhead {
+    const int32_t *tables;
+    int stride, max_nb, num_blocks;
+    uint32_t *err;
+    int s = -1, base = 0, ids = 0, next = 0;
+
+    __device__ __forceinline__ BlockIdsAhead(const int32_t *tables_, int stride_, int max_nb_,
+                                             int nblocks, uint32_t *err_)
+        : tables(tables_), stride(stride_), max_nb(max_nb_), num_blocks(nblocks), err(err_)
+    {
+    }
+
+    __device__ __forceinline__ int fetch(int s_, int j) const
+    {
+        const int jj = j + lane_id();
+        return jj < max_nb ? tables[(int64_t)s_ * stride + jj] : 0;
+    }
+
+    __device__ __forceinline__ int get(int s_, int j)
+    {
+        if (s_ != s || j < base || j >= base + 64) {
+            if (s_ == s && j >= base + 64 && j < base + 128) {
+                ids = next;                    // the window read ahead
+                base += 64;
+            } else {
+                s = s_;
+                base = j;
+                ids = fetch(s_, j);
+            }
+            next = fetch(s, base + 64);
+        }
+        const int id = __builtin_amdgcn_readlane(ids, j - base);
+        const bool bad = id < 0 || id >= num_blocks;
+        if (bad)
+            raise_flag(err, PA_DEVERR_BLOCK_ID);
+        return __builtin_amdgcn_readfirstlane(bad ? -1 : id);
+    }
+};
+
 // Chunk [u0, u0 + n) of the work list for wavefront w of W (n = 0: none) and
 // the cursor of its first unit.  Batches of up to 256 sequences read their
 // lengths once, with independent loads, and derive both the total and the
@@ -380,15 +422,28 @@ struct Chunk {
     Cursor start;
 };
 
+// Units per chunk of a work list of U units over W chunks: chunk_units, or
+// (0) ceil(U / W).  runs: chunk_units > 0 names partitions, and each of the W
+// chunks takes an equal run of whole partitions.
+__device__ __forceinline__ int64_t chunk_len(const DecodeArgs &a, int64_t U, int W, bool runs)
+{
+    if (a.chunk_units <= 0)
+        return (U + W - 1) / W;
+    if (!runs)
+        return a.chunk_units;
+    const int64_t parts = (U + a.chunk_units - 1) / a.chunk_units;
+    return a.chunk_units * ((parts + W - 1) / W);
+}
+
 template <int BS>
-__device__ Chunk my_chunk(const DecodeArgs &a, Lens lens, int w, int W)
+__device__ Chunk my_chunk(const DecodeArgs &a, Lens lens, int w, int W, bool runs = false)
 {
     const int S = a.num_seqs, Hkv = a.num_kv_heads;
     const int cap = a.max_nb * BS;
     uint32_t *flag = w == 0 ? a.err_flag : nullptr;
     if (S > 256) {
         const int64_t U = total_units<BS>(lens, S, Hkv, cap, flag);
-        const int64_t cl = a.chunk_units > 0 ? a.chunk_units : (U + W - 1) / W;
+        const int64_t cl = chunk_len(a, U, W, runs);
         const int64_t u0 = (int64_t)w * cl;
         if (u0 >= U)
             return Chunk{0, 0, Cursor{}};
@@ -414,7 +469,7 @@ __device__ Chunk my_chunk(const DecodeArgs &a, Lens lens, int w, int W)
     }
     if (flag && __ballot(over))
         raise_flag(flag, PA_DEVERR_SEQ_LEN);
-    const int64_t cl = a.chunk_units > 0 ? a.chunk_units : (U + W - 1) / W;
+    const int64_t cl = chunk_len(a, U, W, runs);
     const int64_t u0 = (int64_t)w * cl;
     if (u0 >= U)
         return Chunk{0, 0, Cursor{}};

@@ -42,14 +42,19 @@ struct DecodeArgs {
     float qk_scale_log2;         // scale * log2(e) * k_scale (k_scale = 1 unless fp8)
     float v_scale;               // 1 unless fp8
     int32_t flags;               // kPartialOnly | kPartialsBf16
+    int32_t slot_stride;         // slots of one segment's partials step by this (>= 1)
+    int32_t num_slots;           // slots of the workspace
 };
 
 // DecodeArgs.flags.  kPartialOnly (matrix-core kernels): every segment ends
 // as a partial (acc, m, l), also one a single chunk covers, so that a second
 // pass can combine it with another source.  kPartialsBf16: partial
 // accumulators are stored as bf16 (bf16 outputs only); otherwise f32.
+// kStreamPartials (the per-block e4m3 kernel, G <= 8): partial
+// accumulators are written with nontemporal stores.
 constexpr int32_t kPartialOnly = 1;
 constexpr int32_t kPartialsBf16 = 2;
+constexpr int32_t kStreamPartials = 4;
 
 struct AppendArgs {
     const void *k;               // [T, Hkv, D]
@@ -147,6 +152,7 @@ struct CascadeMergeArgs {
     const float *p_ml;
     int32_t num_seqs, num_heads, num_kv_heads, num_splits;
     int32_t partials_bf16;        // both accumulators stored as bf16
+    int32_t num_slots;            // suffix partial slots of the workspace
 };
 
 // Launchers (defined in the .hip translation units).  Each returns a
@@ -162,6 +168,17 @@ hipError_t launch_decode_valu(const DecodeArgs &a, int q_type, int kv_type, int 
 hipError_t launch_decode_mfma(const DecodeArgs &a, int kv_type, int head_dim, int block_size,
                               int group, hipStream_t stream);
 bool mfma_supported(int q_type, int kv_type, int head_dim, int block_size, int group);
+
+// Matrix-core decode of an e4m3 cache with workgroups of one wavefront per KV
+// head (a.num_kv_heads of them) walking (sequence, block) units; partial slots
+// of a segment step by num_kv_heads (a.slot_stride).  Occupancy in workgroups.
+bool decode_mfma_heads_supported(int kv_type, int head_dim, int block_size, int group,
+                                 int num_kv_heads);
+hipError_t launch_decode_mfma_heads(const DecodeArgs &a, int kv_type, int head_dim,
+                                    int block_size, int group, int workgroups,
+                                    hipStream_t stream);
+hipError_t decode_mfma_heads_occupancy(int kv_type, int head_dim, int block_size, int group,
+                                       int num_kv_heads, bool acc_bf16, int *groups_per_cu);
 
 // Matrix-core decode of several query tokens per sequence; col_tiles = 16-column
 // tiles of (query token, head) pairs per KV head, 1, 2 or 4.
