@@ -43,9 +43,11 @@ KERNEL_SOURCES = {
 KERNEL_SOURCES["blocks"] = ["paged_kv_cache_54_amd/csrc/blocks.hip",
                             "paged_kv_cache_54_amd/csrc/pa_device.h"]
 KERNEL_SOURCES["cascade"] = KERNEL_SOURCES["mfma"] + ["paged_kv_cache_54_amd/csrc/cascade.hip"]
+KERNEL_SOURCES["mfma_heads"] = ["paged_kv_cache_54_amd/csrc/decode_mfma_heads.hip"] + \
+    KERNEL_SOURCES["mfma"][1:]
 KERNEL_NAMES = {"valu": "decode_valu_kernel", "mfma": "decode_mfma_kernel",
                 "mfma_multi": "decode_mfma_multi_kernel",
-                "cascade": "cascade_kernel"}
+                "cascade": "cascade_kernel", "mfma_heads": "decode_mfma_heads_kernel"}
 
 
 def parse():
@@ -63,6 +65,9 @@ def parse():
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--warm", action="store_true",
                     help="run the timed steps back to back with no cache flush between them")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="one-query steps: pa_kv_append then pa_decode (two launches) "
+                         "instead of pa_decode_append")
     ap.add_argument("--bf16-partials", action="store_true",
                     help="store split-KV partial accumulators as bf16 instead of fp32")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -476,7 +481,11 @@ def main():
         ws_bytes = pa.decode_workspace_size(b.q, kc, b.block_tables, P, variant, bf16p)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
-    # descriptors built once; each step is two C calls
+    # One-query steps call pa_decode_append: the append is done by the decode
+    # kernel (matrix-core variants) and its bytes are then that kernel's too.
+    fused = not (cascade or multi or args.separate_append)
+
+    # descriptors built once; each step is one or two C calls
     lib = pa._load()
     d_k, d_v, d_slot = describe(b.k_new), describe(b.v_new), describe(b.slot_mapping)
     d_q, d_kc, d_vc = describe(b.q), describe(kc), describe(vc)
@@ -504,6 +513,15 @@ def main():
             o.kernel_events[0], o.kernel_events[1] = ev.ev[4 * i + 1], ev.ev[4 * i + 2]
         if i is not None:
             ev.record(4 * i, stream)
+        if fused:
+            rc = lib.pa_decode_append(by(d_k), by(d_v), by(d_slot), by(d_q), by(d_kc), by(d_vc),
+                                      by(d_bt), by(d_len), ctypes.c_float(b.scale), by(d_out),
+                                      by(o), stream)
+            if rc:
+                raise pa.PaError("step", rc)
+            if i is not None:
+                ev.record(4 * i + 3, stream)
+            return
         rc = lib.pa_kv_append(by(d_k), by(d_v), by(d_slot), by(d_kc), by(d_vc), by(o), stream)
         if cascade:
             rc = rc or lib.pa_decode_cascade(by(d_q), by(d_kc), by(d_vc), by(d_bt), by(d_len),
@@ -547,7 +565,16 @@ def main():
         variant == pa.VARIANT_AUTO and _mfma_ok(pa, b, kc))) else "valu"
     if cascade:
         used = "cascade"
-    achieved = nbytes["decode"] / (kernel_ms * 1e-3) / 1e9
+    if used == "mfma" and not multi and _heads_kernel(b):
+        used = "mfma_heads"
+    # The library fuses the append into the matrix-core one-query kernels
+    # when the batch has no more (sequence, KV head) segments than the kernel
+    # has wavefronts; the wavefronts follow from the workspace size, whose
+    # slots are wavefronts + segments.
+    in_kernel = (fused and used in ("mfma", "mfma_heads") and b.k_new.shape[0] == b.num_seqs
+                 and b.num_seqs * b.num_kv_heads <= _waves(b, ws_bytes, bf16p))
+    kernel_bytes = nbytes["decode"] + (nbytes["append"] if in_kernel else 0)
+    achieved = kernel_bytes / (kernel_ms * 1e-3) / 1e9
     kname = KERNEL_NAMES[used]
     if multi and b.group_size * b.max_query_len > 16:
         kname = "decode_mfma_multi_coop_kernel"     # more than one 16-column tile
@@ -578,6 +605,8 @@ def main():
                    "q_dtype": b.q_dtype, "cache_dtype": b.cache_dtype,
                    "partition_tokens": P or "auto", "variant": used,
                    "partials": "bf16" if bf16p and b.q_dtype == "bf16" else "f32",
+                   "append": "in the decode kernel" if in_kernel else
+                             ("pa_decode_append, own launch" if fused else "pa_kv_append"),
                    **({"shared_prefix_blocks": b.shared_prefix_blocks} if cascade else {}),
                    **({"query_tokens": b.q.shape[0], "max_query_len": b.max_query_len}
                       if multi else {})},
@@ -592,13 +621,31 @@ def main():
                                        f"the {len(kern_t)} even-numbered of the {args.steps} timed "
                                        f"steps" + ("" if args.warm else
                                                    ", caches flushed before each step"),
-                     "algorithmic_bytes_per_launch": nbytes["decode"]},
+                     "algorithmic_bytes_per_launch": kernel_bytes},
     }
     if nbytes["logical_decode"] != nbytes["decode"]:
         res["logical_decode_bytes"] = nbytes["logical_decode"]
         res["effective_logical_gbs"] = round(nbytes["logical_decode"] / (kernel_ms * 1e-3) / 1e9, 2)
     res["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(b, args.cpu_budget_s)
     print(json.dumps(res), flush=True)
+
+
+def _waves(b, ws_bytes, bf16p):
+    """Wavefronts of a one-query decode plan, from its workspace bytes:
+    acc [slots, G, D] (2 or 4 bytes) | ml [slots, G, 2] f32 | seg [S*Hkv, 2] i32,
+    slots = wavefronts + S*Hkv."""
+    G = b.num_heads // b.num_kv_heads
+    segs = b.num_seqs * b.num_kv_heads
+    per_slot = G * b.head_dim * (2 if bf16p and b.q_dtype == "bf16" else 4) + 8 * G
+    return (ws_bytes - 8 * segs) // per_slot - segs
+
+
+def _heads_kernel(b):
+    """Whether the library runs this one-query batch on its per-block e4m3
+    kernel (workgroups of one wavefront per KV head)."""
+    G = b.num_heads // b.num_kv_heads
+    return (b.cache_dtype == "fp8_e4m3" and b.head_dim == 128 and b.block_size in (16, 32)
+            and b.num_kv_heads in (4, 8) and G in (1, 2, 4, 8))
 
 
 def _mfma_ok(pa, b, kc):

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define PA_VERSION 2
+#define PA_VERSION 3
 
 /* Bytes of the static workspace of pa_decode_noalloc (see there). */
 #define PA_NOALLOC_MAX_WORKSPACE ((size_t)96 << 20)
@@ -86,7 +86,9 @@ typedef enum pa_status {
 /* Bits OR-ed into *opts->err_flag by a kernel that met broken device data. */
 #define PA_DEVERR_BLOCK_ID 0x1u  /* block id outside [0, num_blocks): block skipped */
 #define PA_DEVERR_SEQ_LEN 0x2u   /* seq_len > table capacity: clamped */
-#define PA_DEVERR_SLOT 0x4u      /* slot >= num_blocks * block_size: token not written */
+#define PA_DEVERR_SLOT 0x4u      /* slot >= num_blocks * block_size: token not written;
+                                    pa_decode_append also: an appended row whose slot is not
+                                    that of its sequence's last position (see there) */
 #define PA_DEVERR_REGION 0x8u    /* block-op region base NULL or not 16-byte aligned: skipped */
 #define PA_DEVERR_STEP 0x20u     /* pa_prepare_step: bad state row, count or position, or the
                                     step's tokens exceed max_tokens (see there) */
@@ -124,10 +126,14 @@ typedef struct pa_opts {
     /* Work split.  The batch's work is the list of (sequence, KV head,
        logical block) units, sequence-major; it is cut into chunks of
        consecutive units, one per wavefront, and a KV head's sequence split
-       between chunks is finished by a log-sum-exp merge.  0 (default): as many
-       equal chunks as wavefronts the device holds at once, so every compute
-       unit streams the same number of blocks.  Otherwise: chunks of
-       partition_tokens / block_size units (a multiple of block_size). */
+       between chunks is finished by a log-sum-exp merge.  (One-query decode
+       of an e4m3 cache with 4 or 8 KV heads at head_dim 128 cuts the list of
+       (sequence, logical block) units instead, every KV head of a block
+       together, one chunk per workgroup of one wavefront per KV head.)
+       0 (default): as many equal chunks as the device holds at once, so
+       every compute unit streams the same number of blocks.  Otherwise:
+       partitions of partition_tokens / block_size units (a multiple of
+       block_size), each finished as its own partial. */
     int32_t partition_tokens;
     int32_t variant;            /* PA_VARIANT_* */
     void *workspace;            /* device buffer, pa_decode_workspace_size bytes,
@@ -204,6 +210,39 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
 int pa_decode_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
                              const pa_tensor *block_tables, const pa_opts *opts,
                              size_t *bytes);
+
+/*
+ * pa_decode_append -- pa_kv_append(k, v, slot_mapping, caches) followed by
+ * pa_decode(q, caches, ...) on the same stream: one decode step's write of
+ * the new token's K/V rows into their slots and the attention that reads
+ * them (vLLM concept page, "15-minute deep dive": rows are written into
+ * their block slots, and attention then reads the blocks the table names).
+ *
+ *   k, v, slot_mapping   as pa_kv_append
+ *   other arguments      as pa_decode (same workspace size)
+ *
+ * Results, caches and the error word are those of the two calls.  Where the
+ * decode runs on the matrix cores with one new BF16 row per sequence (T = S,
+ * row s belonging to sequence s) and the batch has no more (sequence, KV
+ * head) pairs than the decode kernel has wavefronts, the append is done
+ * inside the decode kernel: the row of sequence s is written to
+ * slot_mapping[s] and taken as the key/value at position seq_lens[s] - 1
+ * without a round trip through the cache -- one launch less.  That form needs slot_mapping[s] to be the
+ * slot of position seq_lens[s] - 1 (or < 0, nothing appended) and
+ * seq_lens[s] >= 1 where a row is appended; a sequence breaking this raises
+ * PA_DEVERR_SLOT: its row is written to slot_mapping[s] when that lies in
+ * the pool (not when its seq_len is 0), and its attention reads position
+ * seq_lens[s] - 1 from the cache as it found it (as does a read of the slot
+ * the row was written to, if any sequence of the call reads it: it may see
+ * the old or the new row).  A sequence whose last block id is out of range
+ * (PA_DEVERR_BLOCK_ID) also raises PA_DEVERR_SLOT; its row is written.  Any
+ * other case (VALU variant, F32, T != S) runs the append as its own launch
+ * first.  A validation error queues nothing.
+ */
+int pa_decode_append(const pa_tensor *k, const pa_tensor *v, const pa_tensor *slot_mapping,
+                     const pa_tensor *q, pa_tensor *key_cache, pa_tensor *value_cache,
+                     const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,
+                     pa_tensor *out, const pa_opts *opts, void *hip_stream);
 
 /*
  * pa_decode_noalloc -- pa_decode for callers that cannot allocate device

@@ -26,7 +26,7 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["kv_append", "decode", "decode_workspace_size", "decode_noalloc", "decode_multi",
+__all__ = ["kv_append", "decode", "decode_append", "decode_workspace_size", "decode_noalloc", "decode_multi",
            "decode_cascade", "NOALLOC_MAX_WORKSPACE",
            "decode_cascade_workspace_size",
            "decode_multi_workspace_size", "zero_blocks", "copy_blocks",
@@ -103,6 +103,9 @@ def _load():
         lib.pa_decode.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor), P(PaTensor),
                                   P(PaTensor), ctypes.c_float, P(PaTensor), P(PaOpts),
                                   ctypes.c_void_p]
+        lib.pa_decode_append.restype = ctypes.c_int
+        lib.pa_decode_append.argtypes = [P(PaTensor)] * 8 + [ctypes.c_float, P(PaTensor),
+                                                             P(PaOpts), ctypes.c_void_p]
         lib.pa_decode_cascade.restype = ctypes.c_int
         lib.pa_decode_cascade.argtypes = [P(PaTensor), P(PaTensor), P(PaTensor), P(PaTensor),
                                           P(PaTensor), ctypes.c_int32, ctypes.c_float,
@@ -266,6 +269,33 @@ def decode(q, key_cache, value_cache, block_tables, seq_lens, scale, out=None, k
     _check("pa_decode", lib.pa_decode(*[ctypes.byref(x) for x in args], float(scale),
                                       ctypes.byref(describe(out)), ctypes.byref(o),
                                       ts.cuda_stream))
+    return out
+
+
+def decode_append(k, v, slot_mapping, q, key_cache, value_cache, block_tables, seq_lens, scale,
+                  out=None, k_scale=1.0, v_scale=1.0, partition_tokens=0, variant=VARIANT_AUTO,
+                  workspace=None, err_flag=None, events=None, stream=None, bf16_partials=False):
+    """pa_decode_append: kv_append(k, v, slot_mapping, caches) then decode(q,
+    caches, ...), the append done inside the decode kernel where it takes
+    one (one new bf16 row per sequence on the matrix-core kernels).  Same
+    arguments and workspace as ``decode``; returns ``out``."""
+    lib = _load()
+    ts = _torch_stream(stream)
+    with torch.cuda.stream(ts):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            need = decode_workspace_size(q, key_cache, block_tables, partition_tokens, variant,
+                                         bf16_partials)
+            if need:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = _opts(k_scale, v_scale, partition_tokens, variant, workspace, err_flag, events,
+              bf16_partials)
+    args = [describe(x) for x in (k, v, slot_mapping, q, key_cache, value_cache, block_tables,
+                                  seq_lens)]
+    _check("pa_decode_append",
+           lib.pa_decode_append(*[ctypes.byref(x) for x in args], float(scale),
+                                ctypes.byref(describe(out)), ctypes.byref(o), ts.cuda_stream))
     return out
 
 

@@ -18,7 +18,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.cpp", "kv_append.hip", "decode_valu.hip", "decode_mfma.hip",
-           "decode_mfma_heads.hip", "decode_mfma_multi.hip", "merge.hip", "blocks.hip", "step_prep.hip", "cascade.hip",
+           "decode_mfma_append.hip", "decode_mfma_heads.hip", "decode_mfma_heads_append.hip",
+           "decode_mfma_multi.hip", "merge.hip", "blocks.hip", "step_prep.hip", "cascade.hip",
            "static_scratch.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
@@ -31,7 +32,9 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", f"--offload-arch={ARCH}",
 # accumulators with vector instructions, so they keep them in VGPRs rather than
 # copying them between AGPRs and VGPRs on every rescale.
 EXTRA = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "decode_mfma_append.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "decode_mfma_heads.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "decode_mfma_heads_append.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "decode_mfma_multi.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "cascade.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

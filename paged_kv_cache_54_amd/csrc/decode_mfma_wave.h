@@ -40,6 +40,12 @@
 // and of the cascade's suffix pass, which runs it over a batch viewed from a
 // later block on: row s of the tables at a.block_tables + s * v.stride, each
 // length less v.len_offset ({a.max_nb, 0} for a plain batch).
+//
+// The single-query kernels can also do the step's append (the new token's
+// K/V rows written to their slots, concept page "15-minute deep dive"): the
+// wavefront that holds a segment's last position writes that KV head's new
+// row to the cache and puts it into the staged tile in place of the stale
+// row it loaded, so no read has to wait for the write.
 #pragma once
 
 #include "mfma_common.h"
@@ -50,16 +56,17 @@ struct TableView {
     int stride, len_offset;
 };
 
+// Partials of G <= 8 rows written by lane pairs in whole lines.
+constexpr bool kPairedPartials = true;
+
 // One wavefront's attention state for the G query heads of one KV head over
 // a run of staged tiles: the Q^T operand, the fp32 accumulators, the running
 // softmax base and the lane-partial sum.  begin() starts a segment (a
 // sequence's KV head, or the part of it a chunk holds), attend() takes one
 // tile staged in LDS, finish() writes the segment's output rows or its
-// partial.  AB: partial accumulators stored as bf16 (else f32).
-// Partials of G <= 8 rows written by lane pairs in whole lines.
-constexpr bool kPairedPartials = true;
-
-template <int KT, int D, int BS, int G, bool AB>
+// partial.  AB: partial accumulators stored as bf16 (else f32).  APP: the
+// fused append is compiled in (append_row; its rows are loaded with Q).
+template <int KT, int D, int BS, int G, bool AB, bool APP = false>
 struct WaveAttn {
     using Geo = MfmaGeo<KT, D, BS>;
     static constexpr int NC = Geo::NC, ND = Geo::ND, TILE = Geo::TILE, MT = Geo::MT;
@@ -71,6 +78,15 @@ struct WaveAttn {
     f32x4 acc[ND];
     float m = -INFINITY, l = 0.f;
     bool seg_starts = false;
+    // fused append: this lane's 16 bytes of the segment's new K row (lanes
+    // [0, RC)) or V row (lanes [RC, 2 RC)), and the slot it goes to, read
+    // when the segment's last tile is attended.  That costs each segment
+    // end a memory round trip; loaded earlier (with Q, or right behind the
+    // last tile's loads) they took registers the tile loads needed, and
+    // waits between a tile's loads cut the tiles in flight to one.
+    static constexpr int RC = D / 8;           // 16-byte chunks of a bf16 row
+    uint4 nrow = make_uint4(0, 0, 0, 0);
+    int64_t nslot = -1;
 
     __device__ __forceinline__ explicit WaveAttn(int lane) : g4(lane >> 4), c16(lane & 15) {}
 
@@ -100,6 +116,85 @@ struct WaveAttn {
     {
         load_q(a, c);
         reset(c);
+    }
+
+    // Fused append, by the wavefront that staged the tile holding the
+    // segment's last position c.L - 1 (tile tokens tok_base ..).  The new
+    // rows go to cache slot nslot (e4m3: encoded as the append kernel
+    // encodes them); when nslot is that position's slot (block `id`) they
+    // also replace the staged rows, so the attention reads exactly what an
+    // append before the decode would have left there.  (A length clamped to
+    // the table makes c.L - 1 the last position the decode reads, and a row
+    // appended to its slot is what that read would find.)  id < 0: the block
+    // was out of range (nothing staged or replaced; the row is still
+    // written).
+    // append_row does the replacement (before the tile is attended) and
+    // marks the segment; append_store writes the cache rows with the
+    // segment's results, so a wavefront waits for its stores once per
+    // segment, not twice.  A slot outside the pool, or one that is not that
+    // position's, raises PA_DEVERR_SLOT (the first is not written).
+    bool nmark = false;                        // this wavefront writes the segment's rows
+
+    // the 8 values of this lane's 16 bytes of the new row, encoded as e4m3
+    __device__ __forceinline__ uint2 encode_new(float inv) const
+    {
+        const uint32_t w[4] = {nrow.x, nrow.y, nrow.z, nrow.w};
+        uint2 q = make_uint2(0, 0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            q.x |= f32_to_e4m3(bf16_lo(w[i]) * inv) << (16 * i);
+            q.x |= f32_to_e4m3(bf16_hi(w[i]) * inv) << (16 * i + 8);
+            q.y |= f32_to_e4m3(bf16_lo(w[2 + i]) * inv) << (16 * i);
+            q.y |= f32_to_e4m3(bf16_hi(w[2 + i]) * inv) << (16 * i + 8);
+        }
+        return q;
+    }
+
+    __device__ __forceinline__ void append_row(const DecodeArgs &a, uint8_t *kt, uint8_t *vt,
+                                               const Cursor &c, int id, int tok_base)
+    {
+        const int pos = c.L - 1 - tok_base;
+        if (!APP || !a.new_k || c.j != c.nb - 1 || pos < 0 || pos >= TILE)
+            return;
+        nslot = a.new_slots[c.s];
+        if (nslot < 0)
+            return;                            // nothing appended
+        nmark = true;
+        const int lane = 16 * g4 + c16, which = lane / RC, ch = lane % RC;
+        if (which < 2)
+            nrow = *reinterpret_cast<const uint4 *>(
+                static_cast<const uint16_t *>(which ? a.new_v : a.new_k) +
+                ((int64_t)c.s * a.num_kv_heads + c.kvh) * D + 8 * ch);
+        if (id < 0 || nslot != (int64_t)id * BS + (c.L - 1) % BS || which >= 2)
+            return;
+        uint4 lds_row = nrow;
+        if constexpr (KT == KT_E4M3)
+            lds_row = e4m3x8_to_bf16x8(encode_new(which ? a.v_inv_scale : a.k_inv_scale));
+        uint8_t *row = which ? vt + pos * VROWB : kt + pos * KROWB;
+        *reinterpret_cast<uint4 *>(row + 16 * ch) = lds_row;
+    }
+
+    // The cache rows of a segment append_row marked (c: its cursor, id: the
+    // block of its last position).
+    __device__ __forceinline__ void append_store(const DecodeArgs &a, const Cursor &c, int id)
+    {
+        if (!APP || !nmark)
+            return;
+        nmark = false;
+        const int64_t pool = (int64_t)a.num_blocks * BS;
+        const int64_t want = id >= 0 ? (int64_t)id * BS + (c.L - 1) % BS : -1;
+        if ((nslot != want || nslot >= pool) && g4 == 0 && c16 == 0)
+            raise_flag(a.err_flag, PA_DEVERR_SLOT);
+        const int lane = 16 * g4 + c16, which = lane / RC, ch = lane % RC;
+        if (nslot >= pool || which >= 2)
+            return;
+        const int64_t e = (nslot * a.num_kv_heads + c.kvh) * D + 8 * ch;   // element offset
+        void *cache = const_cast<void *>(which ? a.value_cache : a.key_cache);
+        if constexpr (KT == KT_E4M3)
+            *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(cache) + e) =
+                encode_new(which ? a.v_inv_scale : a.k_inv_scale);
+        else
+            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(cache) + e) = nrow;
     }
 
     // The segment's result in partial slot `slot` (segment record too): the
@@ -244,8 +339,8 @@ struct WaveAttn {
 
 // A wavefront's whole share of single-query decode: its chunk of the work list
 // (balanced or fixed), walked tile by tile through its own LDS tiles kt and vt
-// (TILE * KROWB and TILE * VROWB bytes).  AB as WaveAttn.
-template <int KT, int D, int BS, int G, bool AB>
+// (TILE * KROWB and TILE * VROWB bytes).  AB, APP as WaveAttn.
+template <int KT, int D, int BS, int G, bool AB, bool APP = false>
 __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView v, int w,
                                                  uint8_t *const kt, uint8_t *const vt)
 {
@@ -269,7 +364,7 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
     using Tile = MfmaTile<Geo>;
     auto load_tile = [&](int id, int kvh, int half, Tile &t) { loader.load(id, kvh, half, t); };
 
-    WaveAttn<KT, D, BS, G, AB> att(lane);
+    WaveAttn<KT, D, BS, G, AB, APP> att(lane);
 
     // Walk the chunk tile by tile: the load cursor runs one tile ahead of the
     // compute cursor, across block and segment boundaries.
@@ -309,12 +404,17 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
         if (id >= 0)           // stage as bf16, V rows past the sequence end as zeros
             stage_tile<Geo>(loader, kt, vt, t, tok_base, cc.L);
         issue_next();
+        // after the next tile's loads: the append waits for the rows loaded
+        // with Q, as the attention does
+        att.append_row(a, kt, vt, cc, id, tok_base);
         if (id >= 0)
             att.attend(a, kt, vt, tok_base, cc.L);
         if (half == HALVES - 1) {
             const bool ends = cc.j == cc.nb - 1;
-            if (ends || unit == n - 1)
+            if (ends || unit == n - 1) {
+                att.append_store(a, cc, id);
                 att.finish(a, cc, w + cc.s * Hkv + cc.kvh, ends);
+            }
             if (unit + 1 < n)
                 advance<BS>(cc, lens, Hkv, cap);
         }

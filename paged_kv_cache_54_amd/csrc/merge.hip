@@ -122,6 +122,10 @@ __global__ __launch_bounds__(64 * NW) void merge_kernel(DecodeArgs a, int block_
         }
     }
     bool zero_row = live && L <= 0;
+    // a fused append for a sequence with no tokens has no position to take
+    // the row: it is not written, and the contract violation is reported
+    if (zero_row && a.new_k && h == 0 && a.new_slots[s] >= 0)
+        raise_flag(a.err_flag, PA_DEVERR_SLOT);
     const int ss = a.slot_stride;                // slots of a segment: first, first + ss, ..
     if (live && L > 0) {
         // The decode pass writes both ends of every segment with tokens.  A

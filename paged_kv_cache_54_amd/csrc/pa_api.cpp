@@ -396,12 +396,64 @@ int block_op(const int32_t *ids, int64_t n, const void *const *src_bases,
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-// pa_decode (qsl == NULL, qm == 0), pa_decode_multi, and pa_decode_noalloc
-// (use_static: the workspace is the library's static device buffer).
+// Validation and arguments of pa_kv_append (and of pa_decode_append's append).
+int plan_append(const pa_tensor *k, const pa_tensor *v, const pa_tensor *slot_mapping,
+                const pa_tensor *key_cache, const pa_tensor *value_cache, const pa_opts *opts,
+                AppendArgs *a, int *in_type, int *cache_type)
+{
+    int rc;
+    if ((rc = check_tensor(k, 3, 16)) || (rc = check_tensor(v, 3, 16)) ||
+        (rc = check_tensor(slot_mapping, 1, 8)) || (rc = check_tensor(key_cache, 4, 16)) ||
+        (rc = check_tensor(value_cache, 4, 16)))
+        return rc;
+    if (slot_mapping->dtype != PA_I64)
+        return PA_ERR_DTYPE;
+    if (k->dtype != v->dtype || key_cache->dtype != value_cache->dtype)
+        return PA_ERR_DTYPE;
+    const int in_t = kv_type_of(k->dtype), cache_t = kv_type_of(key_cache->dtype);
+    if (in_t < 0 || in_t == KT_E4M3 || cache_t < 0)
+        return PA_ERR_DTYPE;
+    if (cache_t != KT_E4M3 && cache_t != in_t)
+        return PA_ERR_DTYPE;
+    for (int i = 0; i < 3; ++i)
+        if (k->shape[i] != v->shape[i])
+            return PA_ERR_SHAPE;
+    for (int i = 0; i < 4; ++i)
+        if (key_cache->shape[i] != value_cache->shape[i])
+            return PA_ERR_SHAPE;
+    const int64_t T = k->shape[0], Hkv = k->shape[1], D = k->shape[2];
+    if (slot_mapping->shape[0] != T || key_cache->shape[2] != Hkv || key_cache->shape[3] != D)
+        return PA_ERR_SHAPE;
+    if (!supported_head_dim(D) || !supported_block_size(key_cache->shape[1]))
+        return PA_ERR_UNSUPPORTED;
+    float ks = opts ? opts->k_scale : 1.0f, vs = opts ? opts->v_scale : 1.0f;
+    if (cache_t == KT_E4M3 && !(isfinite(ks) && ks > 0.0f && isfinite(vs) && vs > 0.0f))
+        return PA_ERR_UNSUPPORTED;
+    a->k = k->data;
+    a->v = v->data;
+    a->slots = static_cast<const int64_t *>(slot_mapping->data);
+    a->key_cache = key_cache->data;
+    a->value_cache = value_cache->data;
+    a->err_flag = opts ? opts->err_flag : nullptr;
+    a->num_tokens = T;
+    a->row_elems = Hkv * D;
+    a->num_slots = key_cache->shape[0] * key_cache->shape[1];
+    a->k_inv_scale = 1.0f / ks;
+    a->v_inv_scale = 1.0f / vs;
+    *in_type = in_t;
+    *cache_type = cache_t;
+    return PA_OK;
+}
+
+// pa_decode (qsl == NULL, qm == 0), pa_decode_multi, pa_decode_noalloc
+// (use_static: the workspace is the library's static device buffer) and
+// pa_decode_append (app: its append, validated; fused into the decode
+// kernel where that kernel takes one, else launched before it).
 int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_tensor *key_cache,
                const pa_tensor *value_cache, const pa_tensor *block_tables,
                const pa_tensor *seq_lens, float scale, pa_tensor *out, const pa_opts *opts,
-               void *hip_stream, bool use_static = false)
+               void *hip_stream, bool use_static = false, const AppendArgs *app = nullptr,
+               int app_in_type = 0)
 {
     int rc;
     if ((rc = check_tensor(q, 3, 16)) || (rc = check_tensor(key_cache, 4, 16)) ||
@@ -434,8 +486,13 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     DecodePlan p;
     if ((rc = plan_decode(q, key_cache, block_tables, opts, qm, &p)))
         return rc;
-    if (p.S == 0 || p.T == 0)
+    if (p.S == 0 || p.T == 0) {
+        if (app && app->num_tokens > 0 &&
+            launch_kv_append(*app, app_in_type, p.kv_type,
+                             static_cast<hipStream_t>(hip_stream)) != hipSuccess)
+            return PA_ERR_HIP;
         return PA_OK;
+    }
     pa_opts o;
     pa_opts_init(&o);
     if (opts)
@@ -481,6 +538,21 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
               (p.heads > 0 && acc_bytes(p) > kStreamPartialBytes ? kStreamPartials : 0);
     a.slot_stride = p.heads > 0 ? (int32_t)p.heads : 1;
     a.num_slots = (int32_t)p.slots;
+    // The matrix-core single-query kernels take one new bf16 row per
+    // sequence themselves, where the batch has no more (sequence, KV head)
+    // segments than wavefronts: each segment end costs its wavefront one
+    // memory round trip for the row, which beats the append's own launch
+    // at up to about one segment end per wavefront (Llama-shaped batch, 0.5:
+    // step 111.1 against 113.9 us) but not at two (Qwen-shaped, 2: 145.3
+    // against 138.3 us).  Any other append runs as its own launch first.
+    const bool fuse = app && p.variant == PA_VARIANT_MFMA && qm == 0 &&
+                      app_in_type == KT_BF16 && app->num_tokens == p.S &&
+                      p.S * p.Hkv <= p.waves;
+    a.new_k = fuse ? app->k : nullptr;
+    a.new_v = fuse ? app->v : nullptr;
+    a.new_slots = fuse ? app->slots : nullptr;
+    a.k_inv_scale = app ? app->k_inv_scale : 1.0f;
+    a.v_inv_scale = app ? app->v_inv_scale : 1.0f;
 
     // Fixed partitions on the per-block e4m3 kernel: no more workgroups than
     // the device holds at once, each walking an equal run of partitions.
@@ -495,6 +567,9 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     }
 
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    if (app && !fuse && app->num_tokens > 0 &&
+        launch_kv_append(*app, app_in_type, p.kv_type, stream) != hipSuccess)
+        return PA_ERR_HIP;
     hipEvent_t ev0 = static_cast<hipEvent_t>(o.kernel_events[0]);
     hipEvent_t ev1 = static_cast<hipEvent_t>(o.kernel_events[1]);
     if (ev0 && hipEventRecord(ev0, stream) != hipSuccess)
@@ -656,49 +731,11 @@ int pa_kv_append(const pa_tensor *k, const pa_tensor *v, const pa_tensor *slot_m
                  pa_tensor *key_cache, pa_tensor *value_cache, const pa_opts *opts,
                  void *hip_stream)
 {
-    int rc;
-    if ((rc = check_tensor(k, 3, 16)) || (rc = check_tensor(v, 3, 16)) ||
-        (rc = check_tensor(slot_mapping, 1, 8)) || (rc = check_tensor(key_cache, 4, 16)) ||
-        (rc = check_tensor(value_cache, 4, 16)))
-        return rc;
-    if (slot_mapping->dtype != PA_I64)
-        return PA_ERR_DTYPE;
-    if (k->dtype != v->dtype || key_cache->dtype != value_cache->dtype)
-        return PA_ERR_DTYPE;
-    const int in_t = kv_type_of(k->dtype), cache_t = kv_type_of(key_cache->dtype);
-    if (in_t < 0 || in_t == KT_E4M3 || cache_t < 0)
-        return PA_ERR_DTYPE;
-    if (cache_t != KT_E4M3 && cache_t != in_t)
-        return PA_ERR_DTYPE;
-    for (int i = 0; i < 3; ++i)
-        if (k->shape[i] != v->shape[i])
-            return PA_ERR_SHAPE;
-    for (int i = 0; i < 4; ++i)
-        if (key_cache->shape[i] != value_cache->shape[i])
-            return PA_ERR_SHAPE;
-    const int64_t T = k->shape[0], Hkv = k->shape[1], D = k->shape[2];
-    if (slot_mapping->shape[0] != T || key_cache->shape[2] != Hkv || key_cache->shape[3] != D)
-        return PA_ERR_SHAPE;
-    if (!supported_head_dim(D) || !supported_block_size(key_cache->shape[1]))
-        return PA_ERR_UNSUPPORTED;
-    float ks = opts ? opts->k_scale : 1.0f, vs = opts ? opts->v_scale : 1.0f;
-    if (cache_t == KT_E4M3 && !(isfinite(ks) && ks > 0.0f && isfinite(vs) && vs > 0.0f))
-        return PA_ERR_UNSUPPORTED;
-    if (T == 0)
-        return PA_OK;
-
     AppendArgs a;
-    a.k = k->data;
-    a.v = v->data;
-    a.slots = static_cast<const int64_t *>(slot_mapping->data);
-    a.key_cache = key_cache->data;
-    a.value_cache = value_cache->data;
-    a.err_flag = opts ? opts->err_flag : nullptr;
-    a.num_tokens = T;
-    a.row_elems = Hkv * D;
-    a.num_slots = key_cache->shape[0] * key_cache->shape[1];
-    a.k_inv_scale = 1.0f / ks;
-    a.v_inv_scale = 1.0f / vs;
+    int in_t = 0, cache_t = 0;
+    int rc = plan_append(k, v, slot_mapping, key_cache, value_cache, opts, &a, &in_t, &cache_t);
+    if (rc || a.num_tokens == 0)
+        return rc;
     hipError_t e = launch_kv_append(a, in_t, cache_t, static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -806,6 +843,20 @@ int pa_decode(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *v
 {
     return run_decode(q, nullptr, 0, key_cache, value_cache, block_tables, seq_lens, scale, out,
                       opts, hip_stream);
+}
+
+int pa_decode_append(const pa_tensor *k, const pa_tensor *v, const pa_tensor *slot_mapping,
+                     const pa_tensor *q, pa_tensor *key_cache, pa_tensor *value_cache,
+                     const pa_tensor *block_tables, const pa_tensor *seq_lens, float scale,
+                     pa_tensor *out, const pa_opts *opts, void *hip_stream)
+{
+    AppendArgs app;
+    int in_t = 0, cache_t = 0;
+    int rc = plan_append(k, v, slot_mapping, key_cache, value_cache, opts, &app, &in_t, &cache_t);
+    if (rc)
+        return rc;
+    return run_decode(q, nullptr, 0, key_cache, value_cache, block_tables, seq_lens, scale, out,
+                      opts, hip_stream, false, &app, in_t);
 }
 
 int pa_decode_noalloc(const pa_tensor *q, const pa_tensor *key_cache, const pa_tensor *value_cache,
@@ -939,6 +990,9 @@ int pa_decode_cascade(const pa_tensor *q, const pa_tensor *key_cache,
     sa.flags = kPartialOnly | (sp.acc_bf16 ? kPartialsBf16 : 0);
     sa.slot_stride = 1;
     sa.num_slots = (int32_t)sp.slots;
+    sa.new_k = sa.new_v = nullptr;
+    sa.new_slots = nullptr;
+    sa.k_inv_scale = sa.v_inv_scale = 1.0f;
 
     CascadeMergeArgs ma;
     ma.out = out->data;

@@ -44,6 +44,13 @@ struct DecodeArgs {
     int32_t flags;               // kPartialOnly | kPartialsBf16
     int32_t slot_stride;         // slots of one segment's partials step by this (>= 1)
     int32_t num_slots;           // slots of the workspace
+    // Append fused into the decode (matrix-core single-query kernels): row s
+    // of new_k / new_v [S, Hkv, D] (bf16) goes to cache slot new_slots[s],
+    // which should be the slot of position seq_lens[s] - 1, and the attention
+    // takes it at that position.  new_k NULL: no append.
+    const void *new_k, *new_v;
+    const int64_t *new_slots;    // [S]; < 0: nothing appended
+    float k_inv_scale, v_inv_scale;   // e4m3 caches: 1 / k_scale, 1 / v_scale (binary32)
 };
 
 // DecodeArgs.flags.  kPartialOnly (matrix-core kernels): every segment ends

@@ -37,7 +37,8 @@ def test_header_declares_the_expected_entry_points():
         ["pa_kv_append", "pa_decode", "pa_decode_workspace_size", "pa_opts_init",
          "pa_status_string", "pa_version", "pa_zero_blocks", "pa_copy_blocks",
          "pa_decode_multi", "pa_decode_multi_workspace_size", "pa_prepare_step",
-         "pa_decode_cascade", "pa_decode_cascade_workspace_size", "pa_decode_noalloc"])
+         "pa_decode_cascade", "pa_decode_cascade_workspace_size", "pa_decode_noalloc",
+         "pa_decode_append"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -50,7 +51,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert pa.version() == 2
+    assert pa.version() == 3
     for code in range(10):
         assert pa.status_string(code) and pa.status_string(code) != "unknown status"
     assert pa.status_string(99) == "unknown status"
@@ -359,6 +360,43 @@ def test_decode_noalloc_validation_errors():
     assert lib().pa_decode_workspace_size(r(big["q"]), r(big["kc"]), r(big["bt"]),
                                           r(opts(partition_tokens=512)), ctypes.byref(n)) == PA_OK
     assert n.value <= pa.NOALLOC_MAX_WORKSPACE
+
+
+def test_decode_append_validation_errors():
+    """pa_decode_append checks its append like pa_kv_append and its decode
+    like pa_decode, all before anything is queued."""
+    r = lambda x: None if x is None else ctypes.byref(x)
+
+    def call(k, v, slots, a, o=None, scale=0.125):
+        return lib().pa_decode_append(r(k), r(v), r(slots), r(a["q"]), r(a["kc"]), r(a["vc"]),
+                                      r(a["bt"]), r(a["lens"]), scale, r(a["out"]), r(o), None)
+    a = decode_args(S=4, H=8, Hkv=2, D=64, qd=BF16, kd=BF16)
+    k, slots = desc([4, 2, 64], BF16), desc([4], I64)
+    P = opts(partition_tokens=64)
+    # empty batch and no rows: nothing to do
+    e = decode_args(S=0, H=8, Hkv=2, D=64, qd=BF16, kd=BF16)
+    assert call(desc([0, 2, 64], BF16), desc([0, 2, 64], BF16), desc([0], I64), e, P) == PA_OK
+    # the append's checks
+    assert call(None, k, slots, a, P) == PA_ERR_NULL
+    assert call(k, k, desc([4], I32), a, P) == PA_ERR_DTYPE
+    assert call(desc([4, 2, 64], F32), desc([4, 2, 64], F32), slots, a, P) == PA_ERR_DTYPE
+    assert call(k, k, desc([5], I64), a, P) == PA_ERR_SHAPE
+    assert call(desc([4, 4, 64], BF16), desc([4, 4, 64], BF16), desc([4], I64), a, P) \
+        == PA_ERR_SHAPE                                                   # Hkv differs
+    assert call(desc([4, 2, 64], BF16, data=FAKE + 2), k, slots, a, P) == PA_ERR_ALIGN
+    # the decode's checks, with a valid append
+    bad = dict(a)
+    bad["q"] = None
+    assert call(k, k, slots, bad, P) == PA_ERR_NULL
+    bad = dict(a)
+    bad["out"] = desc([4, 8, 64], F32)
+    assert call(k, k, slots, bad, P) == PA_ERR_DTYPE
+    bad = dict(a)
+    bad["lens"] = desc([3], I32)
+    assert call(k, k, slots, bad, P) == PA_ERR_SHAPE
+    assert call(k, k, slots, a, P, scale=float("nan")) == PA_ERR_UNSUPPORTED
+    assert call(k, k, slots, a, opts(partition_tokens=24)) == PA_ERR_UNSUPPORTED
+    assert call(k, k, slots, a, opts(partition_tokens=64, partials=2)) == PA_ERR_UNSUPPORTED
 
 
 def test_noalloc_limit_matches_header():
