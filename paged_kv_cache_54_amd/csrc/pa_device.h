@@ -339,9 +339,12 @@ __device__ __forceinline__ void advance(Cursor &c, Lens lens, int Hkv, int cap)
 }
 
 // Physical block id of a cursor position, wave-uniform; ids of one sequence
-// are read 64 at a time by the lanes and handed out with readlane.  An id
-// outside [0, num_blocks) comes back as -1 and raises PA_DEVERR_BLOCK_ID.
-// Row s of the tables starts at tables + s * stride; max_nb entries are read.
+// are read 64 at a time by the lanes, in windows starting at multiples of 64
+// (a walk that moves to the next KV head of the same sequence restarts at
+// block 0, which then stays in the window), and handed out with readlane.
+// An id outside [0, num_blocks) comes back as -1 and raises
+// PA_DEVERR_BLOCK_ID.  Row s of the tables starts at tables + s * stride;
+// max_nb entries are read.
 struct BlockIds {
     const int32_t *tables;
     int stride, max_nb, num_blocks;
@@ -358,8 +361,8 @@ struct BlockIds {
     {
         if (s_ != s || j < base || j >= base + 64) {
             s = s_;
-            base = j;
-            const int jj = j + lane_id();
+            base = j & ~63;
+            const int jj = base + lane_id();
             ids = jj < max_nb ? tables[(int64_t)s_ * stride + jj] : 0;
         }
         const int id = __builtin_amdgcn_readlane(ids, j - base);
@@ -372,7 +375,8 @@ struct BlockIds {
 
 // BlockIds whose following 64 entries of the same table row are read one
 // window ahead, so a walk along a sequence waits for the table only at its
-// first block (and at a jump), not every 64 blocks.
+// first block (and at a jump), not every 64 blocks.  Windows start at
+// multiples of 64 as in BlockIds.
 struct BlockIdsAhead {
     const int32_t *tables;
     int stride, max_nb, num_blocks;
@@ -399,8 +403,8 @@ struct BlockIdsAhead {
                 base += 64;
             } else {
                 s = s_;
-                base = j;
-                ids = fetch(s_, j);
+                base = j & ~63;
+                ids = fetch(s_, base);
             }
             next = fetch(s, base + 64);
         }
