@@ -35,16 +35,20 @@ KERNEL_SOURCES = {
     "valu": ["paged_kv_cache_54_amd/csrc/decode_valu.hip", "paged_kv_cache_54_amd/csrc/pa_device.h"],
     "mfma": ["paged_kv_cache_54_amd/csrc/decode_mfma.hip",
              "paged_kv_cache_54_amd/csrc/decode_mfma_wave.h",
-             "paged_kv_cache_54_amd/csrc/mfma_common.h", "paged_kv_cache_54_amd/csrc/pa_device.h"],
+             "paged_kv_cache_54_amd/csrc/mfma_common.h", "paged_kv_cache_54_amd/csrc/pa_device.h",
+             "paged_kv_cache_54_amd/csrc/decode_mfma_kernel.h",
+             "paged_kv_cache_54_amd/csrc/decode_mfma_append.hip"],
     "mfma_multi": ["paged_kv_cache_54_amd/csrc/decode_mfma_multi.hip",
                    "paged_kv_cache_54_amd/csrc/mfma_common.h",
                    "paged_kv_cache_54_amd/csrc/pa_device.h"],
 }
 KERNEL_SOURCES["blocks"] = ["paged_kv_cache_54_amd/csrc/blocks.hip",
                             "paged_kv_cache_54_amd/csrc/pa_device.h"]
-KERNEL_SOURCES["cascade"] = KERNEL_SOURCES["mfma"] + ["paged_kv_cache_54_amd/csrc/cascade.hip"]
-KERNEL_SOURCES["mfma_heads"] = ["paged_kv_cache_54_amd/csrc/decode_mfma_heads.hip"] + \
-    KERNEL_SOURCES["mfma"][1:]
+KERNEL_SOURCES["cascade"] = KERNEL_SOURCES["mfma"][1:4] + ["paged_kv_cache_54_amd/csrc/cascade.hip"]
+KERNEL_SOURCES["mfma_heads"] = ["paged_kv_cache_54_amd/csrc/decode_mfma_heads.hip",
+                                "paged_kv_cache_54_amd/csrc/decode_mfma_heads_kernel.h",
+                                "paged_kv_cache_54_amd/csrc/decode_mfma_heads_append.hip"] + \
+    KERNEL_SOURCES["mfma"][1:4]
 KERNEL_NAMES = {"valu": "decode_valu_kernel", "mfma": "decode_mfma_kernel",
                 "mfma_multi": "decode_mfma_multi_kernel",
                 "cascade": "cascade_kernel", "mfma_heads": "decode_mfma_heads_kernel"}
