@@ -79,11 +79,13 @@ struct WaveAttn {
     float m = -INFINITY, l = 0.f;
     bool seg_starts = false;
     // fused append: this lane's 16 bytes of the segment's new K row (lanes
-    // [0, RC)) or V row (lanes [RC, 2 RC)), and the slot it goes to, read
-    // when the segment's last tile is attended.  That costs each segment
-    // end a memory round trip; loaded earlier (with Q, or right behind the
-    // last tile's loads) they took registers the tile loads needed, and
-    // waits between a tile's loads cut the tiles in flight to one.
+    // [0, RC)) or V row (lanes [RC, 2 RC)), and the slot it goes to.  bf16:
+    // the row arrives with the last tile's own loads (load_with_row) and the
+    // slot is read with Q.  e4m3 (the row must be encoded first): both are
+    // read when the last tile is attended, a memory round trip per segment
+    // end; loaded earlier (with Q, or right behind the last tile's loads)
+    // they took registers the tile loads needed, and waits between a tile's
+    // loads cut the tiles in flight to one.
     static constexpr int RC = D / 8;           // 16-byte chunks of a bf16 row
     uint4 nrow = make_uint4(0, 0, 0, 0);
     int64_t nslot = -1;
@@ -99,6 +101,8 @@ struct WaveAttn {
 #pragma unroll
         for (int k = 0; k < NC; ++k)
             qop[k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * k));
+        if (APP && KT == KT_BF16 && a.new_k)
+            nslot = a.new_slots[c.s];
     }
 
     // Empty accumulators and softmax state for a run of tiles starting at c.
@@ -156,6 +160,34 @@ struct WaveAttn {
         const int pos = c.L - 1 - tok_base;
         if (!APP || !a.new_k || c.j != c.nb - 1 || pos < 0 || pos >= TILE)
             return;
+        if constexpr (KT == KT_BF16) {
+            // The tile's loads brought the new rows in at pos.  Kept when
+            // nslot is that position's slot (and read back for the cache
+            // store); otherwise the cache's own row goes back in (and the new
+            // row, if any, is read for the store), as after a separate
+            // append.  Both are rare.
+            const int lane = 16 * g4 + c16, which = lane / RC, ch = lane % RC;
+            nmark = nslot >= 0;
+            const bool keep = id >= 0 && nslot == (int64_t)id * BS + (c.L - 1) % BS;
+            if (which >= 2)
+                return;
+            uint8_t *row = (which ? vt + pos * VROWB : kt + pos * KROWB) + 16 * ch;
+            if (keep) {
+                nrow = *reinterpret_cast<const uint4 *>(row);
+                return;
+            }
+            const int64_t hrow = ((int64_t)c.s * a.num_kv_heads + c.kvh) * D + 8 * ch;
+            if (nmark)
+                nrow = *reinterpret_cast<const uint4 *>(
+                    static_cast<const uint16_t *>(which ? a.new_v : a.new_k) + hrow);
+            if (id >= 0) {
+                const int64_t e =
+                    (((int64_t)id * BS + (c.L - 1) % BS) * a.num_kv_heads + c.kvh) * D + 8 * ch;
+                *reinterpret_cast<uint4 *>(row) = *reinterpret_cast<const uint4 *>(
+                    static_cast<const uint16_t *>(which ? a.value_cache : a.key_cache) + e);
+            }
+            return;
+        }
         nslot = a.new_slots[c.s];
         if (nslot < 0)
             return;                            // nothing appended
@@ -362,8 +394,6 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
 
     const MfmaLoader<Geo> loader(a, lane);
     using Tile = MfmaTile<Geo>;
-    auto load_tile = [&](int id, int kvh, int half, Tile &t) { loader.load(id, kvh, half, t); };
-
     WaveAttn<KT, D, BS, G, AB, APP> att(lane);
 
     // Walk the chunk tile by tile: the load cursor runs one tile ahead of the
@@ -371,6 +401,23 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
     BlockIds ids(a.block_tables, v.stride, a.max_nb, a.num_blocks, a.err_flag);
     Cursor cc = chunk.start;
     Cursor lc = cc;
+
+    // Tile loads at the load cursor; with a bf16 append inside, a segment's
+    // last tile brings the new rows in place of the cache's at its last
+    // position.
+    auto load_tile = [&](int id, int kvh, int half, Tile &t) {
+        if constexpr (APP && KT == KT_BF16) {
+            int rpos = lc.L - 1 - (lc.j * BS + half * TILE);
+            if (!a.new_k || lc.j != lc.nb - 1 || rpos >= TILE)
+                rpos = -1;
+            const int64_t r = ((int64_t)lc.s * Hkv + lc.kvh) * D * 2;
+            load_with_row<Geo>(loader, id, kvh, half, t, rpos,
+                               static_cast<const char *>(a.new_k) + r,
+                               static_cast<const char *>(a.new_v) + r);
+        } else {
+            loader.load(id, kvh, half, t);
+        }
+    };
     const int n = chunk.n;                     // units (blocks)
     const int steps = n * HALVES;              // tiles
 

@@ -238,6 +238,39 @@ struct MfmaLoader {
     }
 };
 
+// Loads of a bf16 tile as MfmaLoader::load, except that the row at tile
+// position rpos (if 0 <= rpos < TILE) comes from the bf16 rows nk / nv (D
+// elements each; this lane reads its chunk) instead of the cache: the new
+// token's rows of a step whose append the decode kernel does, brought in by
+// the tile's own load instructions (no extra load, no wait).  Used for every
+// tile (rpos < 0: none replaced), one load path: with a branch between this
+// and the plain loads the compiler put waits between a tile's loads.
+template <class Geo>
+__device__ __forceinline__ void load_with_row(const MfmaLoader<Geo> &ld, int id, int kvh, int half,
+                                              MfmaTile<Geo> &t, int rpos, const char *nk,
+                                              const char *nv)
+{
+    static_assert(Geo::KT == KT_BF16, "the new rows are bf16, as the cache rows");
+    const int64_t base = (int64_t)(id < 0 ? 0 : id) * ld.block_bytes + ld.l_voff +
+                         kvh * Geo::D * Geo::EB + half * Geo::TILE * ld.slot_bytes;
+    const char *pk = static_cast<const char *>(ld.key_cache) + base;
+    const char *pv = static_cast<const char *>(ld.value_cache) + base;
+    const int step = Geo::LROWS * ld.slot_bytes;
+    const bool mine = rpos >= 0 && ld.l_row == rpos % Geo::LROWS;   // this lane: the new row
+#pragma unroll
+    for (int i = 0; i < Geo::NLOAD; ++i) {
+        const char *ak = pk + i * step, *av = pv + i * step;
+        if (mine && i == rpos / Geo::LROWS) {
+            ak = nk + ld.l_chunk * 16;
+            av = nv + ld.l_chunk * 16;
+        }
+        const u32x4 a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(ak));
+        const u32x4 b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(av));
+        t.k[i] = make_uint4(a.x, a.y, a.z, a.w);
+        t.v[i] = make_uint4(b.x, b.y, b.z, b.w);
+    }
+}
+
 // Store one tensor's rows into an LDS tile (row stride ROWB) as bf16; with
 // MASK, rows whose token is at or beyond t1 are stored as zeros.
 template <class Geo, int ROWB, bool MASK>

@@ -539,12 +539,14 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     a.slot_stride = p.heads > 0 ? (int32_t)p.heads : 1;
     a.num_slots = (int32_t)p.slots;
     // The matrix-core single-query kernels take one new bf16 row per
-    // sequence themselves, where the batch has no more (sequence, KV head)
-    // segments than wavefronts: each segment end costs its wavefront one
-    // memory round trip for the row, which beats the append's own launch
-    // at up to about one segment end per wavefront (Llama-shaped batch, 0.5:
-    // step 111.1 against 113.9 us) but not at two (Qwen-shaped, 2: 145.3
-    // against 138.3 us).  Any other append runs as its own launch first.
+    // sequence themselves (a bf16 cache's new rows come in with the last
+    // tile's own loads; an e4m3 cache's are read and encoded when that tile
+    // is attended), where the batch has no more (sequence, KV head)
+    // segments than wavefronts: the work at each segment end beats the
+    // append's own launch at up to about one segment end per wavefront
+    // (Llama-shaped batch, 0.5: step 109.9 against 112.6 us, the kernel
+    // unchanged) but not at two (Qwen-shaped: 139.8 against 138.0 us).  Any
+    // other append runs as its own launch first.
     const bool fuse = app && p.variant == PA_VARIANT_MFMA && qm == 0 &&
                       app_in_type == KT_BF16 && app->num_tokens == p.S &&
                       p.S * p.Hkv <= p.waves;
