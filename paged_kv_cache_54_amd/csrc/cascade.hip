@@ -352,7 +352,7 @@ __attribute__((amdgpu_waves_per_eu(cascade_waves_per_simd<KT, D, BS>()))) void c
     wg -= p.check_wgs;
     const int wave = threadIdx.x >> 6;
     // wavefronts past s.num_waves get no chunk
-    const TableView view{p.max_nb, p.prefix_blocks * p.block_size};
+    const TableView view{p.max_nb, p.prefix_blocks * p.block_size, true};
     decode_mfma_wave<KT, D, BS, G, AB>(s, view, wg * kSuffixWaves + wave, lds + wave * KTILE,
                                    vt0 + wave * VTILE);
 }

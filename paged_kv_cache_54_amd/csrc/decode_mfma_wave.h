@@ -39,7 +39,8 @@
 // and TILE * VROWB bytes).  It is the body of the single-query decode kernel
 // and of the cascade's suffix pass, which runs it over a batch viewed from a
 // later block on: row s of the tables at a.block_tables + s * v.stride, each
-// length less v.len_offset ({a.max_nb, 0} for a plain batch).
+// length less v.len_offset ({a.max_nb, 0} for a plain batch); v.deep asks
+// for two register tiles in flight with balanced chunks (below).
 //
 // The single-query kernels can also do the step's append (the new token's
 // K/V rows written to their slots, concept page "15-minute deep dive"): the
@@ -54,6 +55,7 @@ namespace pa {
 
 struct TableView {
     int stride, len_offset;
+    bool deep = false;
 };
 
 // Partials of G <= 8 rows written by lane pairs in whole lines.
@@ -177,9 +179,10 @@ struct WaveAttn {
                 return;
             }
             const int64_t hrow = ((int64_t)c.s * a.num_kv_heads + c.kvh) * D + 8 * ch;
-            if (nmark)
-                nrow = *reinterpret_cast<const uint4 *>(
-                    static_cast<const uint16_t *>(which ? a.new_v : a.new_k) + hrow);
+            if (nmark)        // settled: the store at the segment's end waits for
+                              // this rare load here, not on every segment
+                nrow = settled(*reinterpret_cast<const uint4 *>(
+                    static_cast<const uint16_t *>(which ? a.new_v : a.new_k) + hrow));
             if (id >= 0) {
                 const int64_t e =
                     (((int64_t)id * BS + (c.L - 1) % BS) * a.num_kv_heads + c.kvh) * D + 8 * ch;
@@ -378,10 +381,15 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
 {
     using Geo = MfmaGeo<KT, D, BS>;
     constexpr int TILE = Geo::TILE, HALVES = Geo::HALVES;
-    // bf16: two register tiles in flight.  e4m3: two with fixed-size chunks
-    // (short chunks, many rounds of wavefronts: the second tile shortens each
-    // chunk's start), one with balanced chunks (measured faster there).
-    const bool pingpong = KT == KT_BF16 || a.chunk_units > 0;
+    // Register tiles in flight while a tile is computed: two with fixed-size
+    // chunks (short chunks, many rounds of wavefronts: the second tile
+    // shortens each chunk's start) and for a deep view (the cascade's suffix
+    // pass: a small batch, where start-up dominates); one with balanced
+    // chunks.  One tile per wavefront puts about 16 MB in flight at two
+    // wavefronts per SIMD, and that streams fastest: two measured 6 % slower
+    // on the Llama-shaped batch and 2 % on the Qwen-shaped one (3 % faster on
+    // the shared-prefix suffix pass).
+    const bool pingpong = v.deep || a.chunk_units > 0;
 
     const int lane = threadIdx.x & 63;
     const int Hkv = a.num_kv_heads;
@@ -448,8 +456,12 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
     auto step = [&](int k, int id, int half, const Tile &t, auto issue_next) {
         const int unit = k / HALVES;
         const int tok_base = cc.j * BS + half * TILE;
-        if (id >= 0)           // stage as bf16, V rows past the sequence end as zeros
-            stage_tile<Geo>(loader, kt, vt, t, tok_base, cc.L);
+        // Stage as bf16, V rows past the sequence end as zeros.  A missing
+        // block (id < 0, block 0 read) is staged too and never attended:
+        // staging on every path is what tells the compiler that this
+        // register tile's loads are done, so the next loads into it do not
+        // wait for the other tile's.
+        stage_tile<Geo>(loader, kt, vt, t, tok_base, cc.L);
         issue_next();
         // after the next tile's loads: the append waits for the rows loaded
         // with Q, as the attention does
@@ -471,24 +483,31 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
     // wait before staging a tile counts exactly the loads issued after it.
     if (pingpong) {
         // Two register tiles: tile k+1 is loaded into the other tile before
-        // tile k is waited on, so two tiles are in flight at the wait.
+        // tile k is waited on, so two tiles are in flight at the wait.  The
+        // loop takes whole pairs and an odd last tile follows it: an exit
+        // from the middle of the loop body would reach the loop's back edge
+        // in the compiler's view with the second tile still loading, and it
+        // would then wait for that tile at every pair.
         Tile ta, tb;
         int ida = l_id, ha = l_half;
         load_tile(ida, lc.kvh, ha, ta);
-        for (int k = 0; k < steps; k += 2) {
+        int k = 0;
+        for (; k + 1 < steps; k += 2) {
             pre_step(k, ha);
             next_load(k + 1);
             const int idb = l_id, hb = l_half;
             load_tile(idb, lc.kvh, hb, tb);
             step(k, ida, ha, ta, [] {});
-            if (k + 1 >= steps)
-                break;
             pre_step(k + 1, hb);
             next_load(k + 2);
             ida = l_id;
             ha = l_half;
             load_tile(ida, lc.kvh, ha, ta);
             step(k + 1, idb, hb, tb, [] {});
+        }
+        if (k < steps) {
+            pre_step(k, ha);
+            step(k, ida, ha, ta, [] {});
         }
     } else {
         // One register tile: tile k is staged into LDS, then the loads of tile

@@ -235,6 +235,24 @@ __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, int voff, i
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// v itself, as a fresh register value.  A value loaded on a rarely taken path
+// and read on the common one (a block-id window refreshed every 64 blocks)
+// makes the compiler wait for it on the common path as if the load were still
+// outstanding; the memory-load counter retires in order, so that wait also
+// drains every tile load in flight.  Passing the value through this opaque
+// move right after its load puts the wait on the rare path, where it is due.
+__device__ __forceinline__ int settled(int v)
+{
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+__device__ __forceinline__ uint4 settled(uint4 v)
+{
+    return make_uint4(settled((int)v.x), settled((int)v.y), settled((int)v.z), settled((int)v.w));
+}
+
 __device__ __forceinline__ int wave_sum_i(int x)
 {
 #pragma unroll
@@ -363,7 +381,7 @@ struct BlockIds {
             s = s_;
             base = j & ~63;
             const int jj = base + lane_id();
-            ids = jj < max_nb ? tables[(int64_t)s_ * stride + jj] : 0;
+            ids = settled(jj < max_nb ? tables[(int64_t)s_ * stride + jj] : 0);
         }
         const int id = __builtin_amdgcn_readlane(ids, j - base);
         const bool bad = id < 0 || id >= num_blocks;
@@ -440,7 +458,7 @@ __device__ __forceinline__ int64_t chunk_len(const DecodeArgs &a, int64_t U, int
 }
 
 template <int BS>
-__device__ Chunk my_chunk(const DecodeArgs &a, Lens lens, int w, int W, bool runs = false)
+__device__ Chunk find_chunk(const DecodeArgs &a, Lens lens, int w, int W, bool runs)
 {
     const int S = a.num_seqs, Hkv = a.num_kv_heads;
     const int cap = a.max_nb * BS;
@@ -494,6 +512,27 @@ __device__ Chunk my_chunk(const DecodeArgs &a, Lens lens, int w, int W, bool run
         base += tot[k];
     }
     return Chunk{u0, (int)min(cl, U - u0), cur};
+}
+
+__device__ __forceinline__ int uniform_i(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// find_chunk's result, every field marked wave-uniform (it is: it derives
+// from kernel arguments, block ids and cross-lane reductions).  The compiler
+// cannot prove that through find_chunk's branches; without the mark the
+// chunk walk's loop exits become per-lane branches, and their joins make the
+// compiler wait for register tiles that are in fact complete.
+template <int BS>
+__device__ Chunk my_chunk(const DecodeArgs &a, Lens lens, int w, int W, bool runs = false)
+{
+    Chunk c = find_chunk<BS>(a, lens, w, W, runs);
+    c.n = uniform_i(c.n);
+    c.u0 = ((int64_t)uniform_i((int)(c.u0 >> 32)) << 32) | (uint32_t)uniform_i((int)c.u0);
+    c.start.s = uniform_i(c.start.s);
+    c.start.kvh = uniform_i(c.start.kvh);
+    c.start.j = uniform_i(c.start.j);
+    c.start.nb = uniform_i(c.start.nb);
+    c.start.L = uniform_i(c.start.L);
+    return c;
 }
 
 // Slot of chunk w's result for segment g, and the record the merge reads:
