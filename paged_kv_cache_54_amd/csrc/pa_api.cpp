@@ -294,12 +294,13 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
                 return rc;
             p->waves = (int64_t)cus * per_cu;
             // Single-query decode of a bf16 cache on the matrix cores: half as
-            // many wavefronts, each with a chunk twice as long.  With two
-            // register tiles in flight per wavefront that still keeps enough
-            // bytes moving, and a chunk's pipeline start and partial writes
-            // come half as often (1-4 % faster over bf16 batches of 8-256
-            // sequences).  An e4m3 cache's balanced chunks keep one tile in
-            // flight and need every resident wavefront.
+            // many wavefronts, each with a chunk twice as long.  One register
+            // tile in flight per wavefront (about 8 MB over the device) still
+            // keeps enough bytes moving, and a chunk's pipeline start and
+            // partial writes come half as often (1-4 % faster over bf16
+            // batches of 8-256 sequences; a quarter of the wavefronts with
+            // two tiles each was 30 % slower).  An e4m3 cache's per-wavefront
+            // kernel needs every resident wavefront.
             if (p->variant == PA_VARIANT_MFMA && qm == 0 && p->kv_type == KT_BF16)
                 p->waves = (p->waves + 1) / 2;
             if (max_units > 0 && max_units < p->waves)
