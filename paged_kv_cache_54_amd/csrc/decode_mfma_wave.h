@@ -418,10 +418,17 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
             int rpos = lc.L - 1 - (lc.j * BS + half * TILE);
             if (!a.new_k || lc.j != lc.nb - 1 || rpos >= TILE)
                 rpos = -1;
-            const int64_t r = ((int64_t)lc.s * Hkv + lc.kvh) * D * 2;
-            load_with_row<Geo>(loader, id, kvh, half, t, rpos,
-                               static_cast<const char *>(a.new_k) + r,
-                               static_cast<const char *>(a.new_v) + r);
+            // Plain loads on every other tile: the per-lane address select
+            // on each tile cost the Llama-shaped kernel 2 % at one wavefront
+            // per SIMD.
+            if (rpos < 0) {
+                loader.load(id, kvh, half, t);
+            } else {
+                const int64_t r = ((int64_t)lc.s * Hkv + lc.kvh) * D * 2;
+                load_with_row<Geo>(loader, id, kvh, half, t, rpos,
+                                   static_cast<const char *>(a.new_k) + r,
+                                   static_cast<const char *>(a.new_v) + r);
+            }
         } else {
             loader.load(id, kvh, half, t);
         }

@@ -200,7 +200,7 @@ struct MfmaTile {
 // nontemporal global loads from the block's address (measured 0.2-1.1 %
 // faster than buffer loads through a per-block resource on the decode
 // batches).  A missing block (id < 0) reads block 0 instead -- in bounds,
-// and the caller never stages that tile -- so the loads can still be issued
+// and the caller never attends that tile -- so the loads can still be issued
 // unconditionally.
 template <class Geo>
 struct MfmaLoader {
@@ -242,9 +242,9 @@ struct MfmaLoader {
 // position rpos (if 0 <= rpos < TILE) comes from the bf16 rows nk / nv (D
 // elements each; this lane reads its chunk) instead of the cache: the new
 // token's rows of a step whose append the decode kernel does, brought in by
-// the tile's own load instructions (no extra load, no wait).  Used for every
-// tile (rpos < 0: none replaced), one load path: with a branch between this
-// and the plain loads the compiler put waits between a tile's loads.
+// the tile's own load instructions (no extra load, no wait).  Used for a
+// segment's last tile only (rpos < 0: none replaced); other tiles take the
+// plain loads, since the per-lane select on every tile cost 2 %.
 template <class Geo>
 __device__ __forceinline__ void load_with_row(const MfmaLoader<Geo> &ld, int id, int kvh, int half,
                                               MfmaTile<Geo> &t, int rpos, const char *nk,
