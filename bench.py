@@ -572,11 +572,11 @@ def main():
     if used == "mfma" and not multi and _heads_kernel(b):
         used = "mfma_heads"
     # The library fuses the append into the matrix-core one-query kernels
-    # when the batch has no more (sequence, KV head) segments than the kernel
-    # has wavefronts; the wavefronts follow from the workspace size, whose
-    # slots are wavefronts + segments.
+    # when the batch has at most two (sequence, KV head) segments per
+    # wavefront; the wavefronts follow from the workspace size, whose slots
+    # are wavefronts + segments.
     in_kernel = (fused and used in ("mfma", "mfma_heads") and b.k_new.shape[0] == b.num_seqs
-                 and b.num_seqs * b.num_kv_heads <= _waves(b, ws_bytes, bf16p))
+                 and b.num_seqs * b.num_kv_heads <= 2 * _waves(b, ws_bytes, bf16p))
     kernel_bytes = nbytes["decode"] + (nbytes["append"] if in_kernel else 0)
     achieved = kernel_bytes / (kernel_ms * 1e-3) / 1e9
     kname = KERNEL_NAMES[used]

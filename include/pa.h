@@ -223,8 +223,10 @@ int pa_decode_workspace_size(const pa_tensor *q, const pa_tensor *key_cache,
  *
  * Results, caches and the error word are those of the two calls.  Where the
  * decode runs on the matrix cores with one new BF16 row per sequence (T = S,
- * row s belonging to sequence s) and the batch has no more (sequence, KV
- * head) pairs than the decode kernel has wavefronts, the append is done
+ * row s belonging to sequence s) and the batch has at most twice as many
+ * (sequence, KV head) pairs as the decode kernel has wavefronts (a number
+ * the plan takes from the device's compute units and the kernel's
+ * occupancy), the append is done
  * inside the decode kernel: the row of sequence s is written to
  * slot_mapping[s] and taken as the key/value at position seq_lens[s] - 1
  * without a round trip through the cache -- one launch less.  That form needs slot_mapping[s] to be the

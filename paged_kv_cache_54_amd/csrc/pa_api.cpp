@@ -542,15 +542,15 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     // The matrix-core single-query kernels take one new bf16 row per
     // sequence themselves (a bf16 cache's new rows come in with the last
     // tile's own loads; an e4m3 cache's are read and encoded when that tile
-    // is attended), where the batch has no more (sequence, KV head)
-    // segments than wavefronts: the work at each segment end beats the
-    // append's own launch at up to about one segment end per wavefront
-    // (Llama-shaped batch, 0.5: step 109.9 against 112.6 us, the kernel
-    // unchanged) but not at two (Qwen-shaped: 139.8 against 138.0 us).  Any
-    // other append runs as its own launch first.
+    // is attended), where the batch has at most two (sequence, KV head)
+    // segments per wavefront: there the work at each segment end costs less
+    // than the append's own launch (Llama-shaped batch, 0.5 per wavefront:
+    // step 107.3 against 110.4 us, the kernel unchanged; Qwen-shaped, 2:
+    // 136.3 against 137.3 us, the kernel 2 % slower).  Any other append
+    // runs as its own launch first.
     const bool fuse = app && p.variant == PA_VARIANT_MFMA && qm == 0 &&
                       app_in_type == KT_BF16 && app->num_tokens == p.S &&
-                      p.S * p.Hkv <= p.waves;
+                      p.S * p.Hkv <= 2 * p.waves;
     a.new_k = fuse ? app->k : nullptr;
     a.new_v = fuse ? app->v : nullptr;
     a.new_slots = fuse ? app->slots : nullptr;

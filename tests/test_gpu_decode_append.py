@@ -1,6 +1,6 @@
 """GPU tests of pa_decode_append: the new token's append done inside the
 decode kernel (one new bf16 row per sequence on the matrix-core kernels,
-batches with no more (sequence, KV head) pairs than wavefronts -- every
+batches with at most two (sequence, KV head) pairs per wavefront -- every
 batch here), else launched before it.  Its results must be bit for bit those of
 pa_kv_append followed by pa_decode -- the output and the whole of both
 caches -- on every kernel family (per-wavefront bf16 and e4m3, per-block
@@ -37,6 +37,9 @@ CASES = [
                                               max_len=448), pa.VARIANT_AUTO),
     ("e4m3-wave-Hkv2", "long_fp8", dict(num_seqs=5, num_heads=16, num_kv_heads=2,
                                         lens=("uniform", 1, 333), max_len=352), pa.VARIANT_AUTO),
+    # 1,280 (sequence, KV head) pairs: more than one per wavefront
+    ("bf16-many-segments", "llama3_8b_bf16", dict(num_seqs=160, lens=("uniform", 1, 64),
+                                                   max_len=64), pa.VARIANT_AUTO),
     ("bf16-valu", "llama3_8b_bf16", dict(num_seqs=6, lens=("uniform", 1, 700), max_len=704),
      pa.VARIANT_VALU),
     ("f32", "tiny_f32", {}, pa.VARIANT_AUTO),

@@ -226,15 +226,31 @@ NEGATIVE = {"llama3_8b_bf16", "qwen3_0p6b_bf16"}
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_every_row(name):
     """The workloads at their full sizes, in the launch configuration the
-    benchmark times: every output row against the oracle (one whole-batch
-    call), the whole appended cache bit for bit, and for the bf16 batches a
-    negative control (one wrong block in the oracle's input must fail)."""
+    benchmark times (pa_decode_append: the append inside the decode kernel
+    where the library takes it there): every output row against the oracle
+    (one whole-batch call), the whole appended cache bit for bit, the same
+    output and caches bit for bit as the two calls (pa_kv_append, then
+    pa_decode), and for the bf16 batches a negative control (one wrong block
+    in the oracle's input must fail)."""
     announce(name, "full size: generate")
     b = workloads.make_batch(name, device=DEV)
     kc, vc = gpu_caches(b)
-    announce(name, "full size: step")
-    out = gpu_step(b, kc, vc, partition_tokens=b.partition_tokens or 0)
+    kc2, vc2 = kc.clone(), vc.clone()
+    P = b.partition_tokens or 0
+    announce(name, "full size: step (pa_decode_append)")
+    out = pa.decode_append(b.k_new, b.v_new, b.slot_mapping, b.q, kc, vc, b.block_tables,
+                           b.seq_lens, b.scale, k_scale=b.k_scale, v_scale=b.v_scale,
+                           partition_tokens=P)
+    announce(name, "full size: step as two calls")
+    out2 = gpu_step(b, kc2, vc2, partition_tokens=P)
     torch.cuda.synchronize()
+    bits = torch.int16 if out.element_size() == 2 else torch.int32
+    assert torch.equal(out.view(bits), out2.view(bits)), "fused step differs from the two calls"
+    cbits = torch.int16 if kc.element_size() == 2 else (torch.int32 if kc.element_size() == 4
+                                                         else torch.uint8)
+    assert torch.equal(kc.view(cbits), kc2.view(cbits)) and torch.equal(vc.view(cbits),
+                                                                         vc2.view(cbits))
+    del kc2, vc2, out2
     announce(name, "full size: oracle on all", b.num_seqs * b.num_heads, "rows")
     ref, hk, hv = oracle_step(b)
     check_close(out, ref, b.cache_dtype, f"{name} full")
