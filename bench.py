@@ -580,8 +580,9 @@ def main():
     kernel_bytes = nbytes["decode"] + (nbytes["append"] if in_kernel else 0)
     achieved = kernel_bytes / (kernel_ms * 1e-3) / 1e9
     kname = KERNEL_NAMES[used]
-    if multi and b.group_size * b.max_query_len > 16:
-        kname = "decode_mfma_multi_coop_kernel"     # more than one 16-column tile
+    cols = b.group_size * b.max_query_len if multi else 0
+    if cols > 32 or (cols > 16 and b.cache_dtype != "bf16"):
+        kname = "decode_mfma_multi_coop_kernel"     # two wavefronts per chunk
     traffic = traffic_for(used, args.workload, kname)
     res = {
         "metric": METRIC,

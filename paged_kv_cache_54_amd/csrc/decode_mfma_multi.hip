@@ -18,13 +18,15 @@
 // Causality is one more bound per column: column c sees tokens below
 // lim_c = L - q_len + i + 1, applied by selection like the sequence end.
 //
-// Up to 16 columns one wavefront takes a chunk (decode_mfma_multi_kernel).
-// With more, two wavefronts share it (decode_mfma_multi_coop_kernel): each
-// loads half of every tile (K or V) into a shared LDS tile and computes half
-// of the column tiles, so a wavefront holds half the operands and
-// accumulators and three tiles can be in flight at two wavefronts per SIMD.
-// On the Llama-shaped verify step (32 columns) that took the step from 152.2
-// to 147.4 us against one wavefront holding both column tiles.
+// One wavefront takes a chunk (decode_mfma_multi_kernel) up to 16 columns,
+// and up to 32 with a bf16 cache; with more, two wavefronts share it
+// (decode_mfma_multi_coop_kernel): each loads half of every tile (K or V)
+// into a shared LDS tile and computes half of the column tiles, so a
+// wavefront holds half the operands and accumulators.  At 32 columns (the
+// Llama-shaped verify step) the two-wavefront kernel beat one wavefront
+// holding both column tiles at two wavefronts per SIMD (147.4 against
+// 152.2 us per step); one wavefront per SIMD, the single-query kernel's
+// setting for a bf16 cache, turned that around (155.5 against 156.9 us).
 #include "mfma_common.h"
 
 namespace pa {
@@ -435,14 +437,21 @@ constexpr int coop_depth4()
 }
 
 // Threads of a chunk's workgroup for nt column tiles.
-int threads_for(int nt) { return nt >= 2 ? 64 * kCoopWaves : 64; }
+int threads_for(int kv_type, int nt)
+{
+    return nt >= 4 || (nt == 2 && kv_type != KT_BF16) ? 64 * kCoopWaves : 64;
+}
 
 template <int KT, int D, int BS, bool AB>
 DecodeKernel pick_nt(int nt)
 {
     switch (nt) {
     case 1: return decode_mfma_multi_kernel<KT, D, BS, 1, AB>;
-    case 2: return decode_mfma_multi_coop_kernel<KT, D, BS, 1, 3, AB>;
+    case 2:
+        if constexpr (KT == KT_BF16)
+            return decode_mfma_multi_kernel<KT, D, BS, 2, AB>;
+        else
+            return decode_mfma_multi_coop_kernel<KT, D, BS, 1, 3, AB>;
     case 4: return decode_mfma_multi_coop_kernel<KT, D, BS, 2, coop_depth4<KT, BS>(), AB>;
     default: return nullptr;
     }
@@ -478,7 +487,7 @@ hipError_t launch_decode_mfma_multi(const DecodeArgs &a, int kv_type, int head_d
         pick(kv_type, head_dim, block_size, col_tiles, (a.flags & kPartialsBf16) != 0);
     if (!k)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k, dim3(a.num_waves), dim3(threads_for(col_tiles)), 0, stream, a);
+    hipLaunchKernelGGL(k, dim3(a.num_waves), dim3(threads_for(kv_type, col_tiles)), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -489,7 +498,7 @@ hipError_t decode_mfma_multi_occupancy(int kv_type, int head_dim, int block_size
     if (!k)
         return hipErrorInvalidValue;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        waves_per_cu, reinterpret_cast<const void *>(k), threads_for(col_tiles), 0);
+        waves_per_cu, reinterpret_cast<const void *>(k), threads_for(kv_type, col_tiles), 0);
 }
 
 }  // namespace pa

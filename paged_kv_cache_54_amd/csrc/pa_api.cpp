@@ -303,6 +303,14 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
             // kernel needs every resident wavefront.
             if (p->variant == PA_VARIANT_MFMA && qm == 0 && p->kv_type == KT_BF16)
                 p->waves = (p->waves + 1) / 2;
+            // The same for the one-wavefront multi-token kernel holding two
+            // column tiles (a bf16 cache, 17-32 query rows per KV head): one
+            // wavefront per SIMD, 1 % faster than the two-wavefront kernel on
+            // the Llama-shaped verify step (3 % slower at two per SIMD).
+            // Halving the two-wavefront kernel's workgroups was 27 % slower.
+            if (p->variant == PA_VARIANT_MFMA && qm > 0 && p->col_tiles == 2 &&
+                p->kv_type == KT_BF16)
+                p->waves = (p->waves + 1) / 2;
             if (max_units > 0 && max_units < p->waves)
                 p->waves = max_units;
         }
