@@ -21,6 +21,8 @@ DEV = "cuda:0"
 CASES = [
     # base, heads, kv heads, head_dim, block_size, query lengths
     ("llama3_8b_bf16_spec8", 32, 8, 128, 16, ("fixed", 8)),        # G 4 x 8: 2 column tiles
+    ("llama3_8b_bf16_spec8", 16, 4, 64, 16, ("fixed", 6)),         # G 4 x 6: 2 tiles, D 64
+    ("llama3_8b_bf16_spec8", 32, 8, 128, 32, ("uniform", 5, 7)),   # G 4 x 7: 2 tiles, bs 32
     ("llama3_8b_bf16_spec8", 32, 8, 128, 16, ("uniform", 0, 4)),   # 1 tile, some sequences none
     ("llama3_8b_bf16_spec8", 16, 2, 64, 32, ("fixed", 8)),         # G 8 x 8: 4 tiles, D 64
     ("llama3_8b_bf16_spec8", 4, 4, 128, 32, ("uniform", 1, 16)),   # MHA x 16
