@@ -37,9 +37,9 @@ def _draw(rng, kinds):
 
 
 _RNG = np.random.default_rng(20261202)
-DECODE = [_draw(_RNG, ["f32", "bf16", "fp8"]) for _ in range(16)]
-MULTI = [_draw(_RNG, ["bf16", "fp8"]) for _ in range(8)]
-CASCADE = [_draw(_RNG, ["bf16", "fp8"]) for _ in range(8)]
+DECODE = [_draw(_RNG, ["f32", "bf16", "fp8"]) for _ in range(24)]
+MULTI = [_draw(_RNG, ["bf16", "fp8"]) for _ in range(12)]
+CASCADE = [_draw(_RNG, ["bf16", "fp8"]) for _ in range(12)]
 
 
 def _ids(cases):
