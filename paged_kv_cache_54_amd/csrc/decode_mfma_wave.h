@@ -103,8 +103,11 @@ struct WaveAttn {
 #pragma unroll
         for (int k = 0; k < NC; ++k)
             qop[k] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * k));
+        // The slot through the scalar cache (the kernel never writes it): a
+        // vector load would have to be moved to a scalar register at once,
+        // and that wait would drain the tile loads in flight.
         if (APP && KT == KT_BF16 && a.new_k)
-            nslot = a.new_slots[c.s];
+            nslot = *(const __attribute__((address_space(4))) int64_t *)(a.new_slots + c.s);
     }
 
     // Empty accumulators and softmax state for a run of tiles starting at c.
