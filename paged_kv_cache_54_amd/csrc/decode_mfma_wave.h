@@ -442,7 +442,14 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
     // next_load moves the load cursor to tile `k`; past the chunk's last tile
     // it yields no block (id -1), whose loads read nothing.
     int l_half = 0;
-    int l_id = ids.get(lc.s, lc.j);
+    // The cascade's suffix view (short segments, many sequence changes per
+    // chunk) reads the walk's next table window ahead; plain decode reads a
+    // window when the walk enters it (the read-ahead measured 0.3 % slower on
+    // the Qwen-shaped batch and equal on the Llama-shaped one).
+    auto block_id = [&](const Cursor &c) {
+        return v.deep ? ids.walk(c, Hkv, a.num_seqs) : ids.get(c.s, c.j);
+    };
+    int l_id = block_id(lc);
     auto next_load = [&](int k) {
         if (k >= steps) {
             l_id = -1;
@@ -451,7 +458,7 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
         if (++l_half == HALVES) {
             l_half = 0;
             advance<BS>(lc, lens, Hkv, cap);
-            l_id = ids.get(lc.s, lc.j);
+            l_id = block_id(lc);
         }
     };
 

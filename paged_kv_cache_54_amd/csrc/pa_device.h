@@ -279,6 +279,13 @@ struct Lens {
     const int32_t *p;
     int off;
     __device__ __forceinline__ int operator[](int s) const { return p[s] - off; }
+    // A wave-uniform index, read through the scalar cache: its wait does not
+    // drain the vector loads in flight (the lengths are never written by a
+    // kernel that reads them).
+    __device__ __forceinline__ int uniform(int s) const
+    {
+        return *(const __attribute__((address_space(4))) int32_t *)(p + s) - off;
+    }
 };
 
 template <int BS>
@@ -351,7 +358,7 @@ __device__ __forceinline__ void advance(Cursor &c, Lens lens, int Hkv, int cap)
     c.kvh = 0;
     do {
         ++c.s;
-        c.L = __builtin_amdgcn_readfirstlane(min(lens[c.s], cap));
+        c.L = min(lens.uniform(c.s), cap);
         c.nb = seq_blocks<BS>(c.L, cap);
     } while (c.nb == 0);
 }
@@ -368,6 +375,7 @@ struct BlockIds {
     int stride, max_nb, num_blocks;
     uint32_t *err;
     int s = -1, base = 0, ids = 0;
+    int ns = -1, nbase = 0, next = 0;
 
     __device__ __forceinline__ BlockIds(const int32_t *tables_, int stride_, int max_nb_,
                                         int nblocks, uint32_t *err_)
@@ -382,6 +390,43 @@ struct BlockIds {
             base = j & ~63;
             const int jj = base + lane_id();
             ids = settled(jj < max_nb ? tables[(int64_t)s_ * stride + jj] : 0);
+        }
+        const int id = __builtin_amdgcn_readlane(ids, j - base);
+        const bool bad = id < 0 || id >= num_blocks;
+        if (bad)
+            raise_flag(err, PA_DEVERR_BLOCK_ID);
+        return __builtin_amdgcn_readfirstlane(bad ? -1 : id);
+    }
+
+    // get() for a walk in work-list order that also reads the walk's next
+    // window ahead: the next 64 entries of the row while the sequence has
+    // blocks there, else row s's first window when the next KV head needs it
+    // back, else the next sequence's first window (a guess: an empty
+    // sequence in between reads its window when entered).  Rows at or past
+    // S are never read.
+    __device__ __forceinline__ int walk(const Cursor &c, int Hkv, int S)
+    {
+        const int j = c.j;
+        if (c.s != s || j < base || j >= base + 64) {
+            const int b = j & ~63;
+            const bool hit = c.s == ns && b == nbase;
+            const int jj = b + lane_id();
+            const int row = hit ? ns : c.s;
+            ids = settled(hit ? next : (jj < max_nb ? tables[(int64_t)row * stride + jj] : 0));
+            s = c.s;
+            base = b;
+            if (base + 64 < c.nb) {
+                ns = s;
+                nbase = base + 64;
+            } else if (c.kvh + 1 < Hkv && base != 0) {
+                ns = s;
+                nbase = 0;
+            } else {
+                ns = s + 1;
+                nbase = 0;
+            }
+            const int nj = nbase + lane_id();
+            next = ns < S && nj < max_nb ? tables[(int64_t)ns * stride + nj] : 0;
         }
         const int id = __builtin_amdgcn_readlane(ids, j - base);
         const bool bad = id < 0 || id >= num_blocks;
