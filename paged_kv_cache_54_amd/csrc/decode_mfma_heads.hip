@@ -9,9 +9,9 @@ using heads_kernel::HeadsKernel;
 
 namespace {
 
-HeadsKernel pick(int kv_type, int d, int bs, int group, int hk, bool acc_bf16, bool stream)
+HeadsKernel pick(int kv_type, int d, int bs, int group, int hk, bool acc_bf16)
 {
-    return heads_kernel::pick<false>(kv_type, d, bs, group, hk, acc_bf16, stream);
+    return heads_kernel::pick<false>(kv_type, d, bs, group, hk, acc_bf16);
 }
 
 }  // namespace
@@ -19,18 +19,18 @@ HeadsKernel pick(int kv_type, int d, int bs, int group, int hk, bool acc_bf16, b
 bool decode_mfma_heads_supported(int kv_type, int head_dim, int block_size, int group,
                                  int num_kv_heads)
 {
-    return pick(kv_type, head_dim, block_size, group, num_kv_heads, false, false) != nullptr;
+    return pick(kv_type, head_dim, block_size, group, num_kv_heads, false) != nullptr;
 }
 
 hipError_t launch_decode_mfma_heads(const DecodeArgs &a, int kv_type, int head_dim,
                                     int block_size, int group, int workgroups,
                                     hipStream_t stream)
 {
-    const bool ab = (a.flags & kPartialsBf16) != 0, st = (a.flags & kStreamPartials) != 0;
+    const bool ab = (a.flags & kPartialsBf16) != 0;
     const HeadsKernel k =
         a.new_k ? decode_mfma_heads_append_kernel(kv_type, head_dim, block_size, group,
-                                                  a.num_kv_heads, ab, st)
-                : pick(kv_type, head_dim, block_size, group, a.num_kv_heads, ab, st);
+                                                  a.num_kv_heads, ab)
+                : pick(kv_type, head_dim, block_size, group, a.num_kv_heads, ab);
     if (!k || workgroups <= 0)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(k, dim3((unsigned)workgroups), dim3(64 * a.num_kv_heads), 0, stream, a);
@@ -40,7 +40,7 @@ hipError_t launch_decode_mfma_heads(const DecodeArgs &a, int kv_type, int head_d
 hipError_t decode_mfma_heads_occupancy(int kv_type, int head_dim, int block_size, int group,
                                        int num_kv_heads, bool acc_bf16, int *groups_per_cu)
 {
-    const HeadsKernel k = pick(kv_type, head_dim, block_size, group, num_kv_heads, acc_bf16, false);
+    const HeadsKernel k = pick(kv_type, head_dim, block_size, group, num_kv_heads, acc_bf16);
     if (!k)
         return hipErrorInvalidValue;
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(

@@ -6,9 +6,9 @@
 namespace pa {
 
 heads_kernel::HeadsKernel decode_mfma_heads_append_kernel(int kv_type, int d, int bs, int group,
-                                                          int hk, bool acc_bf16, bool stream)
+                                                          int hk, bool acc_bf16)
 {
-    return heads_kernel::pick<true>(kv_type, d, bs, group, hk, acc_bf16, stream);
+    return heads_kernel::pick<true>(kv_type, d, bs, group, hk, acc_bf16);
 }
 
 }  // namespace pa

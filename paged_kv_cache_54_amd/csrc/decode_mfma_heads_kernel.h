@@ -28,12 +28,14 @@
 // ones, one per resident workgroup, or fixed ones of chunk_units blocks --
 // and each workgroup walks one contiguous run of them (with fixed partitions,
 // an equal run per workgroup of a grid no larger than the device holds at
-// once: the same read pattern as the balanced split, with a partial written
-// at every partition boundary).  Head w writes the partial of segment (s, w)
-// in partition q to slot (q + s) * HK + w: distinct over all (q, s, w), as
-// partitions hold non-decreasing sequences, and the slots of one segment step
-// by HK from the first partition touching it to the last (the merge's slot
-// stride).
+// once: the same read pattern as the balanced split).  A wavefront carries its
+// softmax state across the partition boundaries inside its run, so a segment
+// leaves one partial per run that touches it, not one per partition: the
+// log-sum-exp merge is associative, and a run that holds a whole segment
+// writes the output itself.  Head w of run c writes the partial of segment
+// (s, w) to slot (c + s) * HK + w: distinct over all (c, s, w), as runs hold
+// non-decreasing sequences, and the slots of one segment step by HK from the
+// first run touching it to the last (the merge's slot stride).
 //
 // decode_mfma_heads.hip instantiates the plain kernels and launches them;
 // decode_mfma_heads_append.hip the ones that also do the step's append
@@ -64,9 +66,8 @@ struct HeadsGeo {
     static constexpr int LDS = HK * (KTB + VTB);
 };
 
-// ST: partial accumulators written with nontemporal stores.  APP: the
-// step's append compiled in.
-template <int KT, int D, int BS, int G, bool AB, int HK, bool ST, bool APP>
+// APP: the step's append compiled in.
+template <int KT, int D, int BS, int G, bool AB, int HK, bool APP>
 __global__ __launch_bounds__(64 * HK) void decode_mfma_heads_kernel(DecodeArgs a)
 {
     using HG = HeadsGeo<KT, D, BS, HK>;
@@ -90,9 +91,6 @@ __global__ __launch_bounds__(64 * HK) void decode_mfma_heads_kernel(DecodeArgs a
     // them), else the chunk itself.  q is the global index of the current
     // one; a chunk starts on a partition boundary.
     const int n = chunk.n;
-    const int pl = a.chunk_units > 0 ? a.chunk_units : n;
-    int q = a.chunk_units > 0 ? (int)(chunk.u0 / pl) : c;
-    int left = pl;                                        // units left in partition q
 
     // This lane's 16 bytes of piece i * HK + kvh: token slot row_i, head hd,
     // bytes 16 * ch .. of that head's row.
@@ -154,7 +152,7 @@ __global__ __launch_bounds__(64 * HK) void decode_mfma_heads_kernel(DecodeArgs a
         // sequence keeps them.
         if (k == 0 || cc.j == 0)
             att.load_q(a, hc);
-        if (left == pl || cc.j == 0)
+        if (k == 0 || cc.j == 0)
             att.reset(hc);
         const int tok_base = cc.j * BS;
         __syncthreads();                                  // previous tiles fully read
@@ -173,14 +171,9 @@ __global__ __launch_bounds__(64 * HK) void decode_mfma_heads_kernel(DecodeArgs a
         if (id >= 0)
             att.attend(a, kt, vt, tok_base, cc.L);
         const bool ends = cc.j == cc.nb - 1;
-        --left;
-        if (ends || left == 0 || k == n - 1) {
+        if (ends || k == n - 1) {
             att.append_store(a, hc, id);
-            att.template finish<ST>(a, hc, (q + cc.s) * HK + kvh, ends);
-        }
-        if (left == 0) {
-            left = pl;
-            ++q;
+            att.finish(a, hc, (c + cc.s) * HK + kvh, ends);
         }
         if (k + 1 < n)
             advance<BS>(cc, lens, 1, cap);
@@ -190,44 +183,41 @@ __global__ __launch_bounds__(64 * HK) void decode_mfma_heads_kernel(DecodeArgs a
 
 typedef void (*HeadsKernel)(DecodeArgs);
 
-template <int D, int BS, bool AB, int HK, bool ST, bool APP>
+template <int D, int BS, bool AB, int HK, bool APP>
 HeadsKernel pick_g(int group)
 {
     switch (group) {
-    case 1: return decode_mfma_heads_kernel<KT_E4M3, D, BS, 1, AB, HK, ST, APP>;
-    case 2: return decode_mfma_heads_kernel<KT_E4M3, D, BS, 2, AB, HK, ST, APP>;
-    case 4: return decode_mfma_heads_kernel<KT_E4M3, D, BS, 4, AB, HK, ST, APP>;
-    case 8: return decode_mfma_heads_kernel<KT_E4M3, D, BS, 8, AB, HK, ST, APP>;
+    case 1: return decode_mfma_heads_kernel<KT_E4M3, D, BS, 1, AB, HK, APP>;
+    case 2: return decode_mfma_heads_kernel<KT_E4M3, D, BS, 2, AB, HK, APP>;
+    case 4: return decode_mfma_heads_kernel<KT_E4M3, D, BS, 4, AB, HK, APP>;
+    case 8: return decode_mfma_heads_kernel<KT_E4M3, D, BS, 8, AB, HK, APP>;
     default: return nullptr;
     }
 }
 
-template <bool AB, int HK, bool ST, bool APP>
+template <bool AB, int HK, bool APP>
 HeadsKernel pick_bs(int bs, int group)
 {
-    if (bs == 16) return pick_g<128, 16, AB, HK, ST, APP>(group);
-    if (bs == 32) return pick_g<128, 32, AB, HK, ST, APP>(group);
+    if (bs == 16) return pick_g<128, 16, AB, HK, APP>(group);
+    if (bs == 32) return pick_g<128, 32, AB, HK, APP>(group);
     return nullptr;
 }
 
-template <int HK, bool ST, bool APP>
+template <int HK, bool APP>
 HeadsKernel pick_ab(int bs, int group, bool acc_bf16)
 {
-    return acc_bf16 ? pick_bs<true, HK, ST, APP>(bs, group)
-                    : pick_bs<false, HK, ST, APP>(bs, group);
+    return acc_bf16 ? pick_bs<true, HK, APP>(bs, group) : pick_bs<false, HK, APP>(bs, group);
 }
 
 template <bool APP>
-HeadsKernel pick(int kv_type, int d, int bs, int group, int hk, bool acc_bf16, bool stream)
+HeadsKernel pick(int kv_type, int d, int bs, int group, int hk, bool acc_bf16)
 {
     if (kv_type != KT_E4M3 || d != 128)
         return nullptr;
     if (hk == 4)
-        return stream ? pick_ab<4, true, APP>(bs, group, acc_bf16)
-                      : pick_ab<4, false, APP>(bs, group, acc_bf16);
+        return pick_ab<4, APP>(bs, group, acc_bf16);
     if (hk == 8)
-        return stream ? pick_ab<8, true, APP>(bs, group, acc_bf16)
-                      : pick_ab<8, false, APP>(bs, group, acc_bf16);
+        return pick_ab<8, APP>(bs, group, acc_bf16);
     return nullptr;
 }
 
@@ -235,6 +225,6 @@ HeadsKernel pick(int kv_type, int d, int bs, int group, int hk, bool acc_bf16, b
 
 // The append-carrying instance (decode_mfma_heads_append.hip).
 heads_kernel::HeadsKernel decode_mfma_heads_append_kernel(int kv_type, int d, int bs, int group,
-                                                          int hk, bool acc_bf16, bool stream);
+                                                          int hk, bool acc_bf16);
 
 }  // namespace pa

@@ -237,9 +237,7 @@ struct WaveAttn {
 
     // The segment's result in partial slot `slot` (segment record too): the
     // output rows when this run of tiles covered the whole segment, else the
-    // partial (m, l, acc).  ST: partial accumulators written with
-    // nontemporal stores (G <= 8).
-    template <bool ST = false>
+    // partial (m, l, acc).
     __device__ __forceinline__ void finish(const DecodeArgs &a, const Cursor &c, int slot,
                                            bool ends)
     {
@@ -249,7 +247,7 @@ struct WaveAttn {
         const bool whole = seg_starts && ends && !(a.flags & kPartialOnly);
         if constexpr (kPairedPartials && G <= 8) {
             if (!whole) {
-                store_partial_pairs<ND, AB, G, ST>(a.ws_acc, (int64_t)slot * G, g4, c16, acc,
+                store_partial_pairs<ND, AB, G>(a.ws_acc, (int64_t)slot * G, g4, c16, acc,
                                                    a.v_scale);
                 if (g4 == 0 && c16 < G)
                     *reinterpret_cast<float2 *>(a.ws_ml + ((int64_t)slot * G + c16) * 2) =

@@ -91,13 +91,7 @@ __device__ __forceinline__ void store_partial(void *ws_acc, int64_t row, int g4,
 // 2p + 1 -- and every store covers whole 128-byte lines of a row (f32)
 // instead of their halves, in half as many instructions.  Rows r >= G store
 // nothing.
-//
-// ST: nontemporal stores, which leave the lines out of L2 (for calls whose
-// partials outgrow the L2s: their dirty lines, written back in among the KV
-// reads, cost more than the bytes).  A template parameter: a run-time choice
-// between two stores of the same value to the same address is merged by the
-// compiler into one cached store.
-template <int ND, bool BF16, int G, bool ST>
+template <int ND, bool BF16, int G>
 __device__ __forceinline__ void store_partial_pairs(void *ws_acc, int64_t slot_row0, int g4,
                                                     int c16, f32x4 (&acc)[ND], float scale)
 {
@@ -115,17 +109,9 @@ __device__ __forceinline__ void store_partial_pairs(void *ws_acc, int64_t slot_r
         const f32x4 v = hi ? acc[2 * p + 1] : acc[2 * p];
         if constexpr (BF16) {
             u32x2 *o = reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(ws_acc) + base + 32 * p);
-            const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-            if constexpr (ST)
-                __builtin_nontemporal_store(w, o);
-            else
-                *o = w;
+            *o = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         } else {
-            f32x4 *o = reinterpret_cast<f32x4 *>(static_cast<float *>(ws_acc) + base + 32 * p);
-            if constexpr (ST)
-                __builtin_nontemporal_store(v, o);
-            else
-                *o = v;
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(ws_acc) + base + 32 * p) = v;
         }
     }
 }

@@ -109,15 +109,6 @@ struct DecodePlan {
     size_t ws_bytes;
 };
 
-// Partial accumulator bytes above which the per-block e4m3 kernel writes
-// them with nontemporal stores: the combined L2 of the device (8 x 4 MB).
-// Above it dirty partial lines written back in among the KV reads cost more
-// than their bytes (131072-token e4m3 batch in 512-token partitions, 64 MB:
-// 423 us cached, 374 us streamed, 350 us with no accumulator stores at all);
-// below it the merge rereads them from L2 (Llama-shaped bf16 batch, 3 MB of
-// partials: 104.9 us kernel / 112.2 us step cached, 105.7 / 114.6 streamed).
-// The bf16 kernels keep cached stores (their workloads' partials are small).
-constexpr size_t kStreamPartialBytes = size_t(32) << 20;
 
 // Workspace layout: acc [slots, rows, D] | ml [slots, rows, 2] f32 | seg [S*Hkv, 2] i32
 // Partial accumulators are f32; PA_PARTIALS_BF16 stores them as bf16 for a
@@ -543,8 +534,7 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     a.log2_group = __builtin_ctz((unsigned)p.G);
     a.qk_scale_log2 = scale * kLog2e * ks;
     a.v_scale = vs;
-    a.flags = (p.acc_bf16 ? kPartialsBf16 : 0) |
-              (p.heads > 0 && acc_bytes(p) > kStreamPartialBytes ? kStreamPartials : 0);
+    a.flags = p.acc_bf16 ? kPartialsBf16 : 0;
     a.slot_stride = p.heads > 0 ? (int32_t)p.heads : 1;
     a.num_slots = (int32_t)p.slots;
     // The matrix-core single-query kernels take one new bf16 row per
@@ -566,7 +556,8 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     a.v_inv_scale = app ? app->v_inv_scale : 1.0f;
 
     // Fixed partitions on the per-block e4m3 kernel: no more workgroups than
-    // the device holds at once, each walking an equal run of partitions.
+    // the device holds at once, each walking an equal run of partitions (the
+    // workspace has a slot per partition, sized without the device).
     int64_t groups = p.groups;
     if (p.heads > 0 && p.chunk_units > 0) {
         int cus = 0, per_cu = 0;

@@ -57,11 +57,8 @@ struct DecodeArgs {
 // as a partial (acc, m, l), also one a single chunk covers, so that a second
 // pass can combine it with another source.  kPartialsBf16: partial
 // accumulators are stored as bf16 (bf16 outputs only); otherwise f32.
-// kStreamPartials (the per-block e4m3 kernel, G <= 8): partial
-// accumulators are written with nontemporal stores.
 constexpr int32_t kPartialOnly = 1;
 constexpr int32_t kPartialsBf16 = 2;
-constexpr int32_t kStreamPartials = 4;
 
 struct AppendArgs {
     const void *k;               // [T, Hkv, D]

@@ -120,9 +120,10 @@ def test_heads_broken_device_data_is_flagged_not_followed():
 @pytest.mark.parametrize("bs", [32, 16])
 def test_heads_runs_of_partitions(bs):
     """Fixed partitions outnumbering the workgroups the device holds at once:
-    each workgroup walks a run of several, writing a partial at every
-    partition boundary (one-block partitions: hundreds of partials per
-    sequence)."""
+    each workgroup walks a run of several and carries its softmax state
+    across their boundaries, leaving one partial per segment it touches
+    (one-block partitions: runs ending inside a block's worth of a
+    sequence's start or end)."""
     b = workloads.make_batch("long_fp8", device=DEV, num_seqs=6, num_heads=64, num_kv_heads=8,
                              block_size=bs, lens=("uniform", 1500, 2600), max_len=2624,
                              poison=True, seed=61 + bs)
