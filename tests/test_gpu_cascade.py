@@ -2,7 +2,8 @@
 sequences, then each sequence's own blocks, joined by log-sum-exp) against
 the oracle, and against pa_decode on the same caches: bf16 and e4m3 caches,
 group sizes 1 to 8, head_dim 64 and 128, block sizes 16 and 32, sequences
-ending exactly at the prefix, batches whose query rows do not fill the last
+ending exactly at the prefix, sequences whose own blocks span several
+block-table windows, batches whose query rows do not fill the last
 row block of the prefix pass, prefixes split over several token ranges, work
 splits, NaN in unread slots,
 the full-size shared-prefix batch on every row, and a broken contract
@@ -24,6 +25,8 @@ CASES = [
     (16, 2, 64, 32, 64, (0, 70), 9),       # G 8, D 64; some sequences end at the prefix
     (8, 8, 128, 16, 48, (1, 40), 40),      # MHA: 16 per group
     (16, 8, 128, 32, 96, (1, 200), 5),     # G 2
+    # own blocks past one 64-entry table window (up to 138), some none
+    (32, 8, 128, 16, 128, (0, 2200), 10),
 ]
 
 
@@ -45,7 +48,9 @@ def test_cascade_parity(H, Hkv, D, bs, prefix, suffix, S, fp8):
     pa.kv_append(b.k_new, b.v_new, b.slot_mapping, kc, vc, b.k_scale, b.v_scale)
     plain = pa.decode(b.q, kc, vc, b.block_tables, b.seq_lens, b.scale, k_scale=b.k_scale,
                       v_scale=b.v_scale)
-    for P in (0, bs):
+    # balanced, one-block and 40-block chunks (the last cross table windows
+    # and KV heads inside a chunk)
+    for P in (0, bs, 40 * bs):
         print("CASE cascade", H, Hkv, D, bs, prefix, suffix, S, "fp8" if fp8 else "bf16", "P", P,
               flush=True)
         flag = torch.zeros(1, dtype=torch.int32, device=DEV)
