@@ -133,9 +133,11 @@ typedef struct pa_opts {
        0 (default): as many equal chunks as the device holds at once, so
        every compute unit streams the same number of blocks.  Otherwise:
        partitions of partition_tokens / block_size units (a multiple of
-       block_size), each finished as its own partial -- except on the
-       per-block e4m3 kernel, where each workgroup walks an equal run of
-       partitions and leaves one partial per segment it touches. */
+       block_size); a grid of at most as many chunks as the device holds at
+       once walks them in equal runs of whole partitions, and a run carries
+       its softmax state across their boundaries (one partial per segment it
+       touches, not per partition).  The workspace is sized for one chunk
+       per partition of the largest batch the tables allow. */
     int32_t partition_tokens;
     int32_t variant;            /* PA_VARIANT_* */
     void *workspace;            /* device buffer, pa_decode_workspace_size bytes,

@@ -87,9 +87,6 @@ __global__ __launch_bounds__(64 * HK) void decode_mfma_heads_kernel(DecodeArgs a
     const Chunk chunk = my_chunk<BS>(u, lens, c, (int)gridDim.x, true);
     if (chunk.n == 0)
         return;                                           // uniform over the workgroup
-    // Partitions: fixed ones of chunk_units units (a chunk holds a run of
-    // them), else the chunk itself.  q is the global index of the current
-    // one; a chunk starts on a partition boundary.
     const int n = chunk.n;
 
     // This lane's 16 bytes of piece i * HK + kvh: token slot row_i, head hd,

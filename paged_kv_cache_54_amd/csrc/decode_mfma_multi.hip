@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64) void decode_mfma_multi_kernel(DecodeArgs a)
     const int w = blockIdx.x;
 
     const Lens lens{a.seq_lens, 0};
-    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
+    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves, (a.flags & kRuns) != 0);
     if (chunk.n == 0)
         return;
 
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(64 * kCoopWaves) void decode_mfma_multi_coop_kernel
     const int w = blockIdx.x;
 
     const Lens lens{a.seq_lens, 0};
-    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
+    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves, (a.flags & kRuns) != 0);
     if (chunk.n == 0)
         return;
 

@@ -382,24 +382,27 @@ __device__ __forceinline__ void decode_mfma_wave(const DecodeArgs &a, TableView 
 {
     using Geo = MfmaGeo<KT, D, BS>;
     constexpr int TILE = Geo::TILE, HALVES = Geo::HALVES;
-    // Register tiles in flight while a tile is computed: two with fixed-size
-    // chunks (short chunks, many rounds of wavefronts: the second tile
-    // shortens each chunk's start) and for a deep view (the cascade's suffix
-    // pass: a small batch, where start-up dominates); one with balanced
-    // chunks.  One tile per wavefront puts about 16 MB in flight at two
-    // wavefronts per SIMD, and that streams fastest: two measured 6 % slower
-    // on the Llama-shaped batch and 2 % on the Qwen-shaped one (3 % faster on
-    // the shared-prefix suffix pass).
-    const bool pingpong = v.deep || a.chunk_units > 0;
 
     const int lane = threadIdx.x & 63;
     const int Hkv = a.num_kv_heads;
     const int cap = a.max_nb * BS;
 
+    const bool runs = (a.flags & kRuns) != 0;
     const Lens lens{a.seq_lens, v.len_offset};
-    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
+    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves, runs);
     if (chunk.n == 0)
         return;
+
+    // Register tiles in flight while a tile is computed: two for a chunk of
+    // one fixed partition (short chunks, many rounds of wavefronts or a small
+    // batch: the second tile shortens each chunk's start) and for a deep view
+    // (the cascade's suffix pass: a small batch, where start-up dominates);
+    // one for balanced chunks and longer runs of partitions.  One tile per
+    // wavefront puts about 8 MB in flight at one wavefront per SIMD, and that
+    // streams fastest: two measured 6 % slower on the Llama-shaped batch and
+    // 2 % on the Qwen-shaped one (3 % faster on the shared-prefix suffix
+    // pass).
+    const bool pingpong = v.deep || (a.chunk_units > 0 && chunk.n <= a.chunk_units);
 
     const MfmaLoader<Geo> loader(a, lane);
     using Tile = MfmaTile<Geo>;

@@ -42,7 +42,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a)
     const int w = blockIdx.x;
 
     const Lens lens{a.seq_lens, 0};
-    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves);
+    const Chunk chunk = my_chunk<BS>(a, lens, w, a.num_waves, (a.flags & kRuns) != 0);
     if (chunk.n == 0)
         return;
 

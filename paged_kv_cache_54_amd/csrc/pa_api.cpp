@@ -163,6 +163,35 @@ int resident_waves_per_cu(const DecodePlan &p, int *waves, bool cascade = false)
     return PA_OK;
 }
 
+// Chunks of the balanced split of a per-wavefront or multi-token plan: one
+// per wavefront (workgroup, for the two-wavefront multi-token kernel) the
+// device holds at once, halved where one wavefront per SIMD streams faster.
+int balanced_chunks(const DecodePlan &p, int64_t qm, int64_t *chunks)
+{
+    int cus = 0, per_cu = 0, rc;
+    if ((rc = device_cu_count(&cus)) || (rc = resident_waves_per_cu(p, &per_cu)))
+        return rc;
+    int64_t n = (int64_t)cus * per_cu;
+    // Single-query decode of a bf16 cache on the matrix cores: half as many
+    // wavefronts, each with a chunk twice as long.  One register tile in
+    // flight per wavefront (about 8 MB over the device) still keeps enough
+    // bytes moving, and a chunk's pipeline start and partial writes come
+    // half as often (1-4 % faster over bf16 batches of 8-256 sequences; a
+    // quarter of the wavefronts with two tiles each was 30 % slower).  An
+    // e4m3 cache's per-wavefront kernel needs every resident wavefront.
+    if (p.variant == PA_VARIANT_MFMA && qm == 0 && p.kv_type == KT_BF16)
+        n = (n + 1) / 2;
+    // The same for the one-wavefront multi-token kernel holding two column
+    // tiles (a bf16 cache, 17-32 query rows per KV head): one wavefront per
+    // SIMD, 1 % faster than the two-wavefront kernel on the Llama-shaped
+    // verify step (3 % slower at two per SIMD).  Halving the two-wavefront
+    // kernel's workgroups was 27 % slower.
+    if (p.variant == PA_VARIANT_MFMA && qm > 0 && p.col_tiles == 2 && p.kv_type == KT_BF16)
+        n = (n + 1) / 2;
+    *chunks = n;
+    return PA_OK;
+}
+
 // Shapes, dtypes and options common to the decode entry points and their
 // workspace queries.  qm = 0: one query token per sequence (q [S, H, D]);
 // qm > 0: several per sequence, at most qm (q [T, H, D], S from the tables).
@@ -274,34 +303,15 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
         p->waves = max_units > 0 ? (max_units + p->chunk_units - 1) / p->chunk_units : 1;
     } else {
         // balanced: one chunk per wavefront the device holds at once (half
-        // that for bf16 caches, below), but no more wavefronts than the
-        // largest batch of these shapes has units (a small batch then
-        // launches only the wavefronts it can use)
+        // that for bf16 caches), but no more wavefronts than the largest
+        // batch of these shapes has units (a small batch then launches only
+        // the wavefronts it can use)
         p->chunk_units = 0;
         p->waves = 1;
         if (p->S > 0) {
-            int cus = 0, per_cu = 0, rc;
-            if ((rc = device_cu_count(&cus)) || (rc = resident_waves_per_cu(*p, &per_cu)))
+            int rc;
+            if ((rc = balanced_chunks(*p, qm, &p->waves)))
                 return rc;
-            p->waves = (int64_t)cus * per_cu;
-            // Single-query decode of a bf16 cache on the matrix cores: half as
-            // many wavefronts, each with a chunk twice as long.  One register
-            // tile in flight per wavefront (about 8 MB over the device) still
-            // keeps enough bytes moving, and a chunk's pipeline start and
-            // partial writes come half as often (1-4 % faster over bf16
-            // batches of 8-256 sequences; a quarter of the wavefronts with
-            // two tiles each was 30 % slower).  An e4m3 cache's per-wavefront
-            // kernel needs every resident wavefront.
-            if (p->variant == PA_VARIANT_MFMA && qm == 0 && p->kv_type == KT_BF16)
-                p->waves = (p->waves + 1) / 2;
-            // The same for the one-wavefront multi-token kernel holding two
-            // column tiles (a bf16 cache, 17-32 query rows per KV head): one
-            // wavefront per SIMD, 1 % faster than the two-wavefront kernel on
-            // the Llama-shaped verify step (3 % slower at two per SIMD).
-            // Halving the two-wavefront kernel's workgroups was 27 % slower.
-            if (p->variant == PA_VARIANT_MFMA && qm > 0 && p->col_tiles == 2 &&
-                p->kv_type == KT_BF16)
-                p->waves = (p->waves + 1) / 2;
             if (max_units > 0 && max_units < p->waves)
                 p->waves = max_units;
         }
@@ -537,6 +547,20 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     a.flags = p.acc_bf16 ? kPartialsBf16 : 0;
     a.slot_stride = p.heads > 0 ? (int32_t)p.heads : 1;
     a.num_slots = (int32_t)p.slots;
+    // Fixed partitions on the per-wavefront kernels: the balanced split's
+    // grid, each chunk an equal run of whole partitions whose softmax state
+    // runs on across their boundaries (one partial per run and segment, not
+    // per partition: the Llama-shaped batch in 512-token partitions 117 ->
+    // 103 us).  The workspace keeps a slot per partition of the largest
+    // batch, so its size needs no device query.
+    if (p.heads == 0 && p.chunk_units > 0) {
+        int64_t runs = 0;
+        if ((rc = balanced_chunks(p, qm, &runs)))
+            return rc;
+        if (runs > 0 && runs < p.waves)
+            a.num_waves = (int32_t)runs;
+        a.flags |= kRuns;
+    }
     // The matrix-core single-query kernels take one new bf16 row per
     // sequence themselves (a bf16 cache's new rows come in with the last
     // tile's own loads; an e4m3 cache's are read and encoded when that tile
@@ -548,7 +572,7 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     // runs as its own launch first.
     const bool fuse = app && p.variant == PA_VARIANT_MFMA && qm == 0 &&
                       app_in_type == KT_BF16 && app->num_tokens == p.S &&
-                      p.S * p.Hkv <= 2 * p.waves;
+                      p.S * p.Hkv <= 2 * (int64_t)a.num_waves;
     a.new_k = fuse ? app->k : nullptr;
     a.new_v = fuse ? app->v : nullptr;
     a.new_slots = fuse ? app->slots : nullptr;

@@ -57,8 +57,12 @@ struct DecodeArgs {
 // as a partial (acc, m, l), also one a single chunk covers, so that a second
 // pass can combine it with another source.  kPartialsBf16: partial
 // accumulators are stored as bf16 (bf16 outputs only); otherwise f32.
+// kRuns (per-wavefront kernels, chunk_units > 0): chunk_units names
+// partitions, and each of the num_waves chunks is an equal run of whole
+// partitions.
 constexpr int32_t kPartialOnly = 1;
 constexpr int32_t kPartialsBf16 = 2;
+constexpr int32_t kRuns = 4;
 
 struct AppendArgs {
     const void *k;               // [T, Hkv, D]
