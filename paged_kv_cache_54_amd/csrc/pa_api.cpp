@@ -298,7 +298,8 @@ int plan_decode(const pa_tensor *q, const pa_tensor *kc, const pa_tensor *bt,
         p->groups = groups;
         p->waves = groups * p->heads;
     } else if (P > 0) {
-        // fixed chunks: enough wavefronts for the largest possible batch
+        // fixed partitions: a chunk (and partial slot) for each partition of
+        // the largest possible batch; the launch walks them in runs
         p->chunk_units = P / p->bs;
         p->waves = max_units > 0 ? (max_units + p->chunk_units - 1) / p->chunk_units : 1;
     } else {
@@ -550,9 +551,11 @@ int run_decode(const pa_tensor *q, const pa_tensor *qsl, int64_t qm, const pa_te
     // Fixed partitions on the per-wavefront kernels: the balanced split's
     // grid, each chunk an equal run of whole partitions whose softmax state
     // runs on across their boundaries (one partial per run and segment, not
-    // per partition: the Llama-shaped batch in 512-token partitions 117 ->
-    // 103 us).  The workspace keeps a slot per partition of the largest
-    // batch, so its size needs no device query.
+    // per partition: the Qwen-shaped batch in 512-token partitions 137 -> 131
+    // us, the balanced split's time; the Llama-shaped one 117 -> 115 us, its
+    // 2.35 partitions per wavefront rounding up to runs of 3).  The
+    // workspace keeps a slot per partition of the largest batch, so its size
+    // needs no device query.
     if (p.heads == 0 && p.chunk_units > 0) {
         int64_t runs = 0;
         if ((rc = balanced_chunks(p, qm, &runs)))
