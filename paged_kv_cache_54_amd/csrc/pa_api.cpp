@@ -18,12 +18,21 @@ using namespace pa;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Dense row-major: each stride the product of the sizes after it.  The
+// stride of a dimension of size 1 addresses nothing, and a tensor with no
+// elements has nothing to address (frameworks give both arbitrary strides).
 bool is_dense(const pa_tensor *t)
 {
-    int64_t expect = 1;
-    for (int i = t->ndim - 1; i >= 0; --i) {
+    bool empty = false;
+    for (int i = 0; i < t->ndim; ++i) {
         if (t->shape[i] < 0)
             return false;
+        empty |= t->shape[i] == 0;
+    }
+    if (empty)
+        return true;
+    int64_t expect = 1;
+    for (int i = t->ndim - 1; i >= 0; --i) {
         if (t->shape[i] != 1 && t->stride[i] != expect)
             return false;
         expect *= t->shape[i];

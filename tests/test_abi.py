@@ -200,6 +200,12 @@ def test_append_validation_errors():
     slots = desc([4], I64)
     assert call_append(desc([0, 2, 64], BF16), desc([0, 2, 64], BF16), desc([0], I64),
                        cache, cache) == PA_OK                            # T = 0: nothing to do
+    # empty tensors with the arbitrary strides frameworks give them
+    assert call_append(desc([0, 2, 64], BF16, strides=[0, 0, 0]),
+                       desc([0, 2, 64], BF16, strides=[7, 3, 1]), desc([0], I64, strides=[0]),
+                       cache, cache) == PA_OK
+    assert call_append(desc([4, 2, 64], BF16, strides=[128, 64, 2]), k, slots, cache, cache) \
+        == PA_ERR_LAYOUT                                                # not dense, not empty
     assert call_append(None, k, slots, cache, cache) == PA_ERR_NULL
     assert call_append(k, k, desc([4], I32), cache, cache) == PA_ERR_DTYPE
     f32 = desc([4, 2, 64], F32)

@@ -126,3 +126,20 @@ def test_many_rows_head_dim_64_every_row():
     assert b.q.shape[0] * b.num_heads >= 8192
     ref, _, _ = oracle_step(b)
     check_close(out, ref, "bf16", "many-row D64 verify")
+
+
+def test_multi_step_without_new_tokens():
+    """A step in which no sequence has a new token: the empty rows, slots and
+    query tensors (whatever strides the framework gives them) are accepted,
+    nothing is written and the call returns."""
+    b = workloads.make_batch("llama3_8b_bf16", device=DEV, num_seqs=1, num_heads=32,
+                             num_kv_heads=4, head_dim=64, lens=("uniform", 1, 630), max_len=630,
+                             query_lens=("fixed", 0), poison=True, seed=1461281404)
+    assert b.q.shape[0] == 0 and b.slot_mapping.shape[0] == 0
+    ref, _, _ = oracle_step(b)
+    print("CASE multi without new tokens", flush=True)
+    kc, vc = gpu_caches(b)
+    out = gpu_step_multi(b, kc, vc, partition_tokens=64)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 32, 64)
+    check_close(out, ref, b.cache_dtype, "multi without new tokens")
