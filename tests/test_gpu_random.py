@@ -11,7 +11,10 @@ decode:  1-40 sequences, 1-8 KV heads, groups 1-8, head_dim 64 or 128,
          no sequence may read.
 multi:   the same, bf16 query, 0-8 new tokens per sequence.
 cascade: 4-40 sequences sharing a prefix of 1-12 blocks plus 1-200 own
-         tokens each."""
+         tokens each.
+append:  1-69 sequences of up to 4000 tokens, fixed runs of 1-64-block
+         partitions or balanced chunks: pa_decode_append bitwise against
+         pa_kv_append + pa_decode, and pa_decode_noalloc."""
 import numpy as np
 import pytest
 import torch
@@ -112,3 +115,51 @@ def test_random_cascade(c):
     torch.cuda.synchronize()
     assert int(flag.item()) == 0
     check_close(out, ref, b.cache_dtype, f"random cascade {c}")
+
+
+def _draw_long(rng):
+    kind = ["f32", "bf16", "bf16", "fp8"][int(rng.integers(0, 4))]
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    return dict(kind=kind, S=int(rng.integers(1, 70)), Hkv=Hkv, H=Hkv * int(rng.choice([1, 2, 4, 8])),
+                D=int(rng.choice([64, 128])), bs=int(rng.choice([16, 32])),
+                max_len=int(rng.integers(1, 4001)), chunk=int(rng.choice([0, 0, 1, 3, 16, 64])),
+                seed=int(rng.integers(0, 2**31)))
+
+
+_RNG_LONG = np.random.default_rng(20261203)
+APPEND = [_draw_long(_RNG_LONG) for _ in range(16)]
+
+
+def _bits_dtype(t):
+    """Integer dtype of a cache's bit patterns, so NaN-poisoned slots compare equal."""
+    return {torch.float32: torch.int32, torch.bfloat16: torch.int16}.get(t.dtype, t.dtype)
+
+
+@pytest.mark.parametrize("c", APPEND, ids=_ids(APPEND))
+def test_random_decode_append(c):
+    """Longer sequences (up to 4000 tokens, 1-69 of them) and fixed runs of
+    partitions: pa_decode_append bit for bit equal to pa_kv_append then
+    pa_decode (output and both whole caches), that within tolerance of the
+    oracle, and pa_decode_noalloc equal to pa_decode where its static
+    workspace suffices."""
+    b = _batch(c, lens=("uniform", 1, c["max_len"]), max_len=c["max_len"])
+    ref, _, _ = oracle_step(b)
+    P = c["chunk"] * c["bs"]
+    print("CASE random decode_append", c, flush=True)
+    kc, vc = gpu_caches(b)
+    sep = gpu_step(b, kc, vc, partition_tokens=P)
+    kc2, vc2 = gpu_caches(b)
+    fused = pa.decode_append(b.k_new, b.v_new, b.slot_mapping, b.q, kc2, vc2, b.block_tables,
+                             b.seq_lens, b.scale, k_scale=b.k_scale, v_scale=b.v_scale,
+                             partition_tokens=P)
+    torch.cuda.synchronize()
+    check_close(sep, ref, b.cache_dtype, f"random decode_append {c}")
+    assert torch.equal(fused, sep)
+    for x, y in ((kc, kc2), (vc, vc2)):
+        assert torch.equal(x.view(_bits_dtype(x)), y.view(_bits_dtype(x)))
+    if pa.decode_workspace_size(b.q, kc2, b.block_tables, P) <= pa.NOALLOC_MAX_WORKSPACE:
+        out = torch.empty_like(b.q)
+        pa.decode_noalloc(b.q, kc2, vc2, b.block_tables, b.seq_lens, b.scale, out,
+                          k_scale=b.k_scale, v_scale=b.v_scale, partition_tokens=P)
+        torch.cuda.synchronize()
+        assert torch.equal(out, sep)
