@@ -14,7 +14,8 @@ cascade: 4-40 sequences sharing a prefix of 1-12 blocks plus 1-200 own
          tokens each.
 append:  1-69 sequences of up to 4000 tokens, fixed runs of 1-64-block
          partitions or balanced chunks: pa_decode_append bitwise against
-         pa_kv_append + pa_decode, and pa_decode_noalloc."""
+         pa_kv_append + pa_decode, and pa_decode_noalloc; 6 of them with
+         257-1200 sequences."""
 import numpy as np
 import pytest
 import torch
@@ -163,3 +164,22 @@ def test_random_decode_append(c):
                           k_scale=b.k_scale, v_scale=b.v_scale, partition_tokens=P)
         torch.cuda.synchronize()
         assert torch.equal(out, sep)
+
+
+def _draw_wide(rng):
+    c = _draw_long(rng)
+    c.update(S=int(rng.integers(257, 1201)), max_len=int(rng.integers(1, 601)))
+    return c
+
+
+_RNG_WIDE = np.random.default_rng(20261204)
+WIDE = [_draw_wide(_RNG_WIDE) for _ in range(6)]
+
+
+@pytest.mark.parametrize("c", WIDE, ids=_ids(WIDE))
+def test_random_wide_batches(c):
+    """257-1200 sequences: the chunk location for batches beyond one
+    256-sequence register pass (two passes over the lengths), balanced
+    chunks and runs of partitions, the fused append bit for bit against the
+    two calls."""
+    test_random_decode_append(c)
