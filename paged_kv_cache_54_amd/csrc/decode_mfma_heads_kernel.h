@@ -144,13 +144,10 @@ __global__ __launch_bounds__(64 * HK) void decode_mfma_heads_kernel(DecodeArgs a
     for (int k = 0; k < n; ++k) {
         Cursor hc = cc;
         hc.kvh = kvh;
-        // A new sequence's query rows are loaded before the next block's
-        // loads (loads retire in order); a partition boundary inside a
-        // sequence keeps them.
+        // A segment's query rows are loaded before the next block's loads
+        // (loads retire in order).
         if (k == 0 || cc.j == 0)
-            att.load_q(a, hc);
-        if (k == 0 || cc.j == 0)
-            att.reset(hc);
+            att.begin(a, hc);
         const int tok_base = cc.j * BS;
         __syncthreads();                                  // previous tiles fully read
         if (id >= 0)
