@@ -430,6 +430,8 @@ def region_table(caches, device=None, pin=False) -> Regions:
 
 
 def _dev_ptr(t: torch.Tensor, what: str) -> int:
+    if t.numel() == 0:
+        return 0                        # nothing is read; the library takes no pointer
     if not (t.is_cuda or t.is_pinned()):
         raise TypeError(f"{what} must be device memory or pinned host memory")
     if not t.is_contiguous():

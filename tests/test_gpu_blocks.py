@@ -172,3 +172,23 @@ def test_swap_out_and_in():
     torch.cuda.synchronize()
     assert f2 == 0
     assert_regions_equal(case.regions, want_dev, "swap in")
+
+
+@pytest.mark.parametrize("pin", [False, True], ids=["device_ids", "pinned_ids"])
+def test_empty_id_lists_change_nothing(pin):
+    """No ids (an empty tensor, pinned or on the device): nothing is written
+    and no error is raised."""
+    g = torch.Generator(device=DEV).manual_seed(9)
+    regions = [torch.randint(0, 256, (16, 4096), dtype=torch.uint8, device=DEV, generator=g)
+               for _ in range(2)]
+    before = [r.clone() for r in regions]
+    regs = pa.region_table(regions, pin=pin)
+    ids = torch.empty(0, dtype=torch.int32)
+    pairs = torch.empty((0, 2), dtype=torch.int32)
+    flag = flag_word()
+    announce("empty id lists", "pinned" if pin else "device")
+    pa.zero_blocks(ids.pin_memory() if pin else ids.to(DEV), regs, err_flag=flag)
+    pa.copy_blocks(pairs.pin_memory() if pin else pairs.to(DEV), regs, regs, err_flag=flag)
+    torch.cuda.synchronize()
+    assert all(torch.equal(r, b) for r, b in zip(regions, before))
+    assert int(flag.item()) == 0
